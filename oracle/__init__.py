@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for the selective state-space scan (S6).
+
+TEST INFRASTRUCTURE ONLY: the plain sequential definition that the HIP path is
+checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import it.  It shares no code with the HIP
+library (``selective_state_space_28_amd``) and neither imports the other.
+
+The arithmetic lives in ``ssm_oracle.c`` (plain C, double precision); this
+module only converts numpy arrays to float64 and calls it through ctypes.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+against values and identities fixed by the pages (worked impulse response,
+printed exp/softplus values, convolution = recurrence, brute-force
+semiseparable sums, stability bound, chunking/decode identities).  The D-skip
+term and the silu gate are pinned only by their definitions (the pages do not
+state them): parity unpinned by the pages for those two terms.
+"""
+from .oracle import scan_fwd, state_update, lib_path, build  # noqa: F401

@@ -1,0 +1,110 @@
+"""ctypes wrapper around the fp64 oracle (``ssm_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Arguments are numpy
+arrays in the layouts of the C functions; everything is widened to float64
+(exactly: fp32 and bf16 values are representable in fp64) before the call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build() -> str:
+    """Compile ``ssm_oracle.c`` into ``liboracle.so`` with gcc (plain IEEE
+    double arithmetic: no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", _LIB + ".tmp", _SRC,
+           "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    dp = ctypes.POINTER(ctypes.c_double)
+    L = ctypes.c_long
+    lib.oracle_scan_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, dp, dp, dp,
+                                    L, L, L, L, ctypes.c_int]
+    lib.oracle_scan_fwd.restype = ctypes.c_int
+    lib.oracle_state_update.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, dp,
+                                        L, L, L]
+    lib.oracle_state_update.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+             h0=None, nthreads=1):
+    """Sequential fp64 scan.
+
+    u, delta, z: (batch, dim, L); A: (dim, N); B, C: (batch, N, L);
+    D, delta_bias: (dim,); h0: (batch, dim, N).  Returns (y, last_state) as
+    float64 arrays of shapes (batch, dim, L) and (batch, dim, N).
+    """
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias, h0 = map(_f64, (D, z, delta_bias, h0))
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and A.shape == (dim, N)
+    assert B.shape == (batch, N, L) and C.shape == (batch, N, L)
+    assert z is None or z.shape == u.shape
+    assert D is None or D.shape == (dim,)
+    assert delta_bias is None or delta_bias.shape == (dim,)
+    assert h0 is None or h0.shape == (batch, dim, N)
+    y = np.empty((batch, dim, L), dtype=np.float64)
+    last = np.empty((batch, dim, N), dtype=np.float64)
+    rc = _load().oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                 _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
+                                 _ptr(y), _ptr(last), batch, dim, N, L, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan_fwd failed with {rc}")
+    return y, last
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                 delta_softplus=True):
+    """One fp64 decode step.  ``state`` (batch, dim, N) is taken as a new
+    float64 copy, updated and returned together with y (batch, dim)."""
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias = map(_f64, (D, z, delta_bias))
+    batch, dim, N = st.shape
+    assert u.shape == (batch, dim) and delta.shape == (batch, dim)
+    assert A.shape == (dim, N) and B.shape == (batch, N) and C.shape == (batch, N)
+    y = np.empty((batch, dim), dtype=np.float64)
+    rc = _load().oracle_state_update(_ptr(st), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                     _ptr(D), _ptr(z), _ptr(delta_bias),
+                                     int(bool(delta_softplus)), _ptr(y), batch, dim, N)
+    if rc != 0:
+        raise RuntimeError(f"oracle_state_update failed with {rc}")
+    return y, st

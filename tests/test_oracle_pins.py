@@ -1,0 +1,345 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself through a retyped formula: each
+check is a printed value from the pages (tests/golden/*.json), a closed form,
+an identity stated on the pages (convolution = recurrence, scans equal), or an
+independent brute-force form from tests/brute.py.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import brute
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _single_step_abar(A, x, softplus=True):
+    """Abar = exp(Delta*A) read off the oracle: one step from h0 = 1 with no
+    input (u = 0) and C = 1, so y = last_state = Abar."""
+    u = np.zeros((1, 1, 1))
+    dr = np.array([[[x]]], dtype=np.float64)
+    Am = np.array([[A]], dtype=np.float64)
+    B = np.zeros((1, 1, 1))
+    C = np.ones((1, 1, 1))
+    h0 = np.ones((1, 1, 1))
+    y, last = oracle.scan_fwd(u, dr, Am, B, C, h0=h0, delta_softplus=softplus)
+    assert y[0, 0, 0] == last[0, 0, 0]
+    return y[0, 0, 0]
+
+
+def _single_step_delta(x):
+    """Delta = softplus(x) read off the oracle: A = 0 (Abar = 1), h0 = 0,
+    u = B = C = 1, so y = Delta."""
+    y, _ = oracle.scan_fwd(np.ones((1, 1, 1)), np.array([[[x]]]), np.zeros((1, 1)),
+                           np.ones((1, 1, 1)), np.ones((1, 1, 1)))
+    return y[0, 0, 0]
+
+
+# ---------------------------------------------------------------- worked impulse
+def _impulse_setup(through_softplus):
+    g = _golden("impulse_response.json")
+    L = len(g["x"])
+    u = np.array(g["x"], dtype=np.float64).reshape(1, 1, L)
+    A = np.log(np.array(g["Abar_diag"])).reshape(1, 2)
+    B = np.repeat(np.array(g["Bbar"]).reshape(1, 2, 1), L, axis=2)  # Delta = 1 -> Bbar = B
+    C = np.repeat(np.array(g["C"]).reshape(1, 2, 1), L, axis=2)
+    if through_softplus:
+        dr = np.zeros((1, 1, L))
+        bias = np.array([math.log(math.e - 1.0)])   # softplus(ln(e-1)) = 1
+        return g, dict(u=u, delta=dr, A=A, B=B, C=C, delta_bias=bias, delta_softplus=True)
+    dr = np.ones((1, 1, L))
+    return g, dict(u=u, delta=dr, A=A, B=B, C=C, delta_softplus=False)
+
+
+@pytest.mark.parametrize("through_softplus", [False, True])
+def test_worked_impulse_response(through_softplus):
+    g, kw = _impulse_setup(through_softplus)
+    y, last = oracle.scan_fwd(**kw)
+    np.testing.assert_allclose(y[0, 0], g["y"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(last[0, 0], g["h"][-1], rtol=0, atol=1e-12)
+    # intermediate states: run the first k steps
+    for k in range(1, 4):
+        kk = {key: (v[..., :k] if key in ("u", "delta", "B", "C") else v) for key, v in kw.items()}
+        _, hk = oracle.scan_fwd(**kk)
+        np.testing.assert_allclose(hk[0, 0], g["h"][k - 1], rtol=0, atol=1e-12)
+
+
+def test_impulse_response_is_the_convolution_kernel():
+    g, kw = _impulse_setup(False)
+    y, _ = oracle.scan_fwd(**kw)
+    yc, K = brute.lti_convolution_y(g["x"], g["Abar_diag"], g["Bbar"], g["C"])
+    np.testing.assert_allclose(K, g["kernel"], atol=1e-12)
+    np.testing.assert_allclose(y[0, 0], yc, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_lti_recurrence_equals_convolution(seed):
+    """Constant Delta, B, C over time: the output equals the convolution of the
+    input with (C.Bbar, C.Abar.Bbar, ...)."""
+    rng = np.random.default_rng(100 + seed)
+    N, L = 3, 40
+    A = -rng.uniform(0.1, 2.0, size=N)
+    dl = rng.uniform(0.05, 0.8)
+    B = rng.standard_normal(N)
+    C = rng.standard_normal(N)
+    x = rng.standard_normal(L)
+    y, _ = oracle.scan_fwd(x.reshape(1, 1, L), np.full((1, 1, L), dl), A.reshape(1, N),
+                           np.repeat(B.reshape(1, N, 1), L, axis=2),
+                           np.repeat(C.reshape(1, N, 1), L, axis=2), delta_softplus=False)
+    yc, _ = brute.lti_convolution_y(x, np.exp(dl * A), dl * B, C)
+    np.testing.assert_allclose(y[0, 0], yc, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------- printed values
+def test_zoh_values():
+    for e in _golden("discretisation_values.json")["zoh_abar"]:
+        v = _single_step_abar(e["A"], e["delta"], softplus=False)
+        assert abs(v - e["abar"]) <= e["tol"], e
+
+
+def test_softplus_values():
+    for e in _golden("discretisation_values.json")["softplus"]:
+        v = _single_step_delta(e["x"])
+        assert abs(v - e["value"]) <= e["tol"], e
+
+
+def test_softplus_then_zoh_values_and_decay_steps():
+    g = _golden("discretisation_values.json")
+    for e in g["softplus_zoh"]:
+        v = _single_step_abar(e["A"], e["x"], softplus=True)
+        assert abs(v - e["abar"]) <= e["tol"], e
+    for e in g["decay_steps"]:
+        a = _single_step_abar(e["A"], e["x"], softplus=True)
+        n = -1.0 / math.log(a)
+        assert abs(n - e["steps"]) <= e["tol"], e
+
+
+def test_softplus_zoh_closed_form_is_logistic():
+    """With A = -1, exp(-softplus(x)) = 1/(1+e^x) exactly (ln(1+e^x) is the
+    softplus; exp of its negative is the logistic of -x).  Checked over a
+    wide range, which also covers the overflow-prone and digit-losing ends
+    of softplus."""
+    for x in np.linspace(-40, 40, 161):
+        v = _single_step_abar(-1.0, float(x), softplus=True)
+        ref = 1.0 / (1.0 + math.exp(x))
+        assert abs(v - ref) <= 1e-15 + 1e-13 * ref, (x, v, ref)
+
+
+def test_softplus_extremes_finite():
+    assert _single_step_delta(1000.0) == 1000.0
+    v = _single_step_delta(-1000.0)
+    assert v >= 0.0 and v < 1e-300
+    assert abs(_single_step_delta(-30.0) - math.exp(-30.0)) < 1e-25
+
+
+# ------------------------------------------------------------ brute-force sums
+def _tiny_case(rng, batch=2, dim=3, N=4, L=12, gate=True, dskip=True, h0=False):
+    u = rng.standard_normal((batch, dim, L))
+    dr = 0.5 * rng.standard_normal((batch, dim, L))
+    A = -rng.uniform(0.2, 3.0, size=(dim, N))
+    B = rng.standard_normal((batch, N, L))
+    C = rng.standard_normal((batch, N, L))
+    bias = rng.uniform(-3.0, -0.5, size=dim)
+    D = rng.standard_normal(dim) if dskip else None
+    z = rng.standard_normal((batch, dim, L)) if gate else None
+    hh = rng.standard_normal((batch, dim, N)) if h0 else None
+    return dict(u=u, delta=dr, A=A, B=B, C=C, D=D, z=z, delta_bias=bias, h0=hh)
+
+
+@pytest.mark.parametrize("gate,dskip,h0", [(False, False, False), (True, True, False),
+                                           (True, False, True), (False, True, True)])
+def test_oracle_equals_semiseparable_sum(gate, dskip, h0):
+    rng = np.random.default_rng(7)
+    kw = _tiny_case(rng, gate=gate, dskip=dskip, h0=h0)
+    y, _ = oracle.scan_fwd(**kw)
+    yb = brute.semiseparable_y(kw["u"], kw["delta"], kw["A"], kw["B"], kw["C"], kw["D"], kw["z"],
+                               kw["delta_bias"], True, kw["h0"])
+    np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-12)
+
+
+def test_oracle_equals_semiseparable_sum_on_c0():
+    inp = synth.make_scan_inputs(synth.SCAN_CONFIGS["c0"])
+    w = {k: synth.widen(inp[k], "f32") for k in ("u", "delta", "B", "C", "z")}
+    y, _ = oracle.scan_fwd(w["u"], w["delta"], inp["A"], w["B"], w["C"], inp["D"], w["z"],
+                           inp["delta_bias"])
+    yb = brute.semiseparable_y(w["u"], w["delta"], inp["A"].astype(np.float64), w["B"], w["C"],
+                               inp["D"], w["z"], inp["delta_bias"], True)
+    np.testing.assert_allclose(y, yb, rtol=1e-11, atol=1e-11 * np.abs(yb).max())
+
+
+def test_no_decay_is_cumulative_sum():
+    """A = 0 gives Abar = 1 (no decay, the linear-attention special case):
+    y_t = sum_{s<=t} (C_t . B_s) Delta_s u_s."""
+    rng = np.random.default_rng(11)
+    N, L = 4, 30
+    u = rng.standard_normal(L)
+    dl = rng.uniform(0.01, 0.5, size=L)
+    B = rng.standard_normal((N, L))
+    C = rng.standard_normal((N, L))
+    y, last = oracle.scan_fwd(u.reshape(1, 1, L), dl.reshape(1, 1, L), np.zeros((1, N)),
+                              B.reshape(1, N, L), C.reshape(1, N, L), delta_softplus=False)
+    S = np.cumsum(B * (dl * u)[None, :], axis=1)  # (N, L): running sum of inputs
+    np.testing.assert_allclose(y[0, 0], np.sum(C * S, axis=0), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(last[0, 0], S[:, -1], rtol=1e-12, atol=1e-12)
+
+
+def test_zero_delta_ignores_input():
+    """Delta = 0: Abar = 1 and the input term vanishes, so the state is held."""
+    rng = np.random.default_rng(12)
+    kw = _tiny_case(rng, batch=1, dim=2, N=3, L=9, gate=False, dskip=True, h0=True)
+    kw["delta"] = np.zeros_like(kw["delta"])
+    kw["delta_bias"] = None
+    y, last = oracle.scan_fwd(**kw, delta_softplus=False)
+    np.testing.assert_array_equal(last, kw["h0"])
+    ref = np.einsum("bnl,bdn->bdl", kw["C"], kw["h0"]) + kw["D"][None, :, None] * kw["u"]
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-14)
+
+
+def test_dskip_and_gate_by_definition():
+    """D-skip and gate are not stated on the pages (parity unpinned by them);
+    pinned by their definitions: with B = 0 the state stays 0 and
+    y = D u silu(z); silu(0) = 0; silu(z)/z -> 1 for large z."""
+    rng = np.random.default_rng(13)
+    kw = _tiny_case(rng, batch=1, dim=3, N=2, L=8)
+    kw["B"] = np.zeros_like(kw["B"])
+    y, _ = oracle.scan_fwd(**kw)
+    z = kw["z"]
+    np.testing.assert_allclose(y, kw["D"][None, :, None] * kw["u"] * z / (1 + np.exp(-z)),
+                               rtol=1e-14, atol=1e-15)
+    kw["z"] = np.zeros_like(z)
+    y0, _ = oracle.scan_fwd(**kw)
+    assert np.all(y0 == 0.0)
+    kw["z"] = np.full_like(z, 60.0)
+    y60, _ = oracle.scan_fwd(**kw)
+    np.testing.assert_allclose(y60 / 60.0, kw["D"][None, :, None] * kw["u"], rtol=1e-14)
+
+
+# ------------------------------------------------------- scans and the operator
+@pytest.mark.parametrize("L", [1, 7, 16, 33])
+def test_scans_equal_sequential_and_oracle(L):
+    rng = np.random.default_rng(20 + L)
+    kw = _tiny_case(rng, batch=1, dim=1, N=3, L=L, gate=False, dskip=False)
+    dl = brute.deltas(kw["delta"][0], kw["delta_bias"])  # (1, L)
+    elems = brute.affine_elements(kw["u"][0, 0], dl[0], kw["A"][0], kw["B"][0], L)
+    seq = brute.sequential_scan(elems)
+    for other in (brute.hillis_steele_scan(elems), brute.blelloch_scan(elems),
+                  brute.chunked_scan(elems, 4), brute.chunked_scan(elems, 5)):
+        for s, o in zip(seq, other):
+            np.testing.assert_allclose(o[0], s[0], rtol=1e-13)
+            np.testing.assert_allclose(o[1], s[1], rtol=1e-12, atol=1e-14)
+    # state after step t is the b-part of e_0 o ... o e_t (zero start)
+    hs = np.array([s[1] for s in seq])  # (L, N)
+    y_scan = np.sum(kw["C"][0].T * hs, axis=1)
+    y, last = oracle.scan_fwd(**kw)
+    np.testing.assert_allclose(y[0, 0], y_scan, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(last[0, 0], hs[-1], rtol=1e-12, atol=1e-13)
+
+
+def test_operator_associative_not_commutative():
+    rng = np.random.default_rng(3)
+    e = [(rng.uniform(0, 1, 4), rng.standard_normal(4)) for _ in range(3)]
+    l = brute.compose(brute.compose(e[0], e[1]), e[2])
+    r = brute.compose(e[0], brute.compose(e[1], e[2]))
+    np.testing.assert_allclose(l[0], r[0], rtol=1e-15)
+    np.testing.assert_allclose(l[1], r[1], rtol=1e-14)
+    ab, ba = brute.compose(e[0], e[1]), brute.compose(e[1], e[0])
+    assert not np.allclose(ab[1], ba[1])
+
+
+@pytest.mark.parametrize("split", [1, 17, 40])
+def test_segment_split_resumes_exactly(split):
+    rng = np.random.default_rng(30)
+    kw = _tiny_case(rng, batch=2, dim=3, N=4, L=41, h0=True)
+    y, last = oracle.scan_fwd(**kw)
+    k1 = {k: (v[..., :split] if k in ("u", "delta", "B", "C", "z") else v) for k, v in kw.items()}
+    y1, l1 = oracle.scan_fwd(**k1)
+    k2 = {k: (v[..., split:] if k in ("u", "delta", "B", "C", "z") else v) for k, v in kw.items()}
+    k2["h0"] = l1
+    y2, l2 = oracle.scan_fwd(**k2)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=-1), y, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l2, last, rtol=1e-13, atol=1e-14)
+
+
+def test_decode_step_extends_scan():
+    """scan over L+1 tokens = scan over L tokens, then one decode step."""
+    rng = np.random.default_rng(31)
+    kw = _tiny_case(rng, batch=2, dim=3, N=4, L=10, h0=True)
+    y, last = oracle.scan_fwd(**kw)
+    k1 = {k: (v[..., :-1] if k in ("u", "delta", "B", "C", "z") else v) for k, v in kw.items()}
+    _, l1 = oracle.scan_fwd(**k1)
+    yd, st = oracle.state_update(l1, kw["u"][..., -1], kw["delta"][..., -1], kw["A"],
+                                 kw["B"][..., -1], kw["C"][..., -1], kw["D"], kw["z"][..., -1],
+                                 kw["delta_bias"])
+    np.testing.assert_allclose(yd, y[..., -1], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(st, last, rtol=1e-13, atol=1e-14)
+
+
+def test_decode_steps_equal_scan_from_state():
+    """Several decode steps in a row equal one scan started from the same state."""
+    rng = np.random.default_rng(32)
+    kw = _tiny_case(rng, batch=2, dim=4, N=2, L=6, h0=True)
+    y, last = oracle.scan_fwd(**kw)
+    st = kw["h0"]
+    for t in range(6):
+        yd, st = oracle.state_update(st, kw["u"][..., t], kw["delta"][..., t], kw["A"],
+                                     kw["B"][..., t], kw["C"][..., t], kw["D"], kw["z"][..., t],
+                                     kw["delta_bias"])
+        np.testing.assert_allclose(yd, y[..., t], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(st, last, rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------- stability
+def test_bounded_state_when_A_negative():
+    """All A < 0 gives |Abar| < 1 and a bounded state: from a zero start,
+    |h_t,n| <= max_s |Delta_s u_s B_s,n| / (1 - max_s Abar_s,n)."""
+    inp = synth.make_scan_inputs(synth.SCAN_CONFIGS["c0"])
+    w = {k: synth.widen(inp[k], "f32") for k in ("u", "delta", "B", "C")}
+    L = w["u"].shape[-1]
+    x = w["delta"][0] + inp["delta_bias"].astype(np.float64)[:, None]
+    dl = np.logaddexp(0.0, x)  # softplus, numpy's own routine
+    for d in range(inp["A"].shape[0]):
+        A = inp["A"][d].astype(np.float64)
+        amax = np.exp(dl[d][:, None] * A[None, :]).max(axis=0)
+        drive = np.abs(dl[d][:, None] * w["u"][0, d][:, None] * w["B"][0].T).max(axis=0)
+        bound = drive / (1.0 - amax)
+        for t in (1, L // 3, L):
+            _, h = oracle.scan_fwd(w["u"][:, d:d + 1, :t], w["delta"][:, d:d + 1, :t],
+                                   inp["A"][d:d + 1], w["B"][..., :t], w["C"][..., :t],
+                                   delta_bias=inp["delta_bias"][d:d + 1])
+            assert np.all(np.abs(h[0, 0]) <= bound * (1 + 1e-12))
+
+
+def test_positive_A_grows():
+    """A > 0 gives Abar > 1: the unforced state grows (the unstable case)."""
+    y, last = oracle.scan_fwd(np.zeros((1, 1, 50)), np.full((1, 1, 50), 0.1), np.array([[0.5]]),
+                              np.zeros((1, 1, 50)), np.ones((1, 1, 50)), h0=np.ones((1, 1, 1)),
+                              delta_softplus=False)
+    np.testing.assert_allclose(last[0, 0, 0], math.exp(0.5 * 0.1 * 50), rtol=1e-12)
+    assert np.all(np.diff(y[0, 0]) > 0)
+
+
+def test_threads_do_not_change_results():
+    rng = np.random.default_rng(40)
+    kw = _tiny_case(rng, batch=3, dim=5, N=4, L=33, h0=True)
+    y1, l1 = oracle.scan_fwd(**kw, nthreads=1)
+    y4, l4 = oracle.scan_fwd(**kw, nthreads=4)
+    np.testing.assert_array_equal(y1, y4)
+    np.testing.assert_array_equal(l1, l4)
+
+
+def test_empty_inputs():
+    y, last = oracle.scan_fwd(np.zeros((1, 2, 0)), np.zeros((1, 2, 0)), -np.ones((2, 3)),
+                              np.zeros((1, 3, 0)), np.zeros((1, 3, 0)))
+    assert y.shape == (1, 2, 0)
+    np.testing.assert_array_equal(last, 0.0)
