@@ -1,0 +1,139 @@
+/*
+ * ssm.h -- C ABI of libssm: the selective state-space scan (S6) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (one independent channel per (b, d); all tensors row-major):
+ *
+ *   Delta_t  = softplus(delta[b,d,t] + delta_bias[d])  (delta_softplus != 0)
+ *            =          delta[b,d,t] + delta_bias[d]   (delta_softplus == 0)
+ *   Abar_t,n = exp(Delta_t * A[d,n])
+ *   h_t,n    = Abar_t,n * h_{t-1},n + Delta_t * B[b,n,t] * u[b,d,t]
+ *   y[b,d,t] = (sum_n C[b,n,t] * h_t,n + D_skip[d] * u[b,d,t]) * silu(z[b,d,t])
+ *
+ * Sources, cited by page title and section:
+ *  - "Mamba" paper review (wiki.alexanderbaur.de), "SSM": the continuous
+ *    system h' = Ah + Bx, y = Ch; zero-order hold Abar = exp(Delta A);
+ *    the recurrence h_t = Abar h_{t-1} + Bbar x_t; diagonal A used SISO per
+ *    channel.  "Selection Mechanism": Delta, B, C vary per token.
+ *    "Optimization": one fused kernel for discretisation, scan and readout,
+ *    the state never stored in HBM; parallel scan of the associative step.
+ *  - "Paper: Mamba" course module (konke.bhala.ai/m/F12), "Math & data
+ *    structures": zero-order hold for Abar with Euler as the alternative for
+ *    Bbar (the input term here is the Euler form Delta*B*u), and the
+ *    associative composition of affine steps.
+ *  - "Exercises -- State-space models (Mamba, S4)" (brentwoodlivery.com):
+ *    readout y_k = C h_k after the update; zero initial state; softplus as
+ *    the positive time step; decoding one token at a time with a
+ *    constant-size state (O(1) work, O(N) memory per token).
+ *  - The D_skip term and the silu(z) output gate are not written out on the
+ *    pages; the "Mamba" review says only that a gate mixes in the residual.
+ *    They are applied as in the formula above.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing and keeps no state between calls.
+ *  - dtype selects the storage of u, delta, B, C, z and y: SSM_F32 (float)
+ *    or SSM_BF16 (bfloat16 bit patterns, 2 bytes).  A, delta_bias, D_skip,
+ *    h0, last_state and the decode state are always float32.
+ *  - Layouts, L fastest: u, delta, z, y: (batch, dim, seqlen); B, C:
+ *    (batch, dstate, seqlen); A: (dim, dstate); delta_bias, D_skip: (dim);
+ *    h0, last_state, state: (batch, dim, dstate).  Contiguous, no strides.
+ *  - Pointers must be aligned to their element size (SSM_ERR_ALIGN
+ *    otherwise).  16-byte aligned pointers with rows of a multiple of 16
+ *    bytes take the vectorised path; any other legal alignment works, slower.
+ *  - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work and return; they never synchronise.  Two calls that write the same
+ *    outputs or workspace on different streams race.
+ *  - Arguments are validated before any HIP call; on an error nothing is
+ *    enqueued.  A launch failure returns SSM_ERR_HIP.
+ *  - NaN and Inf inputs propagate; A is not checked for sign (A > 0 is an
+ *    unstable system and its state grows, as the pages note).
+ *  - Results are deterministic: the same inputs on the same device give the
+ *    same bits, run after run.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  SSM_ERR_SHAPE = -2,     /* negative size, dstate not in {1,2,4,8,16}, too large */
+  SSM_ERR_DTYPE = -3,     /* dtype not an ssm_dtype_t value                      */
+  SSM_ERR_ALIGN = -4,     /* a pointer not aligned to its element size           */
+  SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query's answer   */
+  SSM_ERR_HIP = -6,       /* the HIP runtime reported an error at launch         */
+  SSM_ERR_ALIAS = -7      /* y (or the decode state) is the same buffer as an input */
+} ssm_status_t;
+
+/*
+ * ssm_scan_fwd_workspace_bytes -- bytes of device workspace that
+ * ssm_scan_fwd needs for this problem (0 when the sequence is not split
+ * across workgroups).  Pure host function: no HIP call.  Returns 0 for
+ * arguments that ssm_scan_fwd would reject.
+ */
+size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seqlen,
+                                    int dtype);
+
+/*
+ * ssm_scan_fwd -- the selective scan over a whole sequence (prefill or the
+ * training forward pass), formula above.
+ *
+ *   u, delta     in   (batch, dim, seqlen), dtype           required
+ *   A            in   (dim, dstate) float32                  required
+ *   B, C         in   (batch, dstate, seqlen), dtype         required
+ *   D_skip       in   (dim) float32                          NULL -> 0
+ *   z            in   (batch, dim, seqlen), dtype            NULL -> no gate
+ *   delta_bias   in   (dim) float32                          NULL -> 0
+ *   delta_softplus    1: Delta = softplus(delta + bias); 0: Delta = delta + bias
+ *   h0           in   (batch, dim, dstate) float32           NULL -> zero state
+ *   y            out  (batch, dim, seqlen), dtype            required; must not
+ *                     be u, delta or z
+ *   last_state   out  (batch, dim, dstate) float32           NULL -> not written
+ *   workspace    scratch of at least ssm_scan_fwd_workspace_bytes(...) bytes,
+ *                device memory owned by the caller; NULL allowed when that is 0.
+ *                Its contents on entry do not matter.
+ *   batch, dim >= 0; dstate in {1,2,4,8,16}; seqlen >= 0.  seqlen == 0 only
+ *   writes last_state (= h0, or zeros).
+ */
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D_skip, const void* z,
+                 const float* delta_bias, int delta_softplus, const float* h0, void* y,
+                 float* last_state, int batch, int dim, int dstate, int64_t seqlen,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_state_update -- one decode step for a single new token per sequence:
+ * the formula above with seqlen = 1, starting from and writing back `state`.
+ *
+ *   state        in/out (batch, dim, dstate) float32, updated in place  required
+ *   u, delta     in   (batch, dim), dtype                               required
+ *   A            in   (dim, dstate) float32                             required
+ *   B, C         in   (batch, dstate), dtype                            required
+ *   D_skip       in   (dim) float32                                     NULL -> 0
+ *   z            in   (batch, dim), dtype                               NULL -> no gate
+ *   delta_bias   in   (dim) float32                                     NULL -> 0
+ *   y            out  (batch, dim), dtype                               required
+ *   batch, dim >= 0; dstate in {1,2,4,8,16}.
+ */
+int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
+                     const void* B, const void* C, const float* D_skip, const void* z,
+                     const float* delta_bias, int delta_softplus, void* y, int batch,
+                     int dim, int dstate, int dtype, void* stream);
+
+/* ssm_status_string -- a static, human-readable name for a status code. */
+const char* ssm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

@@ -1,0 +1,20 @@
+"""Selective state-space scan (S6) on MI355X: Python binding of libssm.
+
+The functions carry the names of the C entry points in include/ssm.h and do
+argument marshalling only (dtype/shape/device checks, output and workspace
+allocation through torch, the current torch stream).  Every step of the
+computation runs in the HIP kernels of libssm.so; if the library is missing
+the calls raise instead of falling back to anything else.
+
+    y, last = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias,
+                           delta_softplus=True, h0=None, return_last_state=True)
+    y = ssm_state_update(state, u, delta, A, B, C, D, z, delta_bias)
+"""
+from __future__ import annotations
+
+from ._lib import SSM_BF16, SSM_F32, SsmError, header_functions, load, status_string  # noqa: F401
+from .ops import (ssm_scan_fwd, ssm_scan_fwd_workspace_bytes, ssm_state_update,  # noqa: F401
+                  ssm_status_string)
+
+__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_state_update",
+           "ssm_status_string", "SsmError", "load"]

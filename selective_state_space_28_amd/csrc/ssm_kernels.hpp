@@ -1,0 +1,61 @@
+// ssm_kernels.hpp -- host-side launch interface between the C ABI layer
+// (ssm_api.cpp) and the HIP kernels (scan_fwd.hip, state_update.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// Time steps one workgroup stages per tile of the forward scan.
+constexpr int kScanTile = 32;
+
+// Storage type of the per-token tensors.
+enum class Dtype { F32 = 0, BF16 = 1 };
+
+struct ScanLaunch {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;     // nullable
+  const void* z;          // nullable
+  const float* bias;      // nullable
+  const float* h0;        // nullable
+  void* y;
+  float* last_state;      // nullable
+  float* ws_hend;         // (nseg-1, batch, dim, dstate) when nseg > 1
+  float* ws_sumdt;        // (nseg-1, batch, dim) when nseg > 1
+  int batch, dim, dstate;
+  int64_t seqlen;
+  int64_t seglen;         // multiple of kScanTile
+  int nseg;               // segments the sequence is split into
+  int softplus;
+  int vec;                // 16-byte vector loads/stores allowed
+  Dtype dtype;
+};
+
+struct DecodeLaunch {
+  float* state;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* Dskip;     // nullable
+  const void* z;          // nullable
+  const float* bias;      // nullable
+  void* y;
+  int batch, dim, dstate;
+  int softplus;
+  int vec;                // state is 16-byte aligned
+  Dtype dtype;
+};
+
+hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream);
+hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
+// last_state = h0 (or zeros when h0 is null) for an empty sequence.
+hipError_t launch_fill_state(float* dst, const float* src, int64_t n, hipStream_t stream);
+
+}  // namespace ssm

@@ -1,0 +1,110 @@
+// state_update.hip -- one decode step of the selective scan for gfx950.
+//
+// Generation feeds one token at a time through the recurrence with a
+// constant-size state per channel ("Exercises -- State-space models (Mamba,
+// S4)", training vs generation: O(1) work and O(N) memory per token).  Per
+// (b, d): Delta = softplus(delta + bias), then for each state
+// h = exp(Delta*A)*h + Delta*B*u, and y = (C.h + D*u)*silu(z).
+//
+// The step is bound by reading and writing the fp32 state (N*8 bytes per
+// channel against a few bytes of token input), so the layout is built for
+// streaming it: NS = min(N, 4) states per lane (one 16-byte load and store),
+// P = N/NS consecutive lanes per channel, so a wave reads and writes 1 KiB of
+// state contiguously.  The P partial readouts are summed with lane shuffles
+// in a fixed order.
+#include "ssm_kernels.hpp"
+#include "ssm_math.hpp"
+
+namespace ssm {
+
+template <typename T, int N>
+__global__ __launch_bounds__(256) void state_update_kernel(
+    float* __restrict__ state, const T* __restrict__ u, const T* __restrict__ delta,
+    const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
+    const float* __restrict__ Dskip, const T* __restrict__ z, const float* __restrict__ bias,
+    T* __restrict__ y, int batch, int dim, int softplus, int vec) {
+  constexpr int NS = N < 4 ? N : 4;
+  constexpr int P = N / NS;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)batch * dim;
+  // Whole channel groups of P lanes are either all in range or all out of
+  // range (P divides 64 and gid ranges start at multiples of 64), so the
+  // shuffles below only ever read lanes that are active.
+  if (gid >= rows * P) return;
+  const int64_t row = gid / P;
+  const int part = (int)(gid % P);
+  const int b = (int)(row / dim);
+  const int d = (int)(row % dim);
+
+  float h[NS];
+  float* sp = state + row * N + part * NS;
+  if (NS == 4 && vec) {
+    const float4 v = *reinterpret_cast<const float4*>(sp);
+    h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) h[k] = sp[k];
+  }
+
+  const float uv = Elem<T>::load(u + row);
+  const float x = Elem<T>::load(delta + row) + (bias != nullptr ? bias[d] : 0.0f);
+  const float dt = softplus ? softplus_f32(x) : x;
+  const float du = dt * uv;
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int n = part * NS + k;
+    const float a = exp2_hw(dt * (A[(int64_t)d * N + n] * kLog2e));
+    h[k] = __builtin_fmaf(a, h[k], du * Elem<T>::load(B + (int64_t)b * N + n));
+    acc = __builtin_fmaf(Elem<T>::load(C + (int64_t)b * N + n), h[k], acc);
+  }
+
+  if (NS == 4 && vec) {
+    *reinterpret_cast<float4*>(sp) = make_float4(h[0], h[1], h[2], h[3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) sp[k] = h[k];
+  }
+
+#pragma unroll
+  for (int off = 1; off < P; off <<= 1) acc += __shfl_xor(acc, off);
+
+  if (part == 0) {
+    float yv = __builtin_fmaf(Dskip != nullptr ? Dskip[d] : 0.0f, uv, acc);
+    if (z != nullptr) yv *= silu_f32(Elem<T>::load(z + row));
+    Elem<T>::store(y + row, yv);
+  }
+}
+
+template <typename T, int N>
+static hipError_t launch_n(const DecodeLaunch& a, hipStream_t stream) {
+  constexpr int NS = N < 4 ? N : 4;
+  constexpr int P = N / NS;
+  const int64_t threads = (int64_t)a.batch * a.dim * P;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  state_update_kernel<T, N><<<grid, 256, 0, stream>>>(
+      a.state, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A,
+      static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.Dskip,
+      static_cast<const T*>(a.z), a.bias, static_cast<T*>(a.y), a.batch, a.dim, a.softplus,
+      a.vec);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_t(const DecodeLaunch& a, hipStream_t stream) {
+  switch (a.dstate) {
+    case 1: return launch_n<T, 1>(a, stream);
+    case 2: return launch_n<T, 2>(a, stream);
+    case 4: return launch_n<T, 4>(a, stream);
+    case 8: return launch_n<T, 8>(a, stream);
+    case 16: return launch_n<T, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream) {
+  if (a.batch == 0 || a.dim == 0) return hipSuccess;
+  return a.dtype == Dtype::BF16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);
+}
+
+}  // namespace ssm

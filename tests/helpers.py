@@ -1,0 +1,92 @@
+"""Shared test helpers: moving generated inputs to the GPU, running both
+sides, and the scaled-max-error comparison used by every parity test."""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOKEN_KEYS = ("u", "delta", "B", "C", "z")
+
+
+def to_torch(arr, dtype: str, device):
+    import torch
+    if arr is None:
+        return None
+    if dtype == "bf16" and arr.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def widened(inp: dict) -> dict:
+    """float64 copies of every input (exact)."""
+    out = {}
+    for k in TOKEN_KEYS:
+        out[k] = synth.widen(inp.get(k), inp["dtype"]) if inp.get(k) is not None else None
+    for k in ("A", "D", "delta_bias", "h0"):
+        out[k] = None if inp.get(k) is None else np.asarray(inp[k], np.float64)
+    return out
+
+
+def gpu_scan(inp: dict, device, h0=None, softplus=True, return_last_state=True, **kw):
+    """Run ssm_scan_fwd on the GPU; returns float64 numpy (y, last_state)."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    dt = inp["dtype"]
+    t = {k: to_torch(inp.get(k), dt, device) for k in TOKEN_KEYS}
+    A = to_torch(inp["A"], "f32", device)
+    D = to_torch(inp.get("D"), "f32", device)
+    bias = to_torch(inp.get("delta_bias"), "f32", device)
+    h0t = to_torch(h0, "f32", device)
+    res = ssm.ssm_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias,
+                           delta_softplus=softplus, h0=h0t, return_last_state=return_last_state,
+                           **kw)
+    torch.cuda.synchronize(device)
+    if return_last_state:
+        y, last = res
+        return y.float().cpu().numpy().astype(np.float64), last.cpu().numpy().astype(np.float64)
+    return res.float().cpu().numpy().astype(np.float64), None
+
+
+def oracle_scan(inp: dict, h0=None, softplus=True, nthreads=8):
+    import oracle
+    w = widened(inp)
+    return oracle.scan_fwd(w["u"], w["delta"], w["A"], w["B"], w["C"], w["D"], w["z"],
+                           w["delta_bias"], softplus, None if h0 is None else np.asarray(h0, np.float64),
+                           nthreads=nthreads)
+
+
+def scaled_err(got, ref) -> float:
+    """max|got - ref| / max|ref| (ref all zero -> plain max abs error)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    m = float(np.max(np.abs(ref)))
+    e = float(np.max(np.abs(got - ref)))
+    return e / m if m > 0 else e
+
+
+def assert_parity(got, ref, dtype: str, what: str = "y"):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = scaled_err(got, ref)
+    assert err <= TOL[dtype], f"{what}: scaled max error {err:.3e} > {TOL[dtype]:.0e}"
+    return err
+
+
+def sub_problem(inp: dict, b: int, ds) -> dict:
+    """The channels `ds` of batch row `b` as a batch-1 problem of its own
+    (rows are independent, so their results are those of the full problem)."""
+    ds = list(ds)
+    out = {"dtype": inp["dtype"]}
+    for k in ("u", "delta", "z"):
+        out[k] = None if inp.get(k) is None else np.ascontiguousarray(inp[k][b:b + 1, ds])
+    for k in ("B", "C"):
+        out[k] = np.ascontiguousarray(inp[k][b:b + 1])
+    out["A"] = np.ascontiguousarray(inp["A"][ds])
+    for k in ("D", "delta_bias"):
+        out[k] = None if inp.get(k) is None else np.ascontiguousarray(inp[k][ds])
+    return out
