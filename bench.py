@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective scan (S6) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one ssm_scan_fwd over the Mamba-2.8B-shaped layer (batch 16,
+D 5120, N 16, L 2048; bf16 inputs and output, fp32 state and arithmetic) with
+every input already resident in HBM.  The line also reports the decode
+workload (ssm_state_update, batch 256, D 5120, N 16, 64 steps) as a second
+object, the roofline of the dominant kernel, and the fp64 CPU oracle timed on
+a bounded sample of the same workload on this host.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan elements/s (batch·D·L) + achieved HBM GB/s vs peak, 1×MI355X"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, public spec
+# One fp32 VALU instruction per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz (the non-packed issue rate; packed fp32 doubles it to 157.3 TFLOP/s
+# of FMA, but packed fp32 is not used here).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Algorithmic VALU work of the scan per (element, state): Delta*A, exp2,
+# Delta*u*B, the state FMA and the readout FMA.
+OPS_PER_ELEMENT_STATE = 5
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_kernel_c3_traffic.json")
+KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, false>"
+KERNEL_SOURCES = ["selective_state_space_28_amd/csrc/scan_fwd.hip",
+                  "selective_state_space_28_amd/csrc/ssm_math.hpp"]
+
+
+def scan_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one scan: every input read once, y written
+    once, parameters once; the state never goes to HBM."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    el = cfg.batch * cfg.dim * cfg.seqlen
+    tok = el * s * (2 + (1 if cfg.gate else 0))          # u, delta (, z)
+    bc = 2 * cfg.batch * cfg.dstate * cfg.seqlen * s      # B, C
+    params = cfg.dim * cfg.dstate * 4 + cfg.dim * 4 * (2 if cfg.dskip else 1)
+    return tok + bc + params + el * s                    # + y
+
+
+def decode_bytes(cfg) -> int:
+    s = 2 if cfg.dtype == "bf16" else 4
+    rows = cfg.batch * cfg.dim
+    state = rows * cfg.dstate * 4 * 2                     # read + write
+    tok = rows * s * (2 + (1 if cfg.gate else 0)) + rows * s   # u, delta, z in; y out
+    bc = 2 * cfg.batch * cfg.dstate * s
+    params = cfg.dim * cfg.dstate * 4 + cfg.dim * 4 * (2 if cfg.dskip else 1)
+    return state + tok + bc + params
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per launch measured by rocprofv3 counters (committed under
+    profiles/), or None when absent or taken on a different kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for the "
+                         "HBM byte counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan is data-parallel over channels; multi-GPU sharding is described "
+              "in DESIGN.md but not built).", file=sys.stderr)
+        return 2
+
+    import torch
+    import selective_state_space_28_amd as ssm
+    import synth
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return 0
+    ssm.load()
+    cfg = synth.SCAN_CONFIGS["c3"]
+    t_gen = time.time()
+    inp = synth.make_scan_inputs(cfg)
+    gen_s = time.time() - t_gen
+
+    def dev_t(a, dt):
+        if a is None:
+            return None
+        if dt == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    dt = cfg.dtype
+    u, delta, B, C, z = (dev_t(inp[k], dt) for k in ("u", "delta", "B", "C", "z"))
+    A, D, bias = (dev_t(inp[k], "f32") for k in ("A", "D", "delta_bias"))
+    y = torch.empty_like(u)
+    need = ssm.ssm_scan_fwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, u.dtype)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssm.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, out=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    # per-launch events on the stream the kernels run on (torch's current one)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per = np.array([s.elapsed_time(e) for s, e in ev])  # ms
+    ms = float(per.mean())
+    wall_ms = wall * 1e3 / args.steps
+    elements = cfg.batch * cfg.dim * cfg.seqlen
+    value = elements / (ms * 1e-3)
+    alg_bytes = scan_bytes(cfg)
+    alg_gbps = alg_bytes / (ms * 1e-3) / 1e9
+    ops = elements * cfg.dstate * OPS_PER_ELEMENT_STATE
+    alu_tops = ops / (ms * 1e-3) / 1e12
+    # the binding roof is the one whose lower-bound time is larger
+    t_hbm = alg_bytes / (HBM_PEAK_GBPS * 1e9)
+    t_alu = ops / (VALU_PEAK_TOPS * 1e12)
+    traffic = traffic_per_launch()
+    if t_alu >= t_hbm:
+        roof = {"bound": "alu", "achieved": round(alu_tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
+                "unit": "TOP/s", "frac": round(alu_tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
+                "kernel": KERNEL_NAME,
+                "work_per_launch": {"ops": ops, "bytes": alg_bytes}}
+    else:
+        roof = {"bound": "hbm", "achieved": round(alg_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(alg_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": KERNEL_NAME,
+                "work_per_launch": {"ops": ops, "bytes": alg_bytes}}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "mamba-2.8b-shaped layer scan: batch 16, D 5120, N 16, L 2048, "
+                               "bf16 inputs/output, fp32 state, silu gate, D-skip, A jittered",
+                   "batch": cfg.batch, "dim": cfg.dim, "dstate": cfg.dstate,
+                   "seqlen": cfg.seqlen, "io_dtype": "bf16", "seed": cfg.seed},
+        "hbm": {"algorithmic_bytes": alg_bytes, "algorithmic_GBps": round(alg_gbps, 1),
+                "frac_of_peak": round(alg_gbps / HBM_PEAK_GBPS, 4),
+                "measured_bytes_per_launch": traffic,
+                "measured_GBps": (round(traffic / (ms * 1e-3) / 1e9, 1) if traffic else None)},
+        "wall_ms_per_step": wall_ms,
+        "roofline": roof,
+    }
+    del u, delta, B, C, z, y, ws
+
+    if not args.no_decode:
+        out["decode"] = bench_decode(dev, args.decode_steps)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp)
+    out["input_generation_s"] = round(gen_s, 2)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def bench_decode(dev, steps):
+    """The decode workload: 64 successive one-token steps on a persistent
+    fp32 state (batch 256, D 5120, N 16), token inputs resident in HBM."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    import synth
+    cfg = synth.DECODE_CONFIG
+    p = synth.make_decode_params(cfg)
+    st = torch.from_numpy(p["h0"]).to(dev)
+    A = torch.from_numpy(p["A"]).to(dev)
+    D = torch.from_numpy(p["D"]).to(dev)
+    bias = torch.from_numpy(p["delta_bias"]).to(dev)
+    toks = []
+    for s in range(steps):
+        t = synth.make_decode_step(cfg, s)
+        toks.append({k: torch.from_numpy(t[k].view(np.int16)).view(torch.bfloat16).to(dev)
+                     for k in ("u", "delta", "B", "C", "z")})
+    ys = [torch.empty_like(toks[0]["u"]) for _ in range(steps)]
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        for s in range(steps):
+            t = toks[s]
+            ssm.ssm_state_update(st, t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias, out=ys[s])
+
+    run()  # warm-up (the state keeps evolving; the work per step is the same)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = decode_bytes(cfg)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "decode ssm_state_update: batch 256, D 5120, N 16, bf16 tokens, fp32 state",
+            "steps": steps, "ms_per_token_step": ms,
+            "channels_per_s": cfg.batch * cfg.dim / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                         "bytes_per_launch": nbytes,
+                         "note": "the 84 MB state fits the 256 MB last-level cache, so "
+                                 "successive steps may be served partly from it"}}
+
+
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle as it stands, timed on this host over a bounded sample
+    of the same workload: the first batch rows' channels, whole sequences."""
+    import oracle
+    import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(os.cpu_count() or 1, 16)
+    nb = 8
+    w = {k: synth.widen(inp[k][:nb], cfg.dtype) for k in ("u", "delta", "B", "C", "z")}
+    t0 = time.perf_counter()
+    oracle.scan_fwd(w["u"], w["delta"], inp["A"], w["B"], w["C"], inp["D"], w["z"],
+                    inp["delta_bias"], True, None, nthreads=threads)
+    sec = time.perf_counter() - t0
+    el = nb * cfg.dim * cfg.seqlen
+    return {"value": el / sec, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": f"batch rows 0..{nb - 1} of the same workload ({nb}x{cfg.dim}x{cfg.seqlen} "
+                      f"elements, N {cfg.dstate}), fp64, {threads} threads, {sec:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

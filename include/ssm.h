@@ -76,9 +76,11 @@ typedef enum {
 
 /*
  * ssm_scan_fwd_workspace_bytes -- bytes of device workspace that
- * ssm_scan_fwd needs for this problem (0 when the sequence is not split
- * across workgroups).  Pure host function: no HIP call.  Returns 0 for
- * arguments that ssm_scan_fwd would reject.
+ * ssm_scan_fwd needs for this problem: fp32 copies of B and C laid out for
+ * the kernel (batch * seqlen * 2 * dstate floats), plus, when the sequence is
+ * split across workgroups, each segment's end state and Delta sum.  Pure host
+ * function: no HIP call.  Returns 0 for an empty problem and for arguments
+ * that ssm_scan_fwd would reject.
  */
 size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seqlen,
                                     int dtype);
@@ -99,8 +101,9 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
  *                     be u, delta or z
  *   last_state   out  (batch, dim, dstate) float32           NULL -> not written
  *   workspace    scratch of at least ssm_scan_fwd_workspace_bytes(...) bytes,
- *                device memory owned by the caller; NULL allowed when that is 0.
- *                Its contents on entry do not matter.
+ *                256-byte aligned device memory owned by the caller (NULL only
+ *                when the query returns 0).  Its contents on entry do not
+ *                matter; calls sharing one workspace must not overlap.
  *   batch, dim >= 0; dstate in {1,2,4,8,16}; seqlen >= 0.  seqlen == 0 only
  *   writes last_state (= h0, or zeros).
  */

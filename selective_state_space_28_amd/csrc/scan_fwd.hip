@@ -8,20 +8,24 @@
 // State-space models (Mamba, S4)", recurrent view).
 //
 // Design (channel-parallel, one fused pass over HBM):
+//  * pack_bc_kernel first rewrites B and C (tiny next to u, delta, z, y:
+//    they are shared by all channels) as fp32 records, one per (batch row,
+//    state group, step) holding that group's B then C values.  In the scan a
+//    wave's record for step t is wave-uniform, so it is read with scalar
+//    loads straight into SGPR operands: no VGPRs, no VALU conversions.
 //  * A workgroup owns 64 consecutive channels of one batch row and G state
 //    groups; wave g holds NS = N/G states of each of its 64 channels in
 //    VGPRs (lane = channel).  The state never touches HBM.
 //  * The sequence is walked in tiles of TL steps.  Per tile, all threads
-//    load u, delta (and z) with coalesced 16-byte loads along L, compute
+//    load u, delta (and z) with coalesced vector loads along L (the next
+//    tile's loads are issued before the current tile's recurrence), compute
 //    Delta = softplus(delta + bias) and Delta*u once per element, and stage
-//    them transposed in LDS (one float2 per (t, channel)).
-//  * Each wave then runs the TL steps of the recurrence for its states.
-//    B[b,n,t] and C[b,n,t] are the same for every lane of a wave (shared by
-//    all channels), so they are scalar loads, not VGPR traffic.  Per
-//    (element, state) the loop is one v_exp_f32 and four fp32 VALU ops.
-//  * The G partial readouts per (t, channel) are summed through LDS in a
+//    them transposed in LDS (one float2 per (step, channel)).
+//  * Each wave runs the TL steps of the recurrence for its states: per
+//    (element, state) one v_exp_f32 and four fp32 VALU ops.
+//  * The G partial readouts per (step, channel) are summed through LDS in a
 //    fixed order, D*u and the silu gate applied, and y stored with coalesced
-//    16-byte stores.
+//    vector stores.
 //  * Long sequences with too few channels to fill the GPU are split into
 //    segments.  The affine steps compose associatively ("NN LAB" Mamba page,
 //    "The Associative Property of Linear Recurrence"): a first launch runs
@@ -44,25 +48,75 @@ struct ScanSizes {
   int ncg;           // 64-channel groups per batch row
   int softplus;
   int vec;
+  int ncu;           // compute units of the device (blocks launched per "rank")
+  int prio_epochs;   // priority rotations per segment (0: no rotation)
 };
 
-template <typename T, int NS, int G, int TL, bool AGG>
-__global__ __launch_bounds__(64 * G) void scan_kernel(
-    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
-    const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ Dskip,
-    const T* __restrict__ z, const float* __restrict__ bias, const float* __restrict__ h0,
-    T* __restrict__ y, float* __restrict__ last_state, float* __restrict__ ws_hend,
-    float* __restrict__ ws_sumdt, const ScanSizes p) {
+// ---- B, C -> fp32 records (batch, state group, step, [B x NS, C x NS]) ------
+template <typename T, int NS, int G>
+__global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B,
+                                                      const T* __restrict__ C,
+                                                      float* __restrict__ bc, int64_t L,
+                                                      int tblocks) {
   constexpr int N = NS * G;
-  constexpr int E = TL / G;  // elements per thread in the load / store phases
-  static_assert(TL % G == 0, "tile must split evenly over the state groups");
+  const int b = blockIdx.x / tblocks;
+  const int64_t t = (int64_t)(blockIdx.x % tblocks) * 256 + threadIdx.x;
+  if (t >= L) return;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float v[2 * NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int64_t src = ((int64_t)b * N + g * NS + k) * L + t;
+      v[k] = Elem<T>::load(B + src);
+      v[NS + k] = Elem<T>::load(C + src);
+    }
+    float* dst = bc + (((int64_t)b * G + g) * L + t) * (2 * NS);
+    if constexpr (NS == 4) {
+      reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2 * NS; ++k) dst[k] = v[k];
+    }
+  }
+}
 
-  __shared__ float2 s_ddu[TL][64];                            // (Delta, Delta*u)
-  __shared__ float s_y[AGG ? 1 : G][AGG ? 1 : TL][64];        // partial readouts
+// Tiles whose u/delta/z loads are issued together: enough to cover a
+// 128-byte line of every row (so each line is fetched once, not once per
+// tile), within a budget of 24 VGPRs of raw words per thread.
+template <typename T, int G, int TL>
+constexpr int load_block_tiles() {
+  constexpr int W = (TL / G) * (int)sizeof(T) / 4;
+  constexpr int by_line = 128 / (TL * (int)sizeof(T));
+  constexpr int by_regs = 8 / W;
+  constexpr int kt = by_line < by_regs ? by_line : by_regs;
+  return kt < 1 ? 1 : (kt > 4 ? 4 : kt);
+}
+
+template <typename T, int NS, int G, int TL, bool AGG>
+__global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
+    const float* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
+    const float* __restrict__ bias, const float* __restrict__ h0, T* __restrict__ y,
+    float* __restrict__ last_state, float* __restrict__ ws_hend, float* __restrict__ ws_sumdt,
+    const ScanSizes p) {
+  constexpr int N = NS * G;
+  constexpr int E = TL / G;                     // elements per thread, load/store phases
+  constexpr int W = E * (int)sizeof(T) / 4;     // their size in 32-bit words
+  constexpr int KT = load_block_tiles<T, G, TL>();
+  constexpr int LDW = 65;                       // padded LDS row: spreads the banks
+  constexpr int CH = 2;                         // steps per software-pipelined chunk
+  constexpr int R = 2 * NS;                     // floats per B, C record
+  static_assert(TL % G == 0 && (E * (int)sizeof(T)) % 4 == 0, "tile must split into words");
+  static_assert(TL % CH == 0, "tile must split into chunks");
+
+  __shared__ float2 s_ddu[TL][LDW];                           // (Delta, Delta*u)
+  __shared__ float s_y[AGG ? 1 : G][AGG ? 1 : TL][LDW];       // partial readouts
 
   // ---- block -> (batch row, channel group, segment) --------------------------
   // Consecutive block ids go to different XCDs; regroup so that the blocks an
-  // XCD runs share batch rows (and hence B and C in that XCD's L2).
+  // XCD runs share batch rows (and hence the B, C records in its L2).
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
@@ -107,130 +161,209 @@ __global__ __launch_bounds__(64 * G) void scan_kernel(
   // ---- load-phase role: thread -> (channel cc, run of E steps) ---------------
   const int cc = tid / G;
   const int chunk = tid % G;
+  const int r0 = chunk * E;                 // first step of this thread's run in a tile
   const int dcc = cg * 64 + cc;
   const bool ccvalid = dcc < p.dim;
-  const int64_t rowcc = (int64_t)b * p.dim + dcc;
+  const int64_t rowcc = (int64_t)b * p.dim + (ccvalid ? dcc : 0);
   const float bias_cc = (bias != nullptr && ccvalid) ? bias[dcc] : 0.0f;
   const float D_cc = (Dskip != nullptr && ccvalid) ? Dskip[dcc] : 0.0f;
-  const bool has_z = (z != nullptr);
+  const bool has_z = !AGG && (z != nullptr);
+  const bool vec = p.vec != 0;
 
-  const T* Bw = B + ((int64_t)b * N + g * NS) * L;  // wave-uniform
-  const T* Cw = C + ((int64_t)b * N + g * NS) * L;
+  const float* bcw = bc + ((int64_t)b * G + g) * L * R;  // wave-uniform records
+
+  // raw words of this thread's runs in the KT tiles of the current load block
+  uint32_t pu[KT][W], pd[KT][W], pz[KT][W];
+  auto block_full = [&](int64_t tb) { return vec && tb + KT * TL <= seg_end; };
+  auto fetch_block = [&](int64_t tb) {
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int64_t off = rowcc * L + tb + j * TL + r0;
+      load_words<W>(u + off, pu[j]);
+      load_words<W>(delta + off, pd[j]);
+      if (has_z) load_words<W>(z + off, pz[j]);
+    }
+  };
+  if (ccvalid && block_full(seg_begin)) fetch_block(seg_begin);
 
   double sumdt = 0.0;
 
-  for (int64_t t0 = seg_begin; t0 < seg_end; t0 += TL) {
-    const int tvalid = (int)((seg_end - t0) < TL ? (seg_end - t0) : TL);
-    const int r0 = chunk * E;                  // first step of this thread's run
-    const int rn = tvalid - r0;                // steps of the run in range
-    const bool full = rn >= E;
+  // The wave arbiter prefers older waves, so of the workgroups resident on a
+  // CU the oldest ones would race ahead and the youngest run alone at the
+  // end, unable to fill the SIMDs.  Blocks are dispatched round-robin over
+  // the CUs, so blockIdx / ncu is a block's age rank on its CU; rotating a
+  // raised wave priority over the ranks keeps them progressing together.
+  const int prio_rank = (int)(blockIdx.x / (unsigned)p.ncu) % 5;
+  const int64_t nblocks = (seg_end - seg_begin + KT * TL - 1) / (KT * TL);
+  const int64_t epoch_len = p.prio_epochs > 0 ? (nblocks + p.prio_epochs - 1) / p.prio_epochs : 0;
+  int64_t blk = 0;
 
-    // ---- load u, delta (z), form Delta and Delta*u, stage in LDS -------------
-    float uu[E], dd[E], zz[E];
-    if (ccvalid && full) {
-      const int64_t off = rowcc * L + t0 + r0;
-      load_run<E>(u + off, p.vec != 0, uu);
-      load_run<E>(delta + off, p.vec != 0, dd);
-      if (!AGG && has_z) load_run<E>(z + off, p.vec != 0, zz);
-    } else {
+  for (int64_t tb = seg_begin; tb < seg_end; tb += KT * TL, ++blk) {
+    const bool fast = block_full(tb);
+    if (epoch_len > 0 && blk % epoch_len == 0) {
+      const int lvl = (int)((prio_rank + blk / epoch_len) % 5);
+      if (lvl <= 1) __builtin_amdgcn_s_setprio(0);
+      else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
+      else if (lvl == 3) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(3);
+    }
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int64_t t0 = tb + j * TL;
+      if (t0 >= seg_end) break;
+      const int tvalid = (int)((seg_end - t0) < TL ? (seg_end - t0) : TL);
+
+      // ---- this tile's u, delta (z) -> Delta, Delta*u in LDS ------------------
+      float uu[E], dd[E], zz[E];
+      if (fast && ccvalid) {
+        words_to_floats<T, E>(pu[j], uu);
+        words_to_floats<T, E>(pd[j], dd);
+        if (has_z) words_to_floats<T, E>(pz[j], zz);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool ok = ccvalid && r0 + e < tvalid;
+          const int64_t off = rowcc * L + t0 + r0 + e;
+          uu[e] = ok ? Elem<T>::load(u + off) : 0.0f;
+          dd[e] = ok ? Elem<T>::load(delta + off) : 0.0f;
+          zz[e] = (ok && has_z) ? Elem<T>::load(z + off) : 0.0f;
+        }
+      }
+      // Entries of channels past dim, or of steps past the tile end, hold
+      // harmless values (u = 0 there, so Delta*u = 0): those steps are never
+      // run and those lanes never store.
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool ok = ccvalid && e < rn;
-        const int64_t off = rowcc * L + t0 + r0 + e;
-        uu[e] = ok ? Elem<T>::load(u + off) : 0.0f;
-        dd[e] = ok ? Elem<T>::load(delta + off) : 0.0f;
-        zz[e] = (ok && !AGG && has_z) ? Elem<T>::load(z + off) : 0.0f;
+        const float x = dd[e] + bias_cc;
+        const float dt = p.softplus ? softplus_f32(x) : x;
+        s_ddu[r0 + e][cc] = make_float2(dt, dt * uu[e]);
       }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float x = dd[e] + bias_cc;
-      float dt = p.softplus ? softplus_f32(x) : x;
-      if (!(ccvalid && e < rn)) dt = 0.0f;
-      s_ddu[r0 + e][cc] = make_float2(dt, dt * uu[e]);
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // ---- the recurrence: TL steps x NS states per lane -------------------------
-    const T* Bt = Bw + t0;
-    const T* Ct = Cw + t0;
-    if (tvalid == TL) {
-#pragma unroll 4
-      for (int t = 0; t < TL; ++t) {
-        const float2 v = s_ddu[t][lane];
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NS; ++k) {
-          const float bv = Elem<T>::load(Bt + (int64_t)k * L + t);
-          const float cv = Elem<T>::load(Ct + (int64_t)k * L + t);
-          const float a = exp2_hw(v.x * A2[k]);
-          h[k] = __builtin_fmaf(a, h[k], v.y * bv);
-          acc = __builtin_fmaf(cv, h[k], acc);
-        }
-        if (!AGG) s_y[AGG ? 0 : g][AGG ? 0 : t][lane] = acc;
-        if (AGG && g == 0) sumdt += (double)v.x;
+      // ---- after the block's last tile is staged, issue the next block ------
+      if (j == KT - 1) {
+        const int64_t tn = tb + KT * TL;
+        if (ccvalid && tn < seg_end && block_full(tn)) fetch_block(tn);
       }
-    } else {
-      for (int t = 0; t < tvalid; ++t) {
-        const float2 v = s_ddu[t][lane];
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NS; ++k) {
-          const float bv = Elem<T>::load(Bt + (int64_t)k * L + t);
-          const float cv = Elem<T>::load(Ct + (int64_t)k * L + t);
-          const float a = exp2_hw(v.x * A2[k]);
-          h[k] = __builtin_fmaf(a, h[k], v.y * bv);
-          acc = __builtin_fmaf(cv, h[k], acc);
-        }
-        if (!AGG) s_y[AGG ? 0 : g][AGG ? 0 : t][lane] = acc;
-        if (AGG && g == 0) sumdt += (double)v.x;
-      }
-    }
-    __syncthreads();
 
-    // ---- readout: sum the G partials, D-skip, gate, store y --------------------
-    if (!AGG) {
-      float yv[E];
+      // ---- the recurrence: TL steps x NS states per lane ---------------------
+      const float* bct = bcw + t0 * R;
+      if (tvalid == TL) {
+        // chunks of CH steps; the next chunk's LDS and scalar loads are issued
+        // before the current chunk's arithmetic so their latency is covered
+        float2 vc[CH], vn[CH];
+        float rc[CH][R], rn[CH][R];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float s = 0.0f;
+        for (int i = 0; i < CH; ++i) {
+          vc[i] = s_ddu[i][lane];
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) s += s_y[AGG ? 0 : gg][AGG ? 0 : r0 + e][cc];
-        s = __builtin_fmaf(D_cc, uu[e], s);
-        if (has_z) s *= silu_f32(zz[e]);
-        yv[e] = s;
-      }
-      if (ccvalid) {
-        const int64_t off = rowcc * L + t0 + r0;
-        if (full) {
-          store_run<E>(y + off, p.vec != 0, yv);
-        } else {
+          for (int q = 0; q < R; ++q) rc[i][q] = bct[i * R + q];
+        }
 #pragma unroll
-          for (int e = 0; e < E; ++e)
-            if (e < rn) Elem<T>::store(y + off + e, yv[e]);
+        for (int c = 0; c < TL / CH; ++c) {
+          if (c + 1 < TL / CH) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+              vn[i] = s_ddu[(c + 1) * CH + i][lane];
+#pragma unroll
+              for (int q = 0; q < R; ++q) rn[i][q] = bct[((c + 1) * CH + i) * R + q];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+              const float a = exp2_hw(vc[i].x * A2[k]);
+              h[k] = __builtin_fmaf(a, h[k], vc[i].y * rc[i][k]);
+              acc = __builtin_fmaf(rc[i][NS + k], h[k], acc);
+            }
+            if constexpr (!AGG) {
+              s_y[g][c * CH + i][lane] = acc;
+            } else {
+              if (g == 0) sumdt += (double)vc[i].x;
+            }
+          }
+          if (c + 1 < TL / CH) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+              vc[i] = vn[i];
+#pragma unroll
+              for (int q = 0; q < R; ++q) rc[i][q] = rn[i][q];
+            }
+          }
+        }
+      } else {
+        for (int t = 0; t < tvalid; ++t) {
+          const float2 v = s_ddu[t][lane];
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < NS; ++k) {
+            const float a = exp2_hw(v.x * A2[k]);
+            h[k] = __builtin_fmaf(a, h[k], v.y * bct[t * R + k]);
+            acc = __builtin_fmaf(bct[t * R + NS + k], h[k], acc);
+          }
+          if constexpr (!AGG) {
+            s_y[g][t][lane] = acc;
+          } else {
+            if (g == 0) sumdt += (double)v.x;
+          }
         }
       }
+      __syncthreads();
+
+      // ---- readout: sum the G partials, D-skip, gate, store y ------------------
+      if constexpr (!AGG) {
+        float yv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float s = s_y[0][r0 + e][cc];
+#pragma unroll
+          for (int gg = 1; gg < G; ++gg) s += s_y[gg][r0 + e][cc];
+          s = __builtin_fmaf(D_cc, uu[e], s);
+          if (has_z) s *= silu_f32(zz[e]);
+          yv[e] = s;
+        }
+        if (ccvalid) {
+          const int64_t off = rowcc * L + t0 + r0;
+          if (vec && tvalid == TL) {
+            store_floats<T, E>(y + off, yv);
+          } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if (r0 + e < tvalid) Elem<T>::store(y + off + e, yv[e]);
+          }
+        }
+      }
+      // The next tile's LDS writes (s_ddu) are not read by this readout, and its
+      // s_y writes come after the next barrier, so no third barrier is needed.
     }
-    // The next tile's LDS writes (s_ddu) are not read by this readout, and its
-    // s_y writes come after the next barrier, so no third barrier is needed.
   }
 
   // ---- segment results ---------------------------------------------------------
   if (!dvalid) return;
-  if (AGG) {
+  if constexpr (AGG) {
     const int64_t plane = (int64_t)p.batch * p.dim;
 #pragma unroll
     for (int k = 0; k < NS; ++k) ws_hend[(seg * plane + row) * N + g * NS + k] = h[k];
     if (g == 0) ws_sumdt[seg * plane + row] = (float)sumdt;
-  } else if (last_state != nullptr && seg == p.nseg - 1) {
+  } else {
+    if (last_state != nullptr && seg == p.nseg - 1) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k) last_state[row * N + g * NS + k] = h[k];
+      for (int k = 0; k < NS; ++k) last_state[row * N + g * NS + k] = h[k];
+    }
   }
 }
 
 template <typename T, int NS, int G>
 static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   constexpr int TL = kScanTile;
+  const T* B = static_cast<const T*>(a.B);
+  const T* C = static_cast<const T*>(a.C);
+  const int tblocks = (int)((a.seqlen + 255) / 256);
+  pack_bc_kernel<T, NS, G><<<(unsigned)((int64_t)a.batch * tblocks), 256, 0, stream>>>(
+      B, C, a.ws_bc, a.seqlen, tblocks);
+
   ScanSizes s;
   s.batch = a.batch;
   s.dim = a.dim;
@@ -240,10 +373,10 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   s.ncg = (a.dim + 63) / 64;
   s.softplus = a.softplus;
   s.vec = a.vec;
+  s.ncu = a.ncu > 0 ? a.ncu : 1;
+  s.prio_epochs = a.prio_epochs;
   const T* u = static_cast<const T*>(a.u);
   const T* dl = static_cast<const T*>(a.delta);
-  const T* B = static_cast<const T*>(a.B);
-  const T* C = static_cast<const T*>(a.C);
   const T* z = static_cast<const T*>(a.z);
   T* y = static_cast<T*>(a.y);
   const int64_t base = (int64_t)a.batch * s.ncg;
@@ -251,12 +384,12 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
     s.nseg_launch = a.nseg - 1;
     const unsigned grid = (unsigned)(base * s.nseg_launch);
     scan_kernel<T, NS, G, TL, true><<<grid, 64 * G, 0, stream>>>(
-        u, dl, a.A, B, C, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
+        u, dl, a.A, a.ws_bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
   }
   s.nseg_launch = a.nseg;
   const unsigned grid = (unsigned)(base * s.nseg_launch);
   scan_kernel<T, NS, G, TL, false><<<grid, 64 * G, 0, stream>>>(
-      u, dl, a.A, B, C, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
+      u, dl, a.A, a.ws_bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 //
 // Every check happens before the first HIP call, so a rejected call enqueues
 // nothing and the validation can be exercised without a GPU.
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <cstdlib>
@@ -24,6 +25,32 @@ struct SegPlan {
   int nseg;
   int64_t seglen;
 };
+
+// Compute units of the current device, cached per device ordinal.
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Wave-priority rotations per segment (SSM_SCAN_PRIO_EPOCHS overrides; 0
+// switches the rotation off).
+int prio_epochs() {
+  if (const char* env = std::getenv("SSM_SCAN_PRIO_EPOCHS")) {
+    const int v = std::atoi(env);
+    if (v >= 0) return v;
+  }
+  return 8;
+}
 
 bool dstate_ok(int n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
 
@@ -57,12 +84,29 @@ SegPlan plan_segments(int batch, int dim, int dstate, int64_t L) {
   return SegPlan{(int)(nseg < 1 ? 1 : nseg), seglen};
 }
 
-size_t workspace_for(int batch, int dim, int dstate, const SegPlan& sp) {
-  if (sp.nseg <= 1) return 0;
+// Workspace: the fp32 B, C records (always), then for a split sequence the
+// end state and Delta sum of every segment but the last; each part 256-byte
+// aligned.
+struct WsLayout {
+  size_t bc, hend, sumdt, total;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+WsLayout workspace_layout(int batch, int dim, int dstate, int64_t L, const SegPlan& sp) {
+  WsLayout w{};
   const size_t plane = (size_t)batch * (size_t)dim;
-  const size_t hend = (size_t)(sp.nseg - 1) * plane * (size_t)dstate * sizeof(float);
-  const size_t sumdt = (size_t)(sp.nseg - 1) * plane * sizeof(float);
-  return ((hend + 255) / 256) * 256 + sumdt;
+  w.bc = 0;
+  w.hend = round256((size_t)batch * (size_t)L * 2 * (size_t)dstate * sizeof(float));
+  size_t end = w.hend;
+  if (sp.nseg > 1) {
+    w.sumdt = w.hend + round256((size_t)(sp.nseg - 1) * plane * (size_t)dstate * sizeof(float));
+    end = w.sumdt + round256((size_t)(sp.nseg - 1) * plane * sizeof(float));
+  } else {
+    w.sumdt = end;
+  }
+  w.total = end;
+  return w;
 }
 
 bool aligned(const void* p, size_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -81,7 +125,8 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
   if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return 0;
   if (batch == 0 || dim == 0 || seqlen == 0) return 0;
-  return workspace_for(batch, dim, dstate, plan_segments(batch, dim, dstate, seqlen));
+  return workspace_layout(batch, dim, dstate, seqlen, plan_segments(batch, dim, dstate, seqlen))
+      .total;
 }
 
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -97,7 +142,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
       !aligned(z, es) || !aligned(y, es) || !aligned(A, 4) || !aligned(D_skip, 4) ||
       !aligned(delta_bias, 4) || !aligned(h0, 4) || !aligned(last_state, 4) ||
-      !aligned(workspace, 4))
+      !aligned(workspace, 256))
     return SSM_ERR_ALIGN;
   if (y != nullptr && (y == u || y == delta || (z != nullptr && y == z))) return SSM_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -111,9 +156,10 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
 
   const SegPlan sp = plan_segments(batch, dim, dstate, seqlen);
   const int64_t blocks = (int64_t)batch * ((dim + 63) / 64) * sp.nseg;
-  if (blocks > INT_MAX) return SSM_ERR_SHAPE;
-  const size_t need = workspace_for(batch, dim, dstate, sp);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+  const int64_t pack_blocks = (int64_t)batch * ((seqlen + 255) / 256);
+  if (blocks > INT_MAX || pack_blocks > INT_MAX) return SSM_ERR_SHAPE;
+  const WsLayout wl = workspace_layout(batch, dim, dstate, seqlen, sp);
+  if (workspace == nullptr || workspace_bytes < wl.total) return SSM_ERR_WORKSPACE;
 
   ssm::ScanLaunch a{};
   a.u = u;
@@ -127,11 +173,11 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   a.h0 = h0;
   a.y = y;
   a.last_state = last_state;
-  if (need > 0) {
-    const size_t plane = (size_t)batch * (size_t)dim;
-    const size_t hend = (size_t)(sp.nseg - 1) * plane * (size_t)dstate * sizeof(float);
-    a.ws_hend = static_cast<float*>(workspace);
-    a.ws_sumdt = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((hend + 255) / 256) * 256);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_bc = reinterpret_cast<float*>(ws + wl.bc);
+  if (sp.nseg > 1) {
+    a.ws_hend = reinterpret_cast<float*>(ws + wl.hend);
+    a.ws_sumdt = reinterpret_cast<float*>(ws + wl.sumdt);
   }
   a.batch = batch;
   a.dim = dim;
@@ -143,6 +189,8 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   const bool rows16 = ((int64_t)es * seqlen) % 16 == 0;
   a.vec = rows16 && aligned(u, 16) && aligned(delta, 16) && aligned(z, 16) && aligned(y, 16);
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
+  a.ncu = device_cu_count();
+  a.prio_epochs = prio_epochs();
   return ssm::launch_scan_fwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

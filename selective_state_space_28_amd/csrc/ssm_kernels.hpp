@@ -8,7 +8,7 @@
 namespace ssm {
 
 // Time steps one workgroup stages per tile of the forward scan.
-constexpr int kScanTile = 32;
+constexpr int kScanTile = 16;
 
 // Storage type of the per-token tensors.
 enum class Dtype { F32 = 0, BF16 = 1 };
@@ -25,6 +25,7 @@ struct ScanLaunch {
   const float* h0;        // nullable
   void* y;
   float* last_state;      // nullable
+  float* ws_bc;           // (batch, G, seqlen, 2*dstate/G) fp32 B, C records
   float* ws_hend;         // (nseg-1, batch, dim, dstate) when nseg > 1
   float* ws_sumdt;        // (nseg-1, batch, dim) when nseg > 1
   int batch, dim, dstate;
@@ -33,6 +34,8 @@ struct ScanLaunch {
   int nseg;               // segments the sequence is split into
   int softplus;
   int vec;                // 16-byte vector loads/stores allowed
+  int ncu;                // compute units of the device
+  int prio_epochs;        // wave-priority rotations per segment (0: none)
   Dtype dtype;
 };
 

@@ -18,31 +18,24 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// ln(1 + w) for w in [0, 1].  Below 1/16 an 8-term Taylor series (truncation
-// below 2^-34 relative).  Above, the hardware log of u = fl(1 + w), whose
-// argument is then far enough from 1 for full relative precision, times
-// w / (u - 1) to undo the rounding of u (u - 1 is exact).
+// ln(1 + w) for w in [0, 1], without branches.  u = fl(1 + w) is rounded;
+// c = w - (u - 1) is the rounding error exactly (u - 1 is exact), and
+// ln(1 + w) = ln(u + c) = ln(u) + c/u + O(c^2).  Replacing c/u by c changes
+// the result by c*(u - 1)/u, below half an ulp of ln(u) over the whole range,
+// so ln(1 + w) = ln(u) + c to working precision.  When w is below half an
+// ulp of 1, u = 1 and the result is c = w.  The hardware log2 keeps full
+// relative precision for u just above 1.
 __device__ __forceinline__ float log1p_unit(float w) {
-  if (w < 0.0625f) {
-    float p = -1.0f / 8.0f;
-    p = __builtin_fmaf(p, w, 1.0f / 7.0f);
-    p = __builtin_fmaf(p, w, -1.0f / 6.0f);
-    p = __builtin_fmaf(p, w, 1.0f / 5.0f);
-    p = __builtin_fmaf(p, w, -1.0f / 4.0f);
-    p = __builtin_fmaf(p, w, 1.0f / 3.0f);
-    p = __builtin_fmaf(p, w, -0.5f);
-    p = __builtin_fmaf(p, w, 1.0f);
-    return p * w;
-  }
   const float u = 1.0f + w;
-  return log2_hw(u) * kLn2 * (w * rcp_hw(u - 1.0f));
+  const float c = w - (u - 1.0f);
+  return __builtin_fmaf(log2_hw(u), kLn2, c);
 }
 
 // softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + e^-|x|): no overflow for
 // large x and no cancellation for very negative x.
 __device__ __forceinline__ float softplus_f32(float x) {
   const float w = exp2_hw(-__builtin_fabsf(x) * kLog2e);
-  return __builtin_fmaxf(x, 0.0f) + log1p_unit(w);
+  return (x > 0.0f ? x : 0.0f) + log1p_unit(w);
 }
 
 // silu(z) = z / (1 + e^-z).  For z -> -inf the reciprocal goes to 0 and the
@@ -83,73 +76,67 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Load E consecutive elements starting at p into fp32 registers.  The caller
-// guarantees all E are in range; `vec` says p is 16-byte aligned.
-template <typename T, int E>
-__device__ __forceinline__ void load_run(const T* __restrict__ p, bool vec, float (&out)[E]);
-
-template <int E>
-__device__ __forceinline__ void load_run(const float* __restrict__ p, bool vec, float (&out)[E]) {
-  if (vec && (E % 4) == 0) {
+// ---- vectorised runs of E consecutive elements ---------------------------------
+// A run of E elements of T is W = E*sizeof(T)/4 32-bit words.  Callers pass
+// pointers aligned to the run size (16 bytes when W is a multiple of 4).
+template <int W>
+__device__ __forceinline__ void load_words(const void* __restrict__ p, uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < E / 4; ++i) {
-      const float4 v = reinterpret_cast<const float4*>(p)[i];
-      out[4 * i + 0] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < E; ++i) out[i] = p[i];
-  }
-}
-
-template <int E>
-__device__ __forceinline__ void load_run(const uint16_t* __restrict__ p, bool vec, float (&out)[E]) {
-  if (vec && (E % 8) == 0) {
-#pragma unroll
-    for (int i = 0; i < E / 8; ++i) {
+    for (int i = 0; i < W / 4; ++i) {
       const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-      out[8 * i + 0] = bf16_lo(v.x); out[8 * i + 1] = bf16_hi(v.x);
-      out[8 * i + 2] = bf16_lo(v.y); out[8 * i + 3] = bf16_hi(v.y);
-      out[8 * i + 4] = bf16_lo(v.z); out[8 * i + 5] = bf16_hi(v.z);
-      out[8 * i + 6] = bf16_lo(v.w); out[8 * i + 7] = bf16_hi(v.w);
+      w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
+  } else if constexpr (W == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
   } else {
 #pragma unroll
-    for (int i = 0; i < E; ++i) out[i] = Elem<uint16_t>::load(p + i);
+    for (int i = 0; i < W; ++i) w[i] = reinterpret_cast<const uint32_t*>(p)[i];
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void store_words(void* __restrict__ p, const uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i)
+      reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else if constexpr (W == 2) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) reinterpret_cast<uint32_t*>(p)[i] = w[i];
   }
 }
 
 template <typename T, int E>
-__device__ __forceinline__ void store_run(T* __restrict__ p, bool vec, const float (&v)[E]);
-
-template <int E>
-__device__ __forceinline__ void store_run(float* __restrict__ p, bool vec, const float (&v)[E]) {
-  if (vec && (E % 4) == 0) {
+__device__ __forceinline__ void words_to_floats(const uint32_t (&w)[E * sizeof(T) / 4], float (&f)[E]) {
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int i = 0; i < E / 4; ++i)
-      reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < E; ++i) p[i] = v[i];
-  }
-}
-
-template <int E>
-__device__ __forceinline__ void store_run(uint16_t* __restrict__ p, bool vec, const float (&v)[E]) {
-  if (vec && (E % 8) == 0) {
-#pragma unroll
-    for (int i = 0; i < E / 8; ++i) {
-      uint4 w;
-      w.x = pack_bf16x2(v[8 * i + 0], v[8 * i + 1]);
-      w.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
-      w.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
-      w.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
-      reinterpret_cast<uint4*>(p)[i] = w;
+    for (int i = 0; i < E / 2; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < E; ++i) Elem<uint16_t>::store(p + i, v[i]);
+    for (int i = 0; i < E; ++i) f[i] = __uint_as_float(w[i]);
   }
+}
+
+// Store E floats as T (bf16: round to nearest even) with vector stores.
+template <typename T, int E>
+__device__ __forceinline__ void store_floats(T* __restrict__ p, const float (&f)[E]) {
+  constexpr int W = E * (int)sizeof(T) / 4;
+  uint32_t w[W];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = __float_as_uint(f[i]);
+  }
+  store_words<W>(p, w);
 }
 
 }  // namespace ssm

@@ -53,7 +53,7 @@ def _upd(**kw):
     (dict(u=None), NULL), (dict(delta=None), NULL), (dict(A=None), NULL), (dict(B=None), NULL),
     (dict(C=None), NULL), (dict(y=None), NULL),
     (dict(u=P + 1), ALIGN), (dict(A=P + 2), ALIGN), (dict(h0=P + 1), ALIGN),
-    (dict(dtype=0, u=P + 2), ALIGN), (dict(last=P + 3), ALIGN),
+    (dict(dtype=0, u=P + 2), ALIGN), (dict(last=P + 3), ALIGN), (dict(ws=P + 16), ALIGN),
     (dict(y=P), ALIAS), (dict(z=P + 0x100000), ALIAS),
 ])
 def test_scan_validation(kw, code):
@@ -61,7 +61,6 @@ def test_scan_validation(kw, code):
 
 
 def test_scan_workspace_checked_before_launch(monkeypatch):
-    monkeypatch.setenv("SSM_SCAN_SEGMENTS", "4")
     need = load().ssm_scan_fwd_workspace_bytes(1, 64, 16, 2048, 1)
     assert need > 0
     assert _scan(ws=None, wsb=0) == WS
@@ -87,10 +86,11 @@ def test_update_validation(kw, code):
 
 def test_workspace_query():
     q = load().ssm_scan_fwd_workspace_bytes
-    # the 2.8B-shaped layer fills the GPU with channels: no split, no workspace
-    assert q(16, 5120, 16, 2048, 1) == 0
-    # the long sequence over few channels is split: workspace for the carries
-    assert q(1, 2048, 16, 65536, 1) > 0
+    # the 2.8B-shaped layer fills the GPU with channels: no split, so only the
+    # fp32 B, C records (batch * L * 2N floats)
+    assert q(16, 5120, 16, 2048, 1) == 16 * 2048 * 32 * 4
+    # the long sequence over few channels is split: records plus carries
+    assert q(1, 2048, 16, 65536, 1) > 1 * 65536 * 32 * 4
     assert q(1, 2048, 16, 65536, 7) == 0      # bad dtype
     assert q(1, 2048, 3, 65536, 1) == 0       # bad dstate
     assert q(0, 2048, 16, 65536, 1) == 0

@@ -1,0 +1,104 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (default segment plan, default priority rotation).
+
+The GPU computes every output; the oracle recomputes a sample of channels
+(whole sequences, so every carry and tile of those channels is covered) and
+the tolerance is applied to the sample: max|y_gpu - y_ref| <= tol * max|y_ref|
+over the sampled rows.  Channels are independent, so a sampled row's
+reference equals that row of the full problem.  Properties that hold at any
+size (finite outputs, run-to-run bit equality) are checked on everything."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import TOL, assert_parity, gpu_scan, oracle_scan, sub_problem, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import selective_state_space_28_amd as ssm
+    ssm.load()
+    return torch.device("cuda:0")
+
+
+def _sample_channels(dim, rng, n_random=12):
+    fixed = {0, 1, 63, 64, 65, dim // 2, dim - 64, dim - 1}
+    rand = set(rng.choice(dim, size=min(n_random, dim), replace=False).tolist())
+    return sorted(c for c in fixed | rand if 0 <= c < dim)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_full_size_scan(dev, name):
+    cfg = synth.SCAN_CONFIGS[name]
+    print(f"{name}: generating {cfg.batch}x{cfg.dim}x{cfg.seqlen} N={cfg.dstate} {cfg.dtype}", flush=True)
+    inp = synth.make_scan_inputs(cfg)
+    y, last = gpu_scan(inp, dev)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(last))
+    rng = np.random.default_rng(100 + cfg.seed)
+    batches = sorted({0, cfg.batch - 1, int(rng.integers(cfg.batch))})
+    worst = 0.0
+    for b in batches:
+        ds = _sample_channels(cfg.dim, rng)
+        sub = sub_problem(inp, b, ds)
+        yr, lr = oracle_scan(sub, nthreads=16)
+        err = assert_parity(y[b:b + 1, ds], yr, cfg.dtype, f"{name} y batch {b}")
+        assert_parity(last[b:b + 1, ds], lr, "f32", f"{name} last_state batch {b}")
+        worst = max(worst, err)
+    print(f"{name}: worst sampled scaled error {worst:.3e} (tol {TOL[cfg.dtype]:.0e})", flush=True)
+
+
+def test_full_size_c3_bitwise_repeatable(dev):
+    import torch
+    import selective_state_space_28_amd as ssm
+    cfg = synth.SCAN_CONFIGS["c3"]
+    inp = synth.make_scan_inputs(cfg)
+    t = {k: to_torch(inp.get(k), cfg.dtype, dev) for k in ("u", "delta", "B", "C", "z")}
+    A, D, bias = (to_torch(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    y1 = ssm.ssm_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias)
+    y2 = ssm.ssm_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_full_size_decode_64_steps(dev):
+    """The decode workload at full size (batch 256, D 5120, N 16), 64 steps:
+    y of sampled rows every step and their fp32 state at the end."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    cfg = synth.DECODE_CONFIG
+    p = synth.make_decode_params(cfg)
+    state = to_torch(p["h0"], "f32", dev).clone()
+    A, D, bias = (to_torch(p[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    rng = np.random.default_rng(44)
+    batches = sorted({0, cfg.batch - 1, *rng.choice(cfg.batch, size=6, replace=False).tolist()})
+    sample = {b: _sample_channels(cfg.dim, rng, n_random=40) for b in batches}
+    ref_state = {b: p["h0"][b, ds].astype(np.float64)[None] for b, ds in sample.items()}
+    worst = 0.0
+    for s in range(cfg.steps):
+        tok = synth.make_decode_step(cfg, s)
+        tt = {k: to_torch(tok[k], cfg.dtype, dev) for k in ("u", "delta", "B", "C", "z")}
+        y = ssm.ssm_state_update(state, tt["u"], tt["delta"], A, tt["B"], tt["C"], D, tt["z"], bias)
+        torch.cuda.synchronize()
+        yg = y.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(yg))
+        w = {k: synth.widen(tok[k], cfg.dtype) for k in ("u", "delta", "B", "C", "z")}
+        ys_ref, ys_gpu = [], []
+        for b, ds in sample.items():
+            yr, ref_state[b] = oracle.state_update(ref_state[b], w["u"][b:b + 1, ds],
+                                                   w["delta"][b:b + 1, ds], p["A"][ds],
+                                                   w["B"][b:b + 1], w["C"][b:b + 1], p["D"][ds],
+                                                   w["z"][b:b + 1, ds], p["delta_bias"][ds])
+            ys_ref.append(yr[0])
+            ys_gpu.append(yg[b, ds])
+        worst = max(worst, assert_parity(np.concatenate(ys_gpu), np.concatenate(ys_ref),
+                                         cfg.dtype, f"decode y step {s}"))
+    sg = state.cpu().numpy().astype(np.float64)
+    got = np.concatenate([sg[b, ds] for b, ds in sample.items()])
+    ref = np.concatenate([ref_state[b][0] for b in sample])
+    serr = assert_parity(got, ref, "f32", "decode state after 64 steps")
+    print(f"decode: worst y error {worst:.3e}, state error {serr:.3e}", flush=True)

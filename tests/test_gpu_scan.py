@@ -175,3 +175,30 @@ def test_workspace_error(dev, monkeypatch):
                           None, None, None, 1, None, y.data_ptr(), None, 1, 64, 16, 256, 0,
                           None, 0, torch.cuda.current_stream().cuda_stream)
     assert rc == -5
+
+
+def test_softplus_and_zoh_accuracy(dev):
+    """Delta and Abar read back through the scan: with L = 1, A = 0 and
+    u = B = C = 1 from a zero state, y = Delta = softplus(x); with A = -1,
+    h0 = 1, u = 0, y = exp(-softplus(x)) = 1/(1+e^x).  Compared with the
+    fp64 values of those closed forms over x in [-30, 30]."""
+    import math
+    x = np.linspace(-30.0, 30.0, 6001).astype(np.float32)
+    K = x.size
+    ones = np.ones((1, K, 1), np.float32)
+    base = dict(delta=x.reshape(1, K, 1), B=np.ones((1, 1, 1), np.float32),
+                C=np.ones((1, 1, 1), np.float32), D=None, z=None, delta_bias=None, dtype="f32")
+    y, _ = gpu_scan(dict(base, u=ones, A=np.zeros((K, 1), np.float32)), dev)
+    xd = x.astype(np.float64)
+    sp = np.logaddexp(0.0, xd)
+    rel = np.abs(y[0, :, 0] - sp) / sp
+    # e^x from an exact fp32 x has condition number |x|: forming x*log2(e) in
+    # fp32 costs about |x| * 2^-24 relative, on top of a few ulp for the rest
+    bound = 5e-7 + 1e-7 * np.abs(xd)
+    assert np.all(rel <= bound), (rel.max(), xd[np.argmax(rel / bound)])
+    y2, _ = gpu_scan(dict(base, u=np.zeros_like(ones), A=-np.ones((K, 1), np.float32)), dev,
+                     h0=ones.reshape(1, K, 1))
+    ref = np.exp(-sp)
+    rel2 = np.abs(y2[0, :, 0] - ref) / ref
+    bound2 = 1e-6 + 2e-7 * np.abs(xd)
+    assert np.all(rel2 <= bound2), (rel2.max(), xd[np.argmax(rel2 / bound2)])
