@@ -15,11 +15,13 @@ namespace {
 
 using ssm::Dtype;
 
-// A launch should put about four waves on each of the 1024 SIMDs of a
-// 256-CU gfx950 before the sequence is split into segments; a segment is never
-// shorter than kMinSegment steps unless a caller forces the split.
-constexpr int64_t kTargetWaves = 4096;
-constexpr int64_t kMinSegment = 512;
+// The forward scan's workgroups are sized so that five fit on a CU (20
+// waves); the planner splits a sequence into segments only as far as needed
+// to give each of the 256 CUs of an MI355X (gfx950) its five workgroups, and
+// never into segments shorter than kMinSegment steps unless forced.
+constexpr int64_t kPlanCUs = 256;
+constexpr int64_t kWavesPerCU = 20;
+constexpr int64_t kMinSegment = 256;
 
 struct SegPlan {
   int nseg;
@@ -63,8 +65,9 @@ SegPlan plan_segments(int batch, int dim, int dstate, int64_t L) {
   const int64_t tile = ssm::kScanTile;
   const int64_t G = dstate >= 4 ? dstate / 4 : 1;
   const int64_t ncg = (dim + 63) / 64;
-  const int64_t waves = (int64_t)batch * ncg * G;
-  int64_t want = waves > 0 ? (kTargetWaves + waves - 1) / waves : 1;
+  const int64_t groups = (int64_t)batch * ncg;        // workgroups per segment
+  const int64_t capacity = kPlanCUs * kWavesPerCU / G;  // resident workgroups
+  int64_t want = groups > 0 ? capacity / groups : 1;
   int64_t cap = L / kMinSegment;
   if (const char* env = std::getenv("SSM_SCAN_SEGMENTS")) {
     const long long v = std::atoll(env);
