@@ -231,7 +231,8 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   a.dim = dim;
   a.dstate = dstate;
   a.softplus = delta_softplus ? 1 : 0;
-  a.vec = aligned(state, 16) ? 1 : 0;
+  // vector path: 16-byte state, A rows and (per lane) B, C pieces
+  a.vec = (aligned(state, 16) && aligned(A, 16) && aligned(B, 4 * es) && aligned(C, 4 * es)) ? 1 : 0;
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
   return ssm::launch_state_update(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK
                                                                                     : SSM_ERR_HIP;

@@ -52,7 +52,7 @@ struct DecodeLaunch {
   void* y;
   int batch, dim, dstate;
   int softplus;
-  int vec;                // state is 16-byte aligned
+  int vec;                // state and A 16-byte aligned, B and C aligned to 4 elements
   Dtype dtype;
 };
 

@@ -23,6 +23,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
     const float* __restrict__ Dskip, const T* __restrict__ z, const float* __restrict__ bias,
     T* __restrict__ y, int batch, int dim, int softplus, int vec) {
+  // vec: state, A, B and C are aligned for the vector loads below
   constexpr int NS = N < 4 ? N : 4;
   constexpr int P = N / NS;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -50,13 +51,37 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   const float x = Elem<T>::load(delta + row) + (bias != nullptr ? bias[d] : 0.0f);
   const float dt = softplus ? softplus_f32(x) : x;
   const float du = dt * uv;
+  // this lane's NS values of A, B and C, each one vector load when aligned
+  float av[NS], bv[NS], cv[NS];
+  const int64_t nb = (int64_t)b * N + part * NS;
+  if (NS == 4 && vec) {
+    const float4 a4 = *reinterpret_cast<const float4*>(A + (int64_t)d * N + part * NS);
+    av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
+    if constexpr (sizeof(T) == 2) {
+      const uint2 b2 = *reinterpret_cast<const uint2*>(B + nb);
+      const uint2 c2 = *reinterpret_cast<const uint2*>(C + nb);
+      bv[0] = bf16_lo(b2.x); bv[1] = bf16_hi(b2.x); bv[2] = bf16_lo(b2.y); bv[3] = bf16_hi(b2.y);
+      cv[0] = bf16_lo(c2.x); cv[1] = bf16_hi(c2.x); cv[2] = bf16_lo(c2.y); cv[3] = bf16_hi(c2.y);
+    } else {
+      const float4 b4 = *reinterpret_cast<const float4*>(B + nb);
+      const float4 c4 = *reinterpret_cast<const float4*>(C + nb);
+      bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+      cv[0] = c4.x; cv[1] = c4.y; cv[2] = c4.z; cv[3] = c4.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      av[k] = A[(int64_t)d * N + part * NS + k];
+      bv[k] = Elem<T>::load(B + nb + k);
+      cv[k] = Elem<T>::load(C + nb + k);
+    }
+  }
   float acc = 0.0f;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    const int n = part * NS + k;
-    const float a = exp2_hw(dt * (A[(int64_t)d * N + n] * kLog2e));
-    h[k] = __builtin_fmaf(a, h[k], du * Elem<T>::load(B + (int64_t)b * N + n));
-    acc = __builtin_fmaf(Elem<T>::load(C + (int64_t)b * N + n), h[k], acc);
+    const float a = exp2_hw(dt * (av[k] * kLog2e));
+    h[k] = __builtin_fmaf(a, h[k], du * bv[k]);
+    acc = __builtin_fmaf(cv[k], h[k], acc);
   }
 
   if (NS == 4 && vec) {

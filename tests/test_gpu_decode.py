@@ -109,3 +109,34 @@ def test_decode_medium_64_steps(dev):
     """The decode workload's recipe at a reduced size, all rows, 64 steps."""
     cfg = DecodeConfig("t", 8, 512, 16, 64, "bf16", seed=4)
     _run_steps(cfg, dev, 64)
+
+
+def _offset_view(t, shape):
+    """A contiguous copy of `t` placed one element past an aligned start, so
+    the vector paths are off and the element-wise fallbacks run."""
+    import torch
+    flat = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = flat[1:].view(shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_unaligned_pointers(dev, dtype):
+    import torch
+    import selective_state_space_28_amd as ssm
+    cfg = DecodeConfig("t", 3, 70, 16, 2, dtype, seed=9)
+    p = synth.make_decode_params(cfg)
+    A, D, bias = (to_torch(p[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    st_a = to_torch(p["h0"], "f32", dev).clone()
+    st_u = _offset_view(st_a, st_a.shape)
+    for s in range(cfg.steps):
+        tok = synth.make_decode_step(cfg, s)
+        t = {k: to_torch(tok[k], dtype, dev) for k in ("u", "delta", "B", "C", "z")}
+        tu = {k: _offset_view(v, v.shape) for k, v in t.items()}
+        ya = ssm.ssm_state_update(st_a, t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias)
+        yu = ssm.ssm_state_update(st_u, tu["u"], tu["delta"], _offset_view(A, A.shape), tu["B"],
+                                  tu["C"], D, tu["z"], bias)
+        torch.cuda.synchronize()
+        assert torch.equal(ya.float(), yu.float())
+    assert torch.equal(st_a, st_u)
