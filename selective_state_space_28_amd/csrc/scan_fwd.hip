@@ -172,8 +172,10 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 
   const float* bcw = bc + ((int64_t)b * G + g) * L * R;  // wave-uniform records
 
-  // raw words of this thread's runs in the KT tiles of the current load block
-  uint32_t pu[KT][W], pd[KT][W], pz[KT][W];
+  // raw words of this thread's runs in the KT tiles of the current load block,
+  // and the packed y of those runs, stored together at the end of the block
+  // so each 128-byte row line is written whole
+  uint32_t pu[KT][W], pd[KT][W], pz[KT][W], py[KT][W];
   auto block_full = [&](int64_t tb) { return vec && tb + KT * TL <= seg_end; };
   auto fetch_block = [&](int64_t tb) {
 #pragma unroll
@@ -325,10 +327,14 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
           yv[e] = s;
         }
         if (ccvalid) {
-          const int64_t off = rowcc * L + t0 + r0;
-          if (vec && tvalid == TL) {
-            store_floats<T, E>(y + off, yv);
+          if (fast) {
+            pack_floats<T, E>(yv, py[j]);
+            if (j == KT - 1) {
+#pragma unroll
+              for (int jj = 0; jj < KT; ++jj) store_words<W>(y + rowcc * L + tb + jj * TL + r0, py[jj]);
+            }
           } else {
+            const int64_t off = rowcc * L + t0 + r0;
 #pragma unroll
             for (int e = 0; e < E; ++e)
               if (r0 + e < tvalid) Elem<T>::store(y + off + e, yv[e]);

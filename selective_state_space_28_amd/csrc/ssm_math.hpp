@@ -124,6 +124,18 @@ __device__ __forceinline__ void words_to_floats(const uint32_t (&w)[E * sizeof(T
   }
 }
 
+// Pack E floats into the words of T storage (bf16: round to nearest even).
+template <typename T, int E>
+__device__ __forceinline__ void pack_floats(const float (&f)[E], uint32_t (&w)[E * sizeof(T) / 4]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) w[i] = __float_as_uint(f[i]);
+  }
+}
+
 // Store E floats as T (bf16: round to nearest even) with vector stores.
 template <typename T, int E>
 __device__ __forceinline__ void store_floats(T* __restrict__ p, const float (&f)[E]) {
