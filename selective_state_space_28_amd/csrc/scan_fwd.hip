@@ -9,10 +9,11 @@
 //
 // Design (channel-parallel, one fused pass over HBM):
 //  * pack_bc_kernel first rewrites B and C (tiny next to u, delta, z, y:
-//    they are shared by all channels) as fp32 records, one per (batch row,
-//    state group, step) holding that group's B then C values.  In the scan a
-//    wave's record for step t is wave-uniform, so it is read with scalar
-//    loads straight into SGPR operands: no VGPRs, no VALU conversions.
+//    they are shared by all channels) as records, one per (batch row, state
+//    group, step) holding that group's B then C values in the input type.
+//    In the scan a wave's record for step t is wave-uniform, so it is read
+//    with scalar loads into SGPR operands: no VGPRs, no VALU work (a bf16
+//    value is widened by a scalar shift or mask).
 //  * A workgroup owns 64 consecutive channels of one batch row and G state
 //    groups; wave g holds NS = N/G states of each of its 64 channels in
 //    VGPRs (lane = channel).  The state never touches HBM.
@@ -52,11 +53,14 @@ struct ScanSizes {
   int prio_epochs;   // priority rotations per segment (0: no rotation)
 };
 
-// ---- B, C -> fp32 records (batch, state group, step, [B x NS, C x NS]) ------
+// ---- B, C -> records (batch, state group, step, [B x NS, C x NS]) -----------
+// Records keep the input type: fp32 inputs give fp32 records, bf16 inputs bf16
+// records (the same values in half the bytes, so twice the steps per scalar
+// cache line).
 template <typename T, int NS, int G>
 __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B,
                                                       const T* __restrict__ C,
-                                                      float* __restrict__ bc, int64_t L,
+                                                      T* __restrict__ bc, int64_t L,
                                                       int tblocks) {
   constexpr int N = NS * G;
   const int b = blockIdx.x / tblocks;
@@ -64,22 +68,31 @@ __global__ __launch_bounds__(256) void pack_bc_kernel(const T* __restrict__ B,
   if (t >= L) return;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float v[2 * NS];
+    T v[2 * NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int64_t src = ((int64_t)b * N + g * NS + k) * L + t;
-      v[k] = Elem<T>::load(B + src);
-      v[NS + k] = Elem<T>::load(C + src);
+      v[k] = B[src];
+      v[NS + k] = C[src];
     }
-    float* dst = bc + (((int64_t)b * G + g) * L + t) * (2 * NS);
-    if constexpr (NS == 4) {
-      reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
-    } else {
+    T* dst = bc + (((int64_t)b * G + g) * L + t) * (2 * NS);
 #pragma unroll
-      for (int k = 0; k < 2 * NS; ++k) dst[k] = v[k];
-    }
+    for (int k = 0; k < 2 * NS; ++k) dst[k] = v[k];
   }
+}
+
+// Value q of a record of 2*NS elements starting at p (wave-uniform, so the
+// loads are scalar and a bf16 widening is a scalar shift or mask).
+template <typename T>
+__device__ __forceinline__ float rec_value(const T* __restrict__ p, int q);
+
+template <>
+__device__ __forceinline__ float rec_value<float>(const float* __restrict__ p, int q) { return p[q]; }
+
+template <>
+__device__ __forceinline__ float rec_value<uint16_t>(const uint16_t* __restrict__ p, int q) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(p)[q >> 1];
+  return (q & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
 // Tiles whose u/delta/z loads are issued together: enough to cover a
@@ -97,7 +110,7 @@ constexpr int load_block_tiles() {
 template <typename T, int NS, int G, int TL, bool AGG>
 __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
-    const float* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
+    const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
     const float* __restrict__ bias, const float* __restrict__ h0, T* __restrict__ y,
     float* __restrict__ last_state, float* __restrict__ ws_hend, float* __restrict__ ws_sumdt,
     const ScanSizes p) {
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   const bool has_z = !AGG && (z != nullptr);
   const bool vec = p.vec != 0;
 
-  const float* bcw = bc + ((int64_t)b * G + g) * L * R;  // wave-uniform records
+  const T* bcw = bc + ((int64_t)b * G + g) * L * R;  // wave-uniform records
 
   // raw words of this thread's runs in the KT tiles of the current load block,
   // and the packed y of those runs, stored together at the end of the block
@@ -249,7 +262,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
       }
 
       // ---- the recurrence: TL steps x NS states per lane ---------------------
-      const float* bct = bcw + t0 * R;
+      const T* bct = bcw + t0 * R;
       if (tvalid == TL) {
         // chunks of CH steps; the next chunk's LDS and scalar loads are issued
         // before the current chunk's arithmetic so their latency is covered
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
         for (int i = 0; i < CH; ++i) {
           vc[i] = s_ddu[i][lane];
 #pragma unroll
-          for (int q = 0; q < R; ++q) rc[i][q] = bct[i * R + q];
+          for (int q = 0; q < R; ++q) rc[i][q] = rec_value<T>(bct + i * R, q);
         }
 #pragma unroll
         for (int c = 0; c < TL / CH; ++c) {
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
             for (int i = 0; i < CH; ++i) {
               vn[i] = s_ddu[(c + 1) * CH + i][lane];
 #pragma unroll
-              for (int q = 0; q < R; ++q) rn[i][q] = bct[((c + 1) * CH + i) * R + q];
+              for (int q = 0; q < R; ++q) rn[i][q] = rec_value<T>(bct + ((c + 1) * CH + i) * R, q);
             }
           }
 #pragma unroll
@@ -302,8 +315,8 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
             const float a = exp2_hw(v.x * A2[k]);
-            h[k] = __builtin_fmaf(a, h[k], v.y * bct[t * R + k]);
-            acc = __builtin_fmaf(bct[t * R + NS + k], h[k], acc);
+            h[k] = __builtin_fmaf(a, h[k], v.y * rec_value<T>(bct + t * R, k));
+            acc = __builtin_fmaf(rec_value<T>(bct + t * R, NS + k), h[k], acc);
           }
           if constexpr (!AGG) {
             s_y[g][t][lane] = acc;
@@ -367,8 +380,9 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   const T* B = static_cast<const T*>(a.B);
   const T* C = static_cast<const T*>(a.C);
   const int tblocks = (int)((a.seqlen + 255) / 256);
+  T* bc = static_cast<T*>(a.ws_bc);
   pack_bc_kernel<T, NS, G><<<(unsigned)((int64_t)a.batch * tblocks), 256, 0, stream>>>(
-      B, C, a.ws_bc, a.seqlen, tblocks);
+      B, C, bc, a.seqlen, tblocks);
 
   ScanSizes s;
   s.batch = a.batch;
@@ -390,12 +404,12 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
     s.nseg_launch = a.nseg - 1;
     const unsigned grid = (unsigned)(base * s.nseg_launch);
     scan_kernel<T, NS, G, TL, true><<<grid, 64 * G, 0, stream>>>(
-        u, dl, a.A, a.ws_bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
+        u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
   }
   s.nseg_launch = a.nseg;
   const unsigned grid = (unsigned)(base * s.nseg_launch);
   scan_kernel<T, NS, G, TL, false><<<grid, 64 * G, 0, stream>>>(
-      u, dl, a.A, a.ws_bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
+      u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
   return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ SegPlan plan_segments(int batch, int dim, int dstate, int64_t L) {
   return SegPlan{(int)(nseg < 1 ? 1 : nseg), seglen};
 }
 
-// Workspace: the fp32 B, C records (always), then for a split sequence the
+// Workspace: the B, C records in the input type (always), then for a split sequence the
 // end state and Delta sum of every segment but the last; each part 256-byte
 // aligned.
 struct WsLayout {
@@ -96,11 +96,11 @@ struct WsLayout {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-WsLayout workspace_layout(int batch, int dim, int dstate, int64_t L, const SegPlan& sp) {
+WsLayout workspace_layout(int batch, int dim, int dstate, int64_t L, int dtype, const SegPlan& sp) {
   WsLayout w{};
   const size_t plane = (size_t)batch * (size_t)dim;
   w.bc = 0;
-  w.hend = round256((size_t)batch * (size_t)L * 2 * (size_t)dstate * sizeof(float));
+  w.hend = round256((size_t)batch * (size_t)L * 2 * (size_t)dstate * (size_t)elem_bytes(dtype));
   size_t end = w.hend;
   if (sp.nseg > 1) {
     w.sumdt = w.hend + round256((size_t)(sp.nseg - 1) * plane * (size_t)dstate * sizeof(float));
@@ -128,7 +128,7 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
   if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return 0;
   if (batch == 0 || dim == 0 || seqlen == 0) return 0;
-  return workspace_layout(batch, dim, dstate, seqlen, plan_segments(batch, dim, dstate, seqlen))
+  return workspace_layout(batch, dim, dstate, seqlen, dtype, plan_segments(batch, dim, dstate, seqlen))
       .total;
 }
 
@@ -161,7 +161,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   const int64_t blocks = (int64_t)batch * ((dim + 63) / 64) * sp.nseg;
   const int64_t pack_blocks = (int64_t)batch * ((seqlen + 255) / 256);
   if (blocks > INT_MAX || pack_blocks > INT_MAX) return SSM_ERR_SHAPE;
-  const WsLayout wl = workspace_layout(batch, dim, dstate, seqlen, sp);
+  const WsLayout wl = workspace_layout(batch, dim, dstate, seqlen, dtype, sp);
   if (workspace == nullptr || workspace_bytes < wl.total) return SSM_ERR_WORKSPACE;
 
   ssm::ScanLaunch a{};
@@ -177,7 +177,7 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   a.y = y;
   a.last_state = last_state;
   char* ws = static_cast<char*>(workspace);
-  a.ws_bc = reinterpret_cast<float*>(ws + wl.bc);
+  a.ws_bc = ws + wl.bc;
   if (sp.nseg > 1) {
     a.ws_hend = reinterpret_cast<float*>(ws + wl.hend);
     a.ws_sumdt = reinterpret_cast<float*>(ws + wl.sumdt);

@@ -25,7 +25,7 @@ struct ScanLaunch {
   const float* h0;        // nullable
   void* y;
   float* last_state;      // nullable
-  float* ws_bc;           // (batch, G, seqlen, 2*dstate/G) fp32 B, C records
+  void* ws_bc;            // (batch, G, seqlen, 2*dstate/G) B, C records, input type
   float* ws_hend;         // (nseg-1, batch, dim, dstate) when nseg > 1
   float* ws_sumdt;        // (nseg-1, batch, dim) when nseg > 1
   int batch, dim, dstate;

@@ -87,8 +87,9 @@ def test_update_validation(kw, code):
 def test_workspace_query():
     q = load().ssm_scan_fwd_workspace_bytes
     # the 2.8B-shaped layer fills the GPU with channels: no split, so only the
-    # fp32 B, C records (batch * L * 2N floats)
-    assert q(16, 5120, 16, 2048, 1) == 16 * 2048 * 32 * 4
+    # B, C records in the input type (batch * L * 2N elements)
+    assert q(16, 5120, 16, 2048, 1) == 16 * 2048 * 32 * 2
+    assert q(16, 5120, 16, 2048, 0) == 16 * 2048 * 32 * 4
     # the long sequence over few channels is split: records plus carries
     assert q(1, 2048, 16, 65536, 1) > 1 * 65536 * 32 * 4
     assert q(1, 2048, 16, 65536, 7) == 0      # bad dtype
