@@ -41,11 +41,11 @@ def _load():
     lib = ctypes.CDLL(_LIB)
     dp = ctypes.POINTER(ctypes.c_double)
     L = ctypes.c_long
-    lib.oracle_scan_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, dp, dp, dp,
-                                    L, L, L, L, ctypes.c_int]
+    lib.oracle_scan_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                    dp, dp, dp, L, L, L, L, ctypes.c_int]
     lib.oracle_scan_fwd.restype = ctypes.c_int
-    lib.oracle_state_update.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, dp,
-                                        L, L, L]
+    lib.oracle_state_update.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
+                                        ctypes.c_int, dp, L, L, L]
     lib.oracle_state_update.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -63,9 +63,16 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def _zoh(bbar):
+    if bbar not in ("euler", "zoh"):
+        raise ValueError(f"bbar must be 'euler' or 'zoh', not {bbar!r}")
+    return int(bbar == "zoh")
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-             h0=None, nthreads=1):
-    """Sequential fp64 scan.
+             h0=None, nthreads=1, bbar="euler"):
+    """Sequential fp64 scan.  bbar selects the input term: 'euler'
+    (Delta*B*u) or 'zoh' ((exp(Delta*A) - 1)/A * B*u).
 
     u, delta, z: (batch, dim, L); A: (dim, N); B, C: (batch, N, L);
     D, delta_bias: (dim,); h0: (batch, dim, N).  Returns (y, last_state) as
@@ -84,7 +91,8 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     y = np.empty((batch, dim, L), dtype=np.float64)
     last = np.empty((batch, dim, N), dtype=np.float64)
     rc = _load().oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                 _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0),
+                                 _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)), _zoh(bbar),
+                                 _ptr(h0),
                                  _ptr(y), _ptr(last), batch, dim, N, L, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_scan_fwd failed with {rc}")
@@ -92,7 +100,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                 delta_softplus=True):
+                 delta_softplus=True, bbar="euler"):
     """One fp64 decode step.  ``state`` (batch, dim, N) is taken as a new
     float64 copy, updated and returned together with y (batch, dim)."""
     st = np.array(state, dtype=np.float64, order="C", copy=True)
@@ -104,7 +112,7 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     y = np.empty((batch, dim), dtype=np.float64)
     rc = _load().oracle_state_update(_ptr(st), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
                                      _ptr(D), _ptr(z), _ptr(delta_bias),
-                                     int(bool(delta_softplus)), _ptr(y), batch, dim, N)
+                                     int(bool(delta_softplus)), _zoh(bbar), _ptr(y), batch, dim, N)
     if rc != 0:
         raise RuntimeError(f"oracle_state_update failed with {rc}")
     return y, st

@@ -10,7 +10,9 @@
  *
  *   Delta_t  = softplus(delta_raw[b,d,t] + bias[d])            (or without softplus)
  *   Abar_t,n = exp(Delta_t * A[d,n])                           (zero-order hold, diagonal A)
- *   h_t,n    = Abar_t,n * h_{t-1},n + Delta_t * B[b,n,t] * u[b,d,t]
+ *   Bbar_t,n = Delta_t                                         (Euler input term, default)
+ *            = (exp(Delta_t * A[d,n]) - 1) / A[d,n]            (zero-order hold, flag; Delta_t at A = 0)
+ *   h_t,n    = Abar_t,n * h_{t-1},n + Bbar_t,n * B[b,n,t] * u[b,d,t]
  *   y_t      = (sum_n C[b,n,t] * h_t,n + Dskip[d] * u[b,d,t]) * silu(z[b,d,t])
  *
  * Sources (web pages, cited by title and section):
@@ -20,9 +22,11 @@
  *    h_t = Abar h_{t-1} + Bbar x_t read out through C; diagonal A applied
  *    per channel in SISO form.
  *  - "Paper: Mamba" course module (konke.bhala.ai/m/F12), "Math & data
- *    structures": zero-order hold for Abar, Euler as the alternative input
- *    discretisation.  The input term used here is the Euler form
- *    Bbar x = Delta * B * x, with the zero-order-hold form for Abar.
+ *    structures": zero-order hold Abar = exp(Delta A),
+ *    Bbar = (exp(Delta A) - 1)/A B, with Euler as the alternative.  The
+ *    default input term is the Euler form Bbar x = Delta * B * x; the flag
+ *    `zoh` selects the zero-order-hold form, written with expm1 so it keeps
+ *    its digits for small Delta*A, and equal to its limit Delta at A = 0.
  *  - "Exercises -- State-space models (Mamba, S4)" (brentwoodlivery.com):
  *    the recurrent view h_k = Abar h_{k-1} + Bbar x_k followed by
  *    y_k = C h_k (the readout comes after the update at the same step), the
@@ -52,6 +56,13 @@ static double softplus(double x) {
   return m + log1p(exp(-fabs(x)));
 }
 
+/* Input-term coefficient: Delta (Euler), or (e^{Delta A} - 1)/A (zero-order
+ * hold), whose limit at A = 0 is Delta. */
+static double bbar(double dt, double a, int zoh) {
+  if (!zoh || a == 0.0) return dt;
+  return expm1(dt * a) / a;
+}
+
 /* silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z -> -inf, e^-z -> inf and
  * the quotient goes to -0, which is the limit. */
 static double silu(double z) { return z / (1.0 + exp(-z)); }
@@ -59,7 +70,7 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 typedef struct {
   const double *u, *delta, *A, *B, *C, *Dskip, *z, *bias, *h0;
   double *y, *last_state;
-  int softplus_on;
+  int softplus_on, zoh;
   long batch, dim, dstate, seqlen;
   long row_begin, row_end;
 } scan_job;
@@ -86,7 +97,7 @@ static void scan_row(const scan_job *j, long row, double *h) {
     double acc = 0.0;
     for (long n = 0; n < N; ++n) {
       const double abar = exp(dt * Ad[n]);                 /* ZOH transition */
-      h[n] = abar * h[n] + dt * Bb[n * L + t] * u[t];       /* Euler input term */
+      h[n] = abar * h[n] + bbar(dt, Ad[n], j->zoh) * Bb[n * L + t] * u[t];
       acc += Cb[n * L + t] * h[n];                          /* readout after update */
     }
     acc += Dd * u[t];
@@ -114,19 +125,21 @@ static void *scan_worker(void *arg) {
  *   Dskip, bias    : (dim,)            (NULL -> 0)
  *   z              : NULL -> no gate
  *   h0, last_state : (batch, dim, dstate) (NULL -> zero start / not written)
+ *   softplus_on    : Delta = softplus(delta + bias), else delta + bias
+ *   zoh            : zero-order-hold input term instead of Euler
  *   nthreads       : worker threads over rows (<= 1 -> run inline)
  * Returns 0 on success, -1 on bad arguments, -2 on allocation/thread failure.
  */
 int oracle_scan_fwd(const double *u, const double *delta, const double *A,
                     const double *B, const double *C, const double *Dskip,
-                    const double *z, const double *bias, int softplus_on,
+                    const double *z, const double *bias, int softplus_on, int zoh,
                     const double *h0, double *y, double *last_state, long batch,
                     long dim, long dstate, long seqlen, int nthreads) {
   if (!u || !delta || !A || !B || !C || !y) return -1;
   if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0) return -1;
   const long rows = batch * dim;
   scan_job base = {u, delta, A, B, C, Dskip, z, bias, h0, y, last_state,
-                   softplus_on, batch, dim, dstate, seqlen, 0, rows};
+                   softplus_on, zoh, batch, dim, dstate, seqlen, 0, rows};
   if (rows == 0) return 0;
   if (nthreads <= 1 || rows < 2) {
     return scan_worker(&base) ? -2 : 0;
@@ -166,7 +179,7 @@ int oracle_scan_fwd(const double *u, const double *delta, const double *A,
 int oracle_state_update(double *state, const double *u, const double *delta,
                         const double *A, const double *B, const double *C,
                         const double *Dskip, const double *z, const double *bias,
-                        int softplus_on, double *y, long batch, long dim,
+                        int softplus_on, int zoh, double *y, long batch, long dim,
                         long dstate) {
   if (!state || !u || !delta || !A || !B || !C || !y) return -1;
   if (batch < 0 || dim < 0 || dstate < 1) return -1;
@@ -179,7 +192,7 @@ int oracle_state_update(double *state, const double *u, const double *delta,
       double acc = 0.0;
       for (long n = 0; n < dstate; ++n) {
         const double abar = exp(dt * A[d * dstate + n]);
-        h[n] = abar * h[n] + dt * B[b * dstate + n] * u[row];
+        h[n] = abar * h[n] + bbar(dt, A[d * dstate + n], zoh) * B[b * dstate + n] * u[row];
         acc += C[b * dstate + n] * h[n];
       }
       acc += (Dskip ? Dskip[d] : 0.0) * u[row];

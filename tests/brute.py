@@ -37,8 +37,11 @@ def deltas(delta_raw, bias, softplus=True):
     return out
 
 
-def semiseparable_y(u, delta_raw, A, B, C, D=None, z=None, bias=None, softplus=True, h0=None):
-    """Unrolled-sum form, O(L^2 N) per channel.  Shapes as the oracle's."""
+def semiseparable_y(u, delta_raw, A, B, C, D=None, z=None, bias=None, softplus=True, h0=None,
+                    zoh=False):
+    """Unrolled-sum form, O(L^2 N) per channel.  Shapes as the oracle's.
+    zoh: input coefficient (Abar - 1)/A (zero-order hold, A != 0) instead of
+    Delta (Euler)."""
     u = np.asarray(u, np.float64)
     batch, dim, L = u.shape
     N = A.shape[1]
@@ -46,14 +49,16 @@ def semiseparable_y(u, delta_raw, A, B, C, D=None, z=None, bias=None, softplus=T
     for b in range(batch):
         dl = deltas(np.asarray(delta_raw[b], np.float64), bias, softplus)  # (dim, L)
         for d in range(dim):
-            abar = np.exp(dl[d][:, None] * np.asarray(A[d], np.float64)[None, :])  # (L, N)
+            Ad = np.asarray(A[d], np.float64)
+            abar = np.exp(dl[d][:, None] * Ad[None, :])  # (L, N)
+            coef = (abar - 1.0) / Ad[None, :] if zoh else np.repeat(dl[d][:, None], N, axis=1)
             for t in range(L):
                 acc = 0.0
                 for s in range(t + 1):
                     prod = np.ones(N)
                     for r in range(s + 1, t + 1):
                         prod = prod * abar[r]
-                    acc += float(np.sum(C[b, :, t] * prod * dl[d, s] * B[b, :, s] * u[b, d, s]))
+                    acc += float(np.sum(C[b, :, t] * prod * coef[s] * B[b, :, s] * u[b, d, s]))
                 if h0 is not None:
                     prod = np.ones(N)
                     for r in range(0, t + 1):

@@ -343,3 +343,102 @@ def test_empty_inputs():
                               np.zeros((1, 3, 0)), np.zeros((1, 3, 0)))
     assert y.shape == (1, 2, 0)
     np.testing.assert_array_equal(last, 0.0)
+
+
+# ------------------------------------------------------- zero-order-hold input
+# NN LAB "Mamba" page, "Derivation of the Discrete Transition Matrices": the
+# input is held constant over each step, the ODE h' = A h + B x is solved
+# over the step, and for diagonal A each state evolves on its own; the
+# "Paper: Mamba" course module, "Math & data structures", gives the result
+# Abar = exp(Delta A), Bbar = (exp(Delta A) - 1)/A B.  The pins below check
+# the oracle's 'zoh' mode against that definition (the ODE), against the
+# gated recurrence it reduces to for N = 1, A = -1, B = 1 (the course
+# module's Theorem 1), against the A -> 0 limit, and against the unrolled sum.
+
+def test_zoh_is_the_exact_solution_of_the_held_input_ode():
+    from scipy.integrate import solve_ivp
+    rng = np.random.default_rng(31)
+    N, L = 3, 10
+    A = -rng.uniform(0.3, 4.0, size=N)
+    u = rng.standard_normal(L)
+    dl = rng.uniform(0.05, 1.5, size=L)        # large Delta*A: Euler is far off here
+    B = rng.standard_normal((N, L))
+    C = rng.standard_normal((N, L))
+    h0 = rng.standard_normal(N)
+    y, last = oracle.scan_fwd(u.reshape(1, 1, L), dl.reshape(1, 1, L), A.reshape(1, N),
+                              B.reshape(1, N, L), C.reshape(1, N, L), h0=h0.reshape(1, 1, N),
+                              delta_softplus=False, bbar="zoh")
+    h = h0.copy()
+    for t in range(L):
+        f = lambda _, hh, t=t: A * hh + B[:, t] * u[t]
+        sol = solve_ivp(f, (0.0, dl[t]), h, method="DOP853", rtol=1e-12, atol=1e-14)
+        h = sol.y[:, -1]
+        assert abs(y[0, 0, t] - float(C[:, t] @ h)) <= 1e-9 * (1 + abs(y[0, 0, t])), t
+    np.testing.assert_allclose(last[0, 0], h, rtol=1e-9, atol=1e-11)
+    # and the Euler input term is a different result at these step sizes
+    ye, _ = oracle.scan_fwd(u.reshape(1, 1, L), dl.reshape(1, 1, L), A.reshape(1, N),
+                            B.reshape(1, N, L), C.reshape(1, N, L), h0=h0.reshape(1, 1, N),
+                            delta_softplus=False)
+    assert np.max(np.abs(ye - y)) > 1e-2
+
+
+def test_zoh_single_state_is_the_gated_recurrence():
+    """N = 1, A = -1, B = C = 1, Delta = softplus(x): Abar = 1 - sigmoid(x),
+    Bbar = sigmoid(x), so h_t = (1 - g_t) h_{t-1} + g_t u_t, g_t = sigmoid(x_t)."""
+    rng = np.random.default_rng(32)
+    L = 50
+    x = 3.0 * rng.standard_normal(L)
+    u = rng.standard_normal(L)
+    y, last = oracle.scan_fwd(u.reshape(1, 1, L), x.reshape(1, 1, L), -np.ones((1, 1)),
+                              np.ones((1, 1, L)), np.ones((1, 1, L)), bbar="zoh")
+    h = 0.0
+    for t in range(L):
+        g = 1.0 / (1.0 + math.exp(-x[t]))
+        h = (1.0 - g) * h + g * u[t]
+        assert abs(y[0, 0, t] - h) <= 1e-13 * (1 + abs(h)), t
+    assert abs(last[0, 0, 0] - h) <= 1e-13 * (1 + abs(h))
+
+
+def test_zoh_small_A_limit_is_euler():
+    """(exp(Delta A) - 1)/A -> Delta as A -> 0, and A = 0 gives Delta itself."""
+    rng = np.random.default_rng(33)
+    kw = _tiny_case(rng, batch=1, dim=2, N=3, L=20)
+    kw["A"] = np.zeros_like(kw["A"])
+    ye, le = oracle.scan_fwd(**kw)
+    yz, lz = oracle.scan_fwd(**kw, bbar="zoh")
+    np.testing.assert_array_equal(yz, ye)
+    np.testing.assert_array_equal(lz, le)
+    kw["A"] = np.full_like(kw["A"], -1e-9)
+    yz, lz = oracle.scan_fwd(**kw, bbar="zoh")
+    scale = np.abs(ye).max()
+    np.testing.assert_allclose(yz, ye, rtol=0, atol=1e-7 * scale)
+
+
+@pytest.mark.parametrize("gate,dskip,h0", [(False, False, False), (True, True, True)])
+def test_zoh_oracle_equals_semiseparable_sum(gate, dskip, h0):
+    rng = np.random.default_rng(34)
+    kw = _tiny_case(rng, gate=gate, dskip=dskip, h0=h0)
+    y, _ = oracle.scan_fwd(**kw, bbar="zoh")
+    yb = brute.semiseparable_y(kw["u"], kw["delta"], kw["A"], kw["B"], kw["C"], kw["D"], kw["z"],
+                               kw["delta_bias"], True, kw["h0"], zoh=True)
+    np.testing.assert_allclose(y, yb, rtol=1e-11, atol=1e-12)
+
+
+def test_zoh_decode_steps_extend_scan():
+    rng = np.random.default_rng(35)
+    kw = _tiny_case(rng, batch=2, dim=3, N=4, L=14, h0=True)
+    yf, lf = oracle.scan_fwd(**kw, bbar="zoh")
+    head = {k: (v[..., :9] if k in ("u", "delta", "B", "C", "z") else v) for k, v in kw.items()}
+    _, st = oracle.scan_fwd(**head, bbar="zoh")
+    for t in range(9, 14):
+        yt, st = oracle.state_update(st, kw["u"][..., t], kw["delta"][..., t], kw["A"],
+                                     kw["B"][..., t], kw["C"][..., t], kw["D"], kw["z"][..., t],
+                                     kw["delta_bias"], bbar="zoh")
+        np.testing.assert_allclose(yt, yf[..., t], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(st, lf, rtol=1e-12, atol=1e-13)
+
+
+def test_bbar_mode_is_checked():
+    with pytest.raises(ValueError):
+        oracle.scan_fwd(np.ones((1, 1, 1)), np.ones((1, 1, 1)), -np.ones((1, 1)),
+                        np.ones((1, 1, 1)), np.ones((1, 1, 1)), bbar="bilinear")
