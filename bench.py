@@ -35,8 +35,11 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # Algorithmic VALU work of the scan per (element, state): Delta*A, exp2,
 # Delta*u*B, the state FMA and the readout FMA.
 OPS_PER_ELEMENT_STATE = 5
+# With the zero-order-hold input term: Delta*A, exp2, u*B, times 1/A, the
+# fma forming (Abar - 1)*w, the state FMA and the readout FMA.
+OPS_PER_ELEMENT_STATE_ZOH = 7
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_kernel_c3_traffic.json")
-KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, false>"
+KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, false, false>"
 KERNEL_SOURCES = ["selective_state_space_28_amd/csrc/scan_fwd.hip",
                   "selective_state_space_28_amd/csrc/ssm_math.hpp"]
 
@@ -194,6 +197,30 @@ def main():
         "wall_ms_per_step": wall_ms,
         "roofline": roof,
     }
+
+    # the same workload with the zero-order-hold input term (flag of the same
+    # entry point), timed the same way
+    def step_zoh():
+        ssm.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, out=y, workspace=ws, bbar="zoh")
+
+    for _ in range(args.warmup):
+        step_zoh()
+    torch.cuda.synchronize(dev)
+    for s, e in ev:
+        s.record(stream)
+        step_zoh()
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_z = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    ops_z = elements * cfg.dstate * OPS_PER_ELEMENT_STATE_ZOH
+    tops_z = ops_z / (ms_z * 1e-3) / 1e12
+    out["zoh"] = {"workload": "the same scan with the zero-order-hold input term (bbar='zoh')",
+                  "ms_per_step": ms_z, "value": elements / (ms_z * 1e-3), "unit": "elements/s",
+                  "roofline": {"bound": "alu", "achieved": round(tops_z, 3),
+                               "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
+                               "frac": round(tops_z / VALU_PEAK_TOPS, 4),
+                               "kernel": KERNEL_NAME.replace("false, false>", "false, true>"),
+                               "ops_per_launch": ops_z}}
     del u, delta, B, C, z, y, ws
 
     if not args.no_decode:
@@ -241,32 +268,58 @@ def bench_decode(dev, steps):
     ms = e0.elapsed_time(e1) / steps
     nbytes = decode_bytes(cfg)
     gbps = nbytes / (ms * 1e-3) / 1e9
+
+    # Reference: a plain in-place update of a state-sized fp32 buffer (torch's
+    # elementwise kernel), rotating over six buffers so that, as in the decode
+    # loop with fresh tokens each step, the state is not held in the 256 MB
+    # last-level cache.  This is the practical HBM rate of the access pattern.
+    bufs = [torch.zeros_like(st) for _ in range(6)]
+    for b_ in bufs:
+        b_.mul_(0.999)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for i in range(steps):
+        bufs[i % 6].mul_(0.999)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ref_ms = e0.elapsed_time(e1) / steps
+    ref_gbps = 2 * st.numel() * 4 / (ref_ms * 1e-3) / 1e9
+    del bufs
     return {"workload": "decode ssm_state_update: batch 256, D 5120, N 16, bf16 tokens, fp32 state",
             "steps": steps, "ms_per_token_step": ms,
             "channels_per_s": cfg.batch * cfg.dim / (ms * 1e-3),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                          "bytes_per_launch": nbytes,
-                         "note": "the 84 MB state fits the 256 MB last-level cache, so "
-                                 "successive steps may be served partly from it"}}
+                         "inplace_update_reference_GBps": round(ref_gbps, 1),
+                         "note": "reference = torch in-place update of a state-sized buffer "
+                                 "over six rotating buffers (the practical HBM rate of an "
+                                 "in-place read-modify-write)"}}
 
 
-def cpu_baseline(cfg, inp):
+def cpu_baseline(cfg, inp, min_core_seconds=12.0):
     """The fp64 oracle as it stands, timed on this host over a bounded sample
-    of the same workload: the first batch rows' channels, whole sequences."""
+    of the same workload: whole batch rows (all channels, whole sequences),
+    four at a time, until about `min_core_seconds` of CPU time (threads x
+    wall) is spent or the whole batch is done."""
     import oracle
     import synth
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(os.cpu_count() or 1, 16)
-    nb = 8
-    w = {k: synth.widen(inp[k][:nb], cfg.dtype) for k in ("u", "delta", "B", "C", "z")}
-    t0 = time.perf_counter()
-    oracle.scan_fwd(w["u"], w["delta"], inp["A"], w["B"], w["C"], inp["D"], w["z"],
-                    inp["delta_bias"], True, None, nthreads=threads)
-    sec = time.perf_counter() - t0
+    sec, nb, chunk = 0.0, 0, 4
+    while nb < cfg.batch and sec * threads < min_core_seconds:
+        sl = slice(nb, min(nb + chunk, cfg.batch))
+        w = {k: synth.widen(inp[k][sl], cfg.dtype) for k in ("u", "delta", "B", "C", "z")}
+        t0 = time.perf_counter()
+        oracle.scan_fwd(w["u"], w["delta"], inp["A"], w["B"], w["C"], inp["D"], w["z"],
+                        inp["delta_bias"], True, None, nthreads=threads)
+        sec += time.perf_counter() - t0
+        nb = sl.stop
+        del w
     el = nb * cfg.dim * cfg.seqlen
     return {"value": el / sec, "unit": "elements/s", "cores": threads, "kind": "oracle",
             "sample": f"batch rows 0..{nb - 1} of the same workload ({nb}x{cfg.dim}x{cfg.seqlen} "
-                      f"elements, N {cfg.dstate}), fp64, {threads} threads, {sec:.1f} s"}
+                      f"elements, N {cfg.dstate}), fp64, {threads} threads, {sec:.1f} s wall, "
+                      f"{sec * threads:.0f} core-s"}
 
 
 if __name__ == "__main__":

@@ -4,10 +4,12 @@
  *
  * The operation (one independent channel per (b, d); all tensors row-major):
  *
- *   Delta_t  = softplus(delta[b,d,t] + delta_bias[d])  (delta_softplus != 0)
- *            =          delta[b,d,t] + delta_bias[d]   (delta_softplus == 0)
+ *   Delta_t  = softplus(delta[b,d,t] + delta_bias[d])  (flags & SSM_DELTA_SOFTPLUS)
+ *            =          delta[b,d,t] + delta_bias[d]   (otherwise)
  *   Abar_t,n = exp(Delta_t * A[d,n])
- *   h_t,n    = Abar_t,n * h_{t-1},n + Delta_t * B[b,n,t] * u[b,d,t]
+ *   Bbar_t,n = Delta_t                                 (Euler, the default)
+ *            = (Abar_t,n - 1) / A[d,n]                 (flags & SSM_BBAR_ZOH)
+ *   h_t,n    = Abar_t,n * h_{t-1},n + Bbar_t,n * B[b,n,t] * u[b,d,t]
  *   y[b,d,t] = (sum_n C[b,n,t] * h_t,n + D_skip[d] * u[b,d,t]) * silu(z[b,d,t])
  *
  * Sources, cited by page title and section:
@@ -18,9 +20,13 @@
  *    "Optimization": one fused kernel for discretisation, scan and readout,
  *    the state never stored in HBM; parallel scan of the associative step.
  *  - "Paper: Mamba" course module (konke.bhala.ai/m/F12), "Math & data
- *    structures": zero-order hold for Abar with Euler as the alternative for
- *    Bbar (the input term here is the Euler form Delta*B*u), and the
- *    associative composition of affine steps.
+ *    structures": zero-order hold Abar = exp(Delta A) and
+ *    Bbar = (exp(Delta A) - 1)/A B, with Euler (Bbar = Delta B) as the
+ *    alternative; the associative composition of affine steps.  Euler is the
+ *    default input term, SSM_BBAR_ZOH selects the zero-order-hold one.
+ *  - NN LAB "Mamba" page (khchao.com), "Derivation of the Discrete
+ *    Transition Matrices": the input held constant over each step, and
+ *    each state of a diagonal A discretised on its own.
  *  - "Exercises -- State-space models (Mamba, S4)" (brentwoodlivery.com):
  *    readout y_k = C h_k after the update; zero initial state; softplus as
  *    the positive time step; decoding one token at a time with a
@@ -48,6 +54,11 @@
  *    enqueued.  A launch failure returns SSM_ERR_HIP.
  *  - NaN and Inf inputs propagate; A is not checked for sign (A > 0 is an
  *    unstable system and its state grows, as the pages note).
+ *  - With SSM_BBAR_ZOH every A[d,n] must be nonzero (A = 0 gives Inf or NaN,
+ *    not the limit Delta).  The term is formed as (Abar - 1) * (u B / A) with
+ *    Abar rounded to float32, so its relative error is about
+ *    2^-23 / |Delta A|: where |Delta A| falls below about 1e-4 the Euler
+ *    term, which zero-order hold tends to there, is the more accurate one.
  *  - Results are deterministic: the same inputs on the same device give the
  *    same bits, run after run.
  */
@@ -71,16 +82,24 @@ typedef enum {
   SSM_ERR_ALIGN = -4,     /* a pointer not aligned to its element size           */
   SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query's answer   */
   SSM_ERR_HIP = -6,       /* the HIP runtime reported an error at launch         */
-  SSM_ERR_ALIAS = -7      /* y (or the decode state) is the same buffer as an input */
+  SSM_ERR_ALIAS = -7,     /* y (or the decode state) is the same buffer as an input */
+  SSM_ERR_FLAGS = -8      /* flags holds a bit that is not an ssm_flag_t value   */
 } ssm_status_t;
+
+/* Bits of the `flags` argument (0 and 1 keep the meaning of the plain
+ * softplus switch). */
+typedef enum {
+  SSM_DELTA_SOFTPLUS = 1, /* Delta = softplus(delta + bias), else delta + bias   */
+  SSM_BBAR_ZOH = 2        /* zero-order-hold input term, else Euler (Delta)      */
+} ssm_flag_t;
 
 /*
  * ssm_scan_fwd_workspace_bytes -- bytes of device workspace that
- * ssm_scan_fwd needs for this problem: fp32 copies of B and C laid out for
- * the kernel (batch * seqlen * 2 * dstate floats), plus, when the sequence is
- * split across workgroups, each segment's end state and Delta sum.  Pure host
- * function: no HIP call.  Returns 0 for an empty problem and for arguments
- * that ssm_scan_fwd would reject.
+ * ssm_scan_fwd needs for this problem: B and C interleaved per step for the
+ * kernel, in the input dtype (batch * seqlen * 2 * dstate elements), plus,
+ * when the sequence is split across workgroups, each segment's end state
+ * and Delta sum.  Pure host function: no HIP call.  Returns 0 for an empty
+ * problem and for arguments that ssm_scan_fwd would reject.
  */
 size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seqlen,
                                     int dtype);
@@ -95,7 +114,7 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
  *   D_skip       in   (dim) float32                          NULL -> 0
  *   z            in   (batch, dim, seqlen), dtype            NULL -> no gate
  *   delta_bias   in   (dim) float32                          NULL -> 0
- *   delta_softplus    1: Delta = softplus(delta + bias); 0: Delta = delta + bias
+ *   flags        bits of ssm_flag_t: SSM_DELTA_SOFTPLUS, SSM_BBAR_ZOH
  *   h0           in   (batch, dim, dstate) float32           NULL -> zero state
  *   y            out  (batch, dim, seqlen), dtype            required; must not
  *                     be u, delta or z
@@ -109,7 +128,7 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
  */
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
                  const void* C, const float* D_skip, const void* z,
-                 const float* delta_bias, int delta_softplus, const float* h0, void* y,
+                 const float* delta_bias, int flags, const float* h0, void* y,
                  float* last_state, int batch, int dim, int dstate, int64_t seqlen,
                  int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -124,12 +143,13 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
  *   D_skip       in   (dim) float32                                     NULL -> 0
  *   z            in   (batch, dim), dtype                               NULL -> no gate
  *   delta_bias   in   (dim) float32                                     NULL -> 0
+ *   flags        bits of ssm_flag_t, as for ssm_scan_fwd
  *   y            out  (batch, dim), dtype                               required
  *   batch, dim >= 0; dstate in {1,2,4,8,16}.
  */
 int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
                      const void* B, const void* C, const float* D_skip, const void* z,
-                     const float* delta_bias, int delta_softplus, void* y, int batch,
+                     const float* delta_bias, int flags, void* y, int batch,
                      int dim, int dstate, int dtype, void* stream);
 
 /* ssm_status_string -- a static, human-readable name for a status code. */

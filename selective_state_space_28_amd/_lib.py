@@ -9,6 +9,7 @@ import re
 from .build import LIB, INCLUDE
 
 SSM_F32, SSM_BF16 = 0, 1
+SSM_DELTA_SOFTPLUS, SSM_BBAR_ZOH = 1, 2
 _lib = None
 
 

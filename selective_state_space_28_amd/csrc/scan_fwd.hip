@@ -95,6 +95,20 @@ __device__ __forceinline__ float rec_value<uint16_t>(const uint16_t* __restrict_
   return (q & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
+// Input term of one (element, state).  Euler: q = Delta*u*B is the term.
+// Zero-order hold ("Paper: Mamba" course module, "Math & data structures":
+// Bbar = (exp(Delta A) - 1)/A B): q = u*B, term = (a - 1) * q / A, formed as
+// fma(a, w, -w) with w = q * (1/A), so a - 1 is never rounded on its own.
+template <bool ZOH>
+__device__ __forceinline__ float input_term(float a, float q, float rA) {
+  if constexpr (ZOH) {
+    const float w = q * rA;
+    return __builtin_fmaf(a, w, -w);
+  } else {
+    return q;
+  }
+}
+
 // Tiles whose u/delta/z loads are issued together: enough to cover a
 // 128-byte line of every row (so each line is fetched once, not once per
 // tile), within a budget of 24 VGPRs of raw words per thread.
@@ -107,7 +121,7 @@ constexpr int load_block_tiles() {
   return kt < 1 ? 1 : (kt > 4 ? 4 : kt);
 }
 
-template <typename T, int NS, int G, int TL, bool AGG>
+template <typename T, int NS, int G, int TL, bool AGG, bool ZOH>
 __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
@@ -124,7 +138,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   static_assert(TL % G == 0 && (E * (int)sizeof(T)) % 4 == 0, "tile must split into words");
   static_assert(TL % CH == 0, "tile must split into chunks");
 
-  __shared__ float2 s_ddu[TL][LDW];                           // (Delta, Delta*u)
+  __shared__ float2 s_ddu[TL][LDW];                           // (Delta, Delta*u), ZOH: (Delta, u)
   __shared__ float s_y[AGG ? 1 : G][AGG ? 1 : TL][LDW];       // partial readouts
 
   // ---- block -> (batch row, channel group, segment) --------------------------
@@ -150,11 +164,13 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   const int64_t seg_end = seg_begin + p.seglen < L ? seg_begin + p.seglen : L;
 
   // ---- per-lane parameters and initial state ---------------------------------
-  float A2[NS], h[NS];
+  float A2[NS], h[NS], rA[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     const int n = g * NS + k;
-    A2[k] = dvalid ? A[(int64_t)d * N + n] * kLog2e : 0.0f;
+    const float a_dn = dvalid ? A[(int64_t)d * N + n] : -1.0f;
+    A2[k] = dvalid ? a_dn * kLog2e : 0.0f;
+    rA[k] = 1.0f / a_dn;  // zero-order-hold input term only
     h[k] = 0.0f;
     if (seg == 0 && h0 != nullptr && dvalid) h[k] = h0[row * N + n];
   }
@@ -251,7 +267,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
       for (int e = 0; e < E; ++e) {
         const float x = dd[e] + bias_cc;
         const float dt = p.softplus ? softplus_f32(x) : x;
-        s_ddu[r0 + e][cc] = make_float2(dt, dt * uu[e]);
+        s_ddu[r0 + e][cc] = make_float2(dt, ZOH ? uu[e] : dt * uu[e]);
       }
       __syncthreads();
 
@@ -290,7 +306,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 #pragma unroll
             for (int k = 0; k < NS; ++k) {
               const float a = exp2_hw(vc[i].x * A2[k]);
-              h[k] = __builtin_fmaf(a, h[k], vc[i].y * rc[i][k]);
+              h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, vc[i].y * rc[i][k], rA[k]));
               acc = __builtin_fmaf(rc[i][NS + k], h[k], acc);
             }
             if constexpr (!AGG) {
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
             const float a = exp2_hw(v.x * A2[k]);
-            h[k] = __builtin_fmaf(a, h[k], v.y * rec_value<T>(bct + t * R, k));
+            h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, v.y * rec_value<T>(bct + t * R, k), rA[k]));
             acc = __builtin_fmaf(rec_value<T>(bct + t * R, NS + k), h[k], acc);
           }
           if constexpr (!AGG) {
@@ -374,7 +390,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   }
 }
 
-template <typename T, int NS, int G>
+template <typename T, int NS, int G, bool ZOH>
 static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   constexpr int TL = kScanTile;
   const T* B = static_cast<const T*>(a.B);
@@ -403,32 +419,33 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   if (a.nseg > 1) {
     s.nseg_launch = a.nseg - 1;
     const unsigned grid = (unsigned)(base * s.nseg_launch);
-    scan_kernel<T, NS, G, TL, true><<<grid, 64 * G, 0, stream>>>(
+    scan_kernel<T, NS, G, TL, true, ZOH><<<grid, 64 * G, 0, stream>>>(
         u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
   }
   s.nseg_launch = a.nseg;
   const unsigned grid = (unsigned)(base * s.nseg_launch);
-  scan_kernel<T, NS, G, TL, false><<<grid, 64 * G, 0, stream>>>(
+  scan_kernel<T, NS, G, TL, false, ZOH><<<grid, 64 * G, 0, stream>>>(
       u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool ZOH>
 static hipError_t launch_by_state(const ScanLaunch& a, hipStream_t stream) {
   switch (a.dstate) {
-    case 1: return launch_typed<T, 1, 1>(a, stream);
-    case 2: return launch_typed<T, 2, 1>(a, stream);
-    case 4: return launch_typed<T, 4, 1>(a, stream);
-    case 8: return launch_typed<T, 4, 2>(a, stream);
-    case 16: return launch_typed<T, 4, 4>(a, stream);
+    case 1: return launch_typed<T, 1, 1, ZOH>(a, stream);
+    case 2: return launch_typed<T, 2, 1, ZOH>(a, stream);
+    case 4: return launch_typed<T, 4, 1, ZOH>(a, stream);
+    case 8: return launch_typed<T, 4, 2, ZOH>(a, stream);
+    case 16: return launch_typed<T, 4, 4, ZOH>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream) {
   if (a.batch == 0 || a.dim == 0 || a.seqlen == 0) return hipSuccess;
-  return a.dtype == Dtype::BF16 ? launch_by_state<uint16_t>(a, stream)
-                                : launch_by_state<float>(a, stream);
+  if (a.dtype == Dtype::BF16)
+    return a.zoh ? launch_by_state<uint16_t, true>(a, stream) : launch_by_state<uint16_t, false>(a, stream);
+  return a.zoh ? launch_by_state<float, true>(a, stream) : launch_by_state<float, false>(a, stream);
 }
 
 __global__ void fill_state_kernel(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {

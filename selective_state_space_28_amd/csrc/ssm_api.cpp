@@ -58,6 +58,8 @@ bool dstate_ok(int n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; 
 
 int elem_bytes(int dtype) { return dtype == SSM_BF16 ? 2 : 4; }
 
+bool flags_ok(int flags) { return (flags & ~(SSM_DELTA_SOFTPLUS | SSM_BBAR_ZOH)) == 0; }
+
 // Segments of the sequence for the forward scan.  SSM_SCAN_SEGMENTS (an
 // integer >= 1) overrides the choice; tests use it to run the carry path at
 // small sizes.
@@ -133,11 +135,12 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
 }
 
 int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D_skip, const void* z, const float* delta_bias, int delta_softplus,
+                 const float* D_skip, const void* z, const float* delta_bias, int flags,
                  const float* h0, void* y, float* last_state, int batch, int dim, int dstate,
                  int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes,
                  void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return SSM_ERR_SHAPE;
   const bool empty = batch == 0 || dim == 0;
   if (!empty && seqlen > 0 && (!u || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
@@ -188,7 +191,8 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   a.seqlen = seqlen;
   a.seglen = sp.seglen;
   a.nseg = sp.nseg;
-  a.softplus = delta_softplus ? 1 : 0;
+  a.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  a.zoh = (flags & SSM_BBAR_ZOH) ? 1 : 0;
   const bool rows16 = ((int64_t)es * seqlen) % 16 == 0;
   a.vec = rows16 && aligned(u, 16) && aligned(delta, 16) && aligned(z, 16) && aligned(y, 16);
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
@@ -199,9 +203,10 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
 
 int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
                      const void* B, const void* C, const float* D_skip, const void* z,
-                     const float* delta_bias, int delta_softplus, void* y, int batch, int dim,
+                     const float* delta_bias, int flags, void* y, int batch, int dim,
                      int dstate, int dtype, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, 1)) return SSM_ERR_SHAPE;
   const bool empty = batch == 0 || dim == 0;
   if (!empty && (!state || !u || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
@@ -230,7 +235,8 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   a.batch = batch;
   a.dim = dim;
   a.dstate = dstate;
-  a.softplus = delta_softplus ? 1 : 0;
+  a.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  a.zoh = (flags & SSM_BBAR_ZOH) ? 1 : 0;
   // vector path: 16-byte state, A rows and (per lane) B, C pieces
   a.vec = (aligned(state, 16) && aligned(A, 16) && aligned(B, 4 * es) && aligned(C, 4 * es)) ? 1 : 0;
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
@@ -248,6 +254,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
     case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported a launch error";
     case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output is the same buffer as an input";
+    case SSM_ERR_FLAGS: return "SSM_ERR_FLAGS: flags holds an unknown bit";
     default: return "unknown ssm status";
   }
 }

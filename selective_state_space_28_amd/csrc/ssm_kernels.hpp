@@ -36,6 +36,7 @@ struct ScanLaunch {
   int vec;                // 16-byte vector loads/stores allowed
   int ncu;                // compute units of the device
   int prio_epochs;        // wave-priority rotations per segment (0: none)
+  int zoh;                // zero-order-hold input term (else Euler)
   Dtype dtype;
 };
 
@@ -53,6 +54,7 @@ struct DecodeLaunch {
   int batch, dim, dstate;
   int softplus;
   int vec;                // state and A 16-byte aligned, B and C aligned to 4 elements
+  int zoh;                // zero-order-hold input term (else Euler)
   Dtype dtype;
 };
 

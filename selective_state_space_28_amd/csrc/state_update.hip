@@ -17,7 +17,7 @@
 
 namespace ssm {
 
-template <typename T, int N>
+template <typename T, int N, bool ZOH>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ u, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
@@ -80,7 +80,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     const float a = exp2_hw(dt * (av[k] * kLog2e));
-    h[k] = __builtin_fmaf(a, h[k], du * bv[k]);
+    if constexpr (ZOH) {
+      // zero-order hold: (a - 1) * u*B / A, as fma(a, w, -w) with w = u*B/A
+      const float w = uv * bv[k] / av[k];
+      h[k] = __builtin_fmaf(a, h[k], __builtin_fmaf(a, w, -w));
+    } else {
+      h[k] = __builtin_fmaf(a, h[k], du * bv[k]);
+    }
     acc = __builtin_fmaf(cv[k], h[k], acc);
   }
 
@@ -101,13 +107,13 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   }
 }
 
-template <typename T, int N>
+template <typename T, int N, bool ZOH>
 static hipError_t launch_n(const DecodeLaunch& a, hipStream_t stream) {
   constexpr int NS = N < 4 ? N : 4;
   constexpr int P = N / NS;
   const int64_t threads = (int64_t)a.batch * a.dim * P;
   const unsigned grid = (unsigned)((threads + 255) / 256);
-  state_update_kernel<T, N><<<grid, 256, 0, stream>>>(
+  state_update_kernel<T, N, ZOH><<<grid, 256, 0, stream>>>(
       a.state, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A,
       static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.Dskip,
       static_cast<const T*>(a.z), a.bias, static_cast<T*>(a.y), a.batch, a.dim, a.softplus,
@@ -115,21 +121,23 @@ static hipError_t launch_n(const DecodeLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool ZOH>
 static hipError_t launch_t(const DecodeLaunch& a, hipStream_t stream) {
   switch (a.dstate) {
-    case 1: return launch_n<T, 1>(a, stream);
-    case 2: return launch_n<T, 2>(a, stream);
-    case 4: return launch_n<T, 4>(a, stream);
-    case 8: return launch_n<T, 8>(a, stream);
-    case 16: return launch_n<T, 16>(a, stream);
+    case 1: return launch_n<T, 1, ZOH>(a, stream);
+    case 2: return launch_n<T, 2, ZOH>(a, stream);
+    case 4: return launch_n<T, 4, ZOH>(a, stream);
+    case 8: return launch_n<T, 8, ZOH>(a, stream);
+    case 16: return launch_n<T, 16, ZOH>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream) {
   if (a.batch == 0 || a.dim == 0) return hipSuccess;
-  return a.dtype == Dtype::BF16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);
+  if (a.dtype == Dtype::BF16)
+    return a.zoh ? launch_t<uint16_t, true>(a, stream) : launch_t<uint16_t, false>(a, stream);
+  return a.zoh ? launch_t<float, true>(a, stream) : launch_t<float, false>(a, stream);
 }
 
 }  // namespace ssm

@@ -3,7 +3,7 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import SSM_BF16, SSM_F32, SsmError, load, status_string
+from ._lib import SSM_BBAR_ZOH, SSM_BF16, SSM_DELTA_SOFTPLUS, SSM_F32, SsmError, load, status_string
 
 _DTYPES = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16}
 
@@ -16,6 +16,12 @@ def _code(t: torch.Tensor) -> int:
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def _flags(delta_softplus, bbar):
+    if bbar not in ("euler", "zoh"):
+        raise ValueError(f"bbar must be 'euler' or 'zoh', not {bbar!r}")
+    return (SSM_DELTA_SOFTPLUS if delta_softplus else 0) | (SSM_BBAR_ZOH if bbar == "zoh" else 0)
 
 
 def _check(name, t, shape, dtype, device, required=True):
@@ -43,8 +49,10 @@ def ssm_scan_fwd_workspace_bytes(batch: int, dim: int, dstate: int, seqlen: int,
 
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                 h0=None, *, return_last_state=False, out=None, workspace=None):
+                 h0=None, *, bbar="euler", return_last_state=False, out=None, workspace=None):
     """Selective scan over (batch, dim, L) inputs; see include/ssm.h.
+    bbar: 'euler' (input term Delta*B*u) or 'zoh' ((exp(Delta*A) - 1)/A*B*u,
+    A nonzero).
 
     u, delta, z: (batch, dim, L) float32 or bfloat16 (one dtype for all);
     B, C: (batch, N, L) same dtype; A: (dim, N) float32; D, delta_bias: (dim,)
@@ -80,7 +88,7 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
         workspace = None
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(y),
+                          _ptr(delta_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(y),
                           _ptr(last), batch, dim, N, L, code, _ptr(workspace), ws_bytes, stream)
     if rc != 0:
         raise SsmError(rc, "ssm_scan_fwd")
@@ -88,7 +96,7 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
 
 
 def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                     delta_softplus=True, *, out=None):
+                     delta_softplus=True, *, bbar="euler", out=None):
     """One decode step; `state` (batch, dim, N) float32 is updated in place.
     u, delta, z: (batch, dim); B, C: (batch, N); returns y (batch, dim)."""
     lib = load()
@@ -111,7 +119,7 @@ def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     _check("out", y, (batch, dim), dt, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.ssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                              _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(delta_softplus)),
+                              _ptr(D), _ptr(z), _ptr(delta_bias), _flags(delta_softplus, bbar),
                               _ptr(y), batch, dim, N, code, stream)
     if rc != 0:
         raise SsmError(rc, "ssm_state_update")

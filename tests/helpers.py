@@ -51,12 +51,12 @@ def gpu_scan(inp: dict, device, h0=None, softplus=True, return_last_state=True, 
     return res.float().cpu().numpy().astype(np.float64), None
 
 
-def oracle_scan(inp: dict, h0=None, softplus=True, nthreads=8):
+def oracle_scan(inp: dict, h0=None, softplus=True, nthreads=8, bbar="euler"):
     import oracle
     w = widened(inp)
     return oracle.scan_fwd(w["u"], w["delta"], w["A"], w["B"], w["C"], w["D"], w["z"],
                            w["delta_bias"], softplus, None if h0 is None else np.asarray(h0, np.float64),
-                           nthreads=nthreads)
+                           nthreads=nthreads, bbar=bbar)
 
 
 def scaled_err(got, ref) -> float:

@@ -7,7 +7,7 @@ import pytest
 import selective_state_space_28_amd as ssm
 from selective_state_space_28_amd._lib import header_functions, load
 
-OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS, FLAGS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 P = 0x10000  # a 256-byte aligned fake device address, never dereferenced
 
 
@@ -21,7 +21,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS, FLAGS):
         s = ssm.ssm_status_string(code)
         assert s.startswith("SSM_")
     assert "unknown" in ssm.ssm_status_string(42)
@@ -55,6 +55,7 @@ def _upd(**kw):
     (dict(u=P + 1), ALIGN), (dict(A=P + 2), ALIGN), (dict(h0=P + 1), ALIGN),
     (dict(dtype=0, u=P + 2), ALIGN), (dict(last=P + 3), ALIGN), (dict(ws=P + 16), ALIGN),
     (dict(y=P), ALIAS), (dict(z=P + 0x100000), ALIAS),
+    (dict(sp=4), FLAGS), (dict(sp=-1), FLAGS), (dict(sp=8 | 1), FLAGS),
 ])
 def test_scan_validation(kw, code):
     assert _scan(**kw) == code
@@ -78,7 +79,7 @@ def test_empty_problems_need_no_gpu():
     (dict(dtype=5), DTYPE), (dict(dstate=6), SHAPE), (dict(batch=-2), SHAPE),
     (dict(state=None), NULL), (dict(u=None), NULL), (dict(B=None), NULL), (dict(y=None), NULL),
     (dict(state=P + 2), ALIGN), (dict(u=P + 1), ALIGN), (dict(bias=P + 1), ALIGN),
-    (dict(y=P), ALIAS),
+    (dict(y=P), ALIAS), (dict(sp=6), FLAGS), (dict(sp=1 << 30), FLAGS),
 ])
 def test_update_validation(kw, code):
     assert _upd(**kw) == code
@@ -103,3 +104,12 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_python_bbar_mode_is_checked():
+    import torch
+    from selective_state_space_28_amd.ops import _flags
+    assert _flags(True, "euler") == 1 and _flags(False, "euler") == 0
+    assert _flags(True, "zoh") == 3 and _flags(False, "zoh") == 2
+    with pytest.raises(ValueError):
+        _flags(True, "bilinear")
