@@ -35,9 +35,13 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # Algorithmic VALU work of the scan per (element, state): Delta*A, exp2,
 # Delta*u*B, the state FMA and the readout FMA.
 OPS_PER_ELEMENT_STATE = 5
-# With the zero-order-hold input term: Delta*A, exp2, u*B, times 1/A, the
-# fma forming (Abar - 1)*w, the state FMA and the readout FMA.
+# With the zero-order-hold input term, counted as the plain formula needs it:
+# Delta*A, exp2, u*B, times 1/A, the fma forming (Abar - 1)*w, the state FMA
+# and the readout FMA.  The kernel executes more (13): it also evaluates the
+# Taylor series that keeps small |Delta A| accurate, and selects between the
+# two forms.
 OPS_PER_ELEMENT_STATE_ZOH = 7
+OPS_EXECUTED_PER_ELEMENT_STATE_ZOH = 13
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_kernel_c3_traffic.json")
 KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, false, false>"
 KERNEL_SOURCES = ["selective_state_space_28_amd/csrc/scan_fwd.hip",
@@ -220,7 +224,8 @@ def main():
                                "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
                                "frac": round(tops_z / VALU_PEAK_TOPS, 4),
                                "kernel": KERNEL_NAME.replace("false, false>", "false, true>"),
-                               "ops_per_launch": ops_z}}
+                               "ops_per_launch": ops_z,
+                               "ops_executed_per_element_state": OPS_EXECUTED_PER_ELEMENT_STATE_ZOH}}
     del u, delta, B, C, z, y, ws
 
     if not args.no_decode:

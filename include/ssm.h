@@ -54,11 +54,10 @@
  *    enqueued.  A launch failure returns SSM_ERR_HIP.
  *  - NaN and Inf inputs propagate; A is not checked for sign (A > 0 is an
  *    unstable system and its state grows, as the pages note).
- *  - With SSM_BBAR_ZOH every A[d,n] must be nonzero (A = 0 gives Inf or NaN,
- *    not the limit Delta).  The term is formed as (Abar - 1) * (u B / A) with
- *    Abar rounded to float32, so its relative error is about
- *    2^-23 / |Delta A|: where |Delta A| falls below about 1e-4 the Euler
- *    term, which zero-order hold tends to there, is the more accurate one.
+ *  - With SSM_BBAR_ZOH the coefficient (Abar - 1)/A is taken from the Taylor
+ *    series Delta (1 + x/2 + x^2/6 + x^3/24), x = Delta A, where |x| < 0.1,
+ *    and from (Abar - 1)/A elsewhere, so its float32 relative error stays
+ *    near 1e-6 for every Delta A; A = 0 gives Delta, the limit.
  *  - Results are deterministic: the same inputs on the same device give the
  *    same bits, run after run.
  */

@@ -97,13 +97,11 @@ __device__ __forceinline__ float rec_value<uint16_t>(const uint16_t* __restrict_
 
 // Input term of one (element, state).  Euler: q = Delta*u*B is the term.
 // Zero-order hold ("Paper: Mamba" course module, "Math & data structures":
-// Bbar = (exp(Delta A) - 1)/A B): q = u*B, term = (a - 1) * q / A, formed as
-// fma(a, w, -w) with w = q * (1/A), so a - 1 is never rounded on its own.
+// Bbar = (exp(Delta A) - 1)/A B): q = u*B times the coefficient zoh_coef.
 template <bool ZOH>
-__device__ __forceinline__ float input_term(float a, float q, float rA) {
+__device__ __forceinline__ float input_term(float a, float x2, float dt, float q, float rA) {
   if constexpr (ZOH) {
-    const float w = q * rA;
-    return __builtin_fmaf(a, w, -w);
+    return q * zoh_coef(a, x2, dt, rA);
   } else {
     return q;
   }
@@ -305,8 +303,9 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
             float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < NS; ++k) {
-              const float a = exp2_hw(vc[i].x * A2[k]);
-              h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, vc[i].y * rc[i][k], rA[k]));
+              const float x2 = vc[i].x * A2[k];
+              const float a = exp2_hw(x2);
+              h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, vc[i].x, vc[i].y * rc[i][k], rA[k]));
               acc = __builtin_fmaf(rc[i][NS + k], h[k], acc);
             }
             if constexpr (!AGG) {
@@ -330,8 +329,9 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
           float acc = 0.0f;
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
-            const float a = exp2_hw(v.x * A2[k]);
-            h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, v.y * rec_value<T>(bct + t * R, k), rA[k]));
+            const float x2 = v.x * A2[k];
+            const float a = exp2_hw(x2);
+            h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, v.x, v.y * rec_value<T>(bct + t * R, k), rA[k]));
             acc = __builtin_fmaf(rec_value<T>(bct + t * R, NS + k), h[k], acc);
           }
           if constexpr (!AGG) {

@@ -40,6 +40,25 @@ __device__ __forceinline__ float softplus_f32(float x) {
 
 // silu(z) = z / (1 + e^-z).  For z -> -inf the reciprocal goes to 0 and the
 // product to -0; no NaN for finite z.
+// Zero-order-hold input coefficient Bbar/B = (exp(Delta A) - 1)/A, given
+// x2 = Delta*A*log2(e), a = exp2(x2), Delta and 1/A.  Where |Delta A| < 0.1
+// the difference a - 1 would carry the rounding error of a magnified by
+// 1/|Delta A|, so the Taylor series Delta*(1 + x/2 + x^2/6 + x^3/24),
+// x = Delta A, is taken there (dropped terms below x^4/120 < 1e-6 relative);
+// elsewhere (a - 1)/A, formed as one fma (relative error about 2^-23/0.1).
+// A = 0 lands in the series and gives Delta, the limit.  Branch-free: both
+// forms are computed and one is selected.
+constexpr float kZohSeriesX2 = 0.1f * kLog2e;
+__device__ __forceinline__ float zoh_coef(float a, float x2, float dt, float rA) {
+  constexpr float k1 = kLn2 / 2.0f;
+  constexpr float k2 = kLn2 * kLn2 / 6.0f;
+  constexpr float k3 = kLn2 * kLn2 * kLn2 / 24.0f;
+  const float p = __builtin_fmaf(x2, __builtin_fmaf(x2, __builtin_fmaf(x2, k3, k2), k1), 1.0f);
+  const float series = dt * p;
+  const float direct = __builtin_fmaf(a, rA, -rA);
+  return __builtin_fabsf(x2) < kZohSeriesX2 ? series : direct;
+}
+
 __device__ __forceinline__ float silu_f32(float z) {
   return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
 }

@@ -79,11 +79,11 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   float acc = 0.0f;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    const float a = exp2_hw(dt * (av[k] * kLog2e));
+    const float x2 = dt * (av[k] * kLog2e);
+    const float a = exp2_hw(x2);
     if constexpr (ZOH) {
-      // zero-order hold: (a - 1) * u*B / A, as fma(a, w, -w) with w = u*B/A
-      const float w = uv * bv[k] / av[k];
-      h[k] = __builtin_fmaf(a, h[k], __builtin_fmaf(a, w, -w));
+      // zero-order hold: u*B * (exp(Delta A) - 1)/A
+      h[k] = __builtin_fmaf(a, h[k], uv * bv[k] * zoh_coef(a, x2, dt, 1.0f / av[k]));
     } else {
       h[k] = __builtin_fmaf(a, h[k], du * bv[k]);
     }
