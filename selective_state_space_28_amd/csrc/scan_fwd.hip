@@ -2,10 +2,11 @@
 //
 // What it computes is stated in include/ssm.h: per channel (b, d) and state
 // n, Delta = softplus(delta + bias), Abar = exp(Delta*A) (zero-order hold,
-// "Mamba" paper review, "SSM"), input term Delta*B*u (the Euler form named
-// in the "Paper: Mamba" course module), h = Abar*h + Delta*B*u, and the
-// readout y = (C.h + D*u)*silu(z) after each update ("Exercises --
-// State-space models (Mamba, S4)", recurrent view).
+// "Mamba" paper review, "SSM"), input term Bbar*B*u with Bbar = Delta (the
+// Euler form) or, under a flag, (exp(Delta*A) - 1)/A (zero-order hold; both
+// in the "Paper: Mamba" course module, "Math & data structures"),
+// h = Abar*h + Bbar*B*u, and the readout y = (C.h + D*u)*silu(z) after each
+// update ("Exercises -- State-space models (Mamba, S4)", recurrent view).
 //
 // Design (channel-parallel, one fused pass over HBM):
 //  * pack_bc_kernel first rewrites B and C (tiny next to u, delta, z, y:
@@ -17,16 +18,18 @@
 //  * A workgroup owns 64 consecutive channels of one batch row and G state
 //    groups; wave g holds NS = N/G states of each of its 64 channels in
 //    VGPRs (lane = channel).  The state never touches HBM.
-//  * The sequence is walked in tiles of TL steps.  Per tile, all threads
-//    load u, delta (and z) with coalesced vector loads along L (the next
-//    tile's loads are issued before the current tile's recurrence), compute
-//    Delta = softplus(delta + bias) and Delta*u once per element, and stage
-//    them transposed in LDS (one float2 per (step, channel)).
+//  * The sequence is walked in tiles of TL steps, grouped in load blocks of
+//    KT tiles whose u, delta (and z) loads are issued together, one block
+//    ahead, so each 128-byte line of a row is fetched once.  Per tile, all
+//    threads compute Delta = softplus(delta + bias) and Delta*u (u under
+//    zero-order hold) once per element and stage them transposed in LDS
+//    (one float2 per (step, channel)).
 //  * Each wave runs the TL steps of the recurrence for its states: per
-//    (element, state) one v_exp_f32 and four fp32 VALU ops.
+//    (element, state) one v_exp_f32 and four fp32 VALU ops (Euler).
 //  * The G partial readouts per (step, channel) are summed through LDS in a
-//    fixed order, D*u and the silu gate applied, and y stored with coalesced
-//    vector stores.
+//    fixed order, D*u and the silu gate applied, and y kept in registers
+//    until the load block ends, then stored so each row line is written
+//    whole.
 //  * Long sequences with too few channels to fill the GPU are split into
 //    segments.  The affine steps compose associatively ("NN LAB" Mamba page,
 //    "The Associative Property of Linear Recurrence"): a first launch runs
