@@ -13,6 +13,11 @@ against values and identities fixed by the pages (worked impulse response,
 printed exp/softplus values, convolution = recurrence, brute-force
 semiseparable sums, stability bound, chunking/decode identities).  The D-skip
 term and the silu gate are pinned only by their definitions (the pages do not
-state them): parity unpinned by the pages for those two terms.
+state them): parity unpinned by the pages for those two terms.  The
+convolution prologue (causal_conv1d_silu, conv_step) is pinned against numpy's
+convolution with the taps reversed, its identity and delay special cases,
+and its own chunking and decode identities; its tap order, width and
+non-linearity are readings of the pages, not printed on them.
 """
-from .oracle import scan_fwd, state_update, lib_path, build  # noqa: F401
+from .oracle import (build, causal_conv1d_silu, conv_scan_fwd, conv_step,  # noqa: F401
+                     lib_path, scan_fwd, state_update)

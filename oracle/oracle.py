@@ -47,6 +47,10 @@ def _load():
     lib.oracle_state_update.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
                                         ctypes.c_int, dp, L, L, L]
     lib.oracle_state_update.restype = ctypes.c_int
+    lib.oracle_causal_conv1d_silu.argtypes = [dp, dp, dp, L, dp, dp, dp, L, L, L]
+    lib.oracle_causal_conv1d_silu.restype = ctypes.c_int
+    lib.oracle_conv_step.argtypes = [dp, dp, dp, dp, L, dp, L, L]
+    lib.oracle_conv_step.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -116,3 +120,47 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise RuntimeError(f"oracle_state_update failed with {rc}")
     return y, st
+
+
+def causal_conv1d_silu(x, w, cb=None, state_in=None):
+    """u = silu(causal depthwise conv of x with w (dim, K), + cb).  x:
+    (batch, dim, L); state_in: (batch, dim, K-1), the inputs before t = 0
+    (zeros if None).  Returns (u, state_out), state_out the K-1 last
+    inputs."""
+    x, w, cb, state_in = map(_f64, (x, w, cb, state_in))
+    batch, dim, L = x.shape
+    K = w.shape[1]
+    assert w.shape == (dim, K) and K >= 1
+    assert cb is None or cb.shape == (dim,)
+    assert state_in is None or state_in.shape == (batch, dim, K - 1)
+    u = np.empty_like(x)
+    st = np.empty((batch, dim, K - 1), dtype=np.float64)
+    rc = _load().oracle_causal_conv1d_silu(_ptr(x), _ptr(w), _ptr(cb), K, _ptr(state_in), _ptr(u),
+                                           _ptr(st) if K > 1 else None, batch, dim, L)
+    if rc != 0:
+        raise RuntimeError(f"oracle_causal_conv1d_silu failed with {rc}")
+    return u, st
+
+
+def conv_step(conv_state, x, w, cb=None):
+    """One decode token of the convolution: returns (u, new conv_state)."""
+    cs = np.array(conv_state, dtype=np.float64, order="C", copy=True)
+    x, w, cb = map(_f64, (x, w, cb))
+    batch, dim = x.shape
+    K = w.shape[1]
+    assert cs.shape == (batch, dim, K - 1)
+    u = np.empty_like(x)
+    rc = _load().oracle_conv_step(_ptr(cs) if K > 1 else None, _ptr(x), _ptr(w), _ptr(cb), K,
+                                  _ptr(u), batch, dim)
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_step failed with {rc}")
+    return u, cs
+
+
+def conv_scan_fwd(x, conv_w, conv_b, conv_state_in, delta, A, B, C, D=None, z=None,
+                  delta_bias=None, delta_softplus=True, h0=None, nthreads=1, bbar="euler"):
+    """The convolution prologue, then the scan on its output (two separate
+    steps, in that order).  Returns (y, last_state, conv_state_out)."""
+    u, cst = causal_conv1d_silu(x, conv_w, conv_b, conv_state_in)
+    y, last = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, nthreads, bbar)
+    return y, last, cst

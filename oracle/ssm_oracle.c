@@ -35,6 +35,15 @@
  *  - "Mamba" paper review, section "Mamba" block description: a gating
  *    mechanism mixes in the residual.  Read here as the output gate
  *    y <- (C.h + Dskip*u) * silu(z) with silu(z) = z / (1 + e^-z).
+ *  - The same block description: the expanded input passes through a
+ *    convolution and a non-linearity before the SSM; NN LAB "Mamba" page,
+ *    "Kernel Fusion in On-Chip SRAM": that convolution is causal and 1-D.
+ *    Read here as a depthwise (per channel) causal convolution of width K
+ *    along t, the last tap on the current input, plus a per-channel bias,
+ *    followed by silu:  u[t] = silu(cb[d] + sum_k w[d,k] x[t-K+1+k]),
+ *    with the K-1 inputs before t = 0 taken from a carried conv state (or
+ *    zero).  oracle_causal_conv1d_silu computes it on its own; its output is
+ *    the u of the scan.
  *
  * Precision: every input is widened to double before use and all arithmetic
  * is double.  No blocking, fusion or reordering beyond the sequential
@@ -199,6 +208,66 @@ int oracle_state_update(double *state, const double *u, const double *delta,
       if (z) acc *= silu(z[row]);
       y[row] = acc;
     }
+  }
+  return 0;
+}
+
+/*
+ * oracle_causal_conv1d_silu: u = silu(causal depthwise conv(x) + cb).
+ *   x, u      : (batch, dim, seqlen)
+ *   w         : (dim, K), tap K-1 multiplies the current input
+ *   cb        : (dim,) or NULL
+ *   state_in  : (batch, dim, K-1) or NULL: the K-1 inputs before t = 0,
+ *               oldest first (NULL -> zeros)
+ *   state_out : (batch, dim, K-1) or NULL: the K-1 last inputs (oldest
+ *               first), taken from state_in where seqlen < K-1
+ */
+int oracle_causal_conv1d_silu(const double *x, const double *w, const double *cb, long K,
+                              const double *state_in, double *u, double *state_out,
+                              long batch, long dim, long seqlen) {
+  if (!x || !w || !u || K < 1 || batch < 0 || dim < 0 || seqlen < 0) return -1;
+  const long H = K - 1;
+  for (long row = 0; row < batch * dim; ++row) {
+    const long d = row % dim;
+    const double *xr = x + row * seqlen;
+    const double *si = state_in ? state_in + row * H : NULL;
+    for (long t = 0; t < seqlen; ++t) {
+      double acc = cb ? cb[d] : 0.0;
+      for (long k = 0; k < K; ++k) {
+        const long s = t - H + k;
+        const double xv = s >= 0 ? xr[s] : (si ? si[H + s] : 0.0);
+        acc += w[d * K + k] * xv;
+      }
+      u[row * seqlen + t] = silu(acc);
+    }
+    if (state_out)
+      for (long j = 0; j < H; ++j) {
+        const long s = seqlen - H + j;
+        state_out[row * H + j] = s >= 0 ? xr[s] : (si ? si[H + s] : 0.0);
+      }
+  }
+  return 0;
+}
+
+/*
+ * oracle_conv_step: one token of the same convolution for decoding.
+ *   conv_state : (batch, dim, K-1) inputs before this token, oldest first;
+ *                shifted in place to end with x
+ *   x, u       : (batch, dim)
+ */
+int oracle_conv_step(double *conv_state, const double *x, const double *w, const double *cb,
+                     long K, double *u, long batch, long dim) {
+  if ((!conv_state && K > 1) || !x || !w || !u || K < 1 || batch < 0 || dim < 0) return -1;
+  const long H = K - 1;
+  for (long row = 0; row < batch * dim; ++row) {
+    const long d = row % dim;
+    double *cs = conv_state ? conv_state + row * H : NULL;
+    double acc = cb ? cb[d] : 0.0;
+    for (long k = 0; k < H; ++k) acc += w[d * K + k] * cs[k];
+    acc += w[d * K + H] * x[row];
+    u[row] = silu(acc);
+    for (long k = 0; k + 1 < H; ++k) cs[k] = cs[k + 1];
+    if (H > 0) cs[H - 1] = x[row];
   }
   return 0;
 }

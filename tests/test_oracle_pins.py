@@ -442,3 +442,99 @@ def test_bbar_mode_is_checked():
     with pytest.raises(ValueError):
         oracle.scan_fwd(np.ones((1, 1, 1)), np.ones((1, 1, 1)), -np.ones((1, 1)),
                         np.ones((1, 1, 1)), np.ones((1, 1, 1)), bbar="bilinear")
+
+
+# ------------------------------------------------------ convolution prologue
+# "Mamba" paper review, "Mamba" block description (a convolution and a
+# non-linearity before the SSM) and NN LAB "Mamba" page, "Kernel Fusion in
+# On-Chip SRAM" (causal 1-D convolution fused with the scan).  Reading:
+# depthwise, causal, tap K-1 on the current input, bias, then silu.
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_conv_equals_numpy_convolution(K):
+    """Causal conv with taps w[0..K-1] (w[K-1] on the current input) is
+    np.convolve with the taps reversed, truncated to the first L outputs."""
+    rng = np.random.default_rng(70 + K)
+    b, dim, L = 2, 5, 23
+    x = rng.standard_normal((b, dim, L))
+    w = rng.standard_normal((dim, K))
+    cb = rng.standard_normal(dim)
+    u, st = oracle.causal_conv1d_silu(x, w, cb)
+    for i in range(b):
+        for d in range(dim):
+            ref = np.convolve(x[i, d], w[d, ::-1])[:L] + cb[d]
+            np.testing.assert_allclose(u[i, d], _silu(ref), rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(st, x[:, :, L - (K - 1):] if K > 1 else st)
+
+
+def test_conv_identity_and_delay_taps():
+    rng = np.random.default_rng(75)
+    x = rng.standard_normal((1, 3, 12))
+    cb = rng.standard_normal(3)
+    w = np.zeros((3, 4)); w[:, 3] = 1.0           # current input only
+    u, _ = oracle.causal_conv1d_silu(x, w, cb)
+    np.testing.assert_allclose(u, _silu(x + cb[None, :, None]), rtol=1e-15)
+    w = np.zeros((3, 4)); w[:, 0] = 1.0           # input three steps back
+    prev = rng.standard_normal((1, 3, 3))
+    u, _ = oracle.causal_conv1d_silu(x, w, None, prev)
+    np.testing.assert_allclose(u[..., 3:], _silu(x[..., :-3]), rtol=1e-15)
+    np.testing.assert_allclose(u[..., :3], _silu(prev), rtol=1e-15)
+    u0, _ = oracle.causal_conv1d_silu(x, w)      # no state: zeros before t = 0
+    np.testing.assert_array_equal(u0[..., :3], 0.0)
+
+
+@pytest.mark.parametrize("split", [1, 2, 7, 19])
+def test_conv_state_resumes_exactly(split):
+    rng = np.random.default_rng(76)
+    x = rng.standard_normal((2, 4, 20))
+    w = rng.standard_normal((4, 4))
+    cb = rng.standard_normal(4)
+    s0 = rng.standard_normal((2, 4, 3))
+    u, st = oracle.causal_conv1d_silu(x, w, cb, s0)
+    u1, st1 = oracle.causal_conv1d_silu(x[..., :split], w, cb, s0)
+    u2, st2 = oracle.causal_conv1d_silu(x[..., split:], w, cb, st1)
+    np.testing.assert_array_equal(np.concatenate([u1, u2], -1), u)
+    np.testing.assert_array_equal(st2, st)
+
+
+def test_conv_short_sequence_state_out():
+    """L < K-1: the new state keeps the tail of the old one."""
+    s0 = np.array([[[1.0, 2.0, 3.0]]])
+    x = np.array([[[4.0]]])
+    _, st = oracle.causal_conv1d_silu(x, np.ones((1, 4)), None, s0)
+    np.testing.assert_array_equal(st, [[[2.0, 3.0, 4.0]]])
+    _, st = oracle.causal_conv1d_silu(np.zeros((1, 1, 0)), np.ones((1, 4)), None, s0)
+    np.testing.assert_array_equal(st, s0)
+
+
+def test_conv_decode_steps_equal_the_sequence():
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((2, 3, 9))
+    w = rng.standard_normal((3, 4))
+    cb = rng.standard_normal(3)
+    s0 = rng.standard_normal((2, 3, 3))
+    u, st = oracle.causal_conv1d_silu(x, w, cb, s0)
+    cs = s0
+    for t in range(9):
+        ut, cs = oracle.conv_step(cs, x[..., t], w, cb)
+        np.testing.assert_allclose(ut, u[..., t], rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(cs, st)
+
+
+def test_conv_scan_is_conv_then_scan():
+    """The composed oracle: its y is the scan of the convolution's output,
+    and with an identity tap and no bias it is the scan of silu(x)."""
+    rng = np.random.default_rng(78)
+    kw = _tiny_case(rng, batch=1, dim=2, N=3, L=10)
+    x = rng.standard_normal((1, 2, 10))
+    w = np.zeros((2, 4)); w[:, 3] = 1.0
+    y, last, _ = oracle.conv_scan_fwd(x, w, None, None, kw["delta"], kw["A"], kw["B"], kw["C"],
+                                      kw["D"], kw["z"], kw["delta_bias"])
+    y2, last2 = oracle.scan_fwd(_silu(x), kw["delta"], kw["A"], kw["B"], kw["C"], kw["D"], kw["z"],
+                                kw["delta_bias"])
+    np.testing.assert_allclose(y, y2, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(last, last2, rtol=1e-14, atol=1e-15)
