@@ -151,6 +151,60 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
                      const float* delta_bias, int flags, void* y, int batch,
                      int dim, int dstate, int dtype, void* stream);
 
+/*
+ * ssm_conv_scan_fwd -- ssm_scan_fwd with the block's convolution prologue
+ * fused in: the scan's u is computed in the kernel from x as
+ *
+ *   u[b,d,t] = silu(conv_b[d] + sum_{k<K} conv_w[d,k] * x[b,d,t-K+1+k])
+ *
+ * (depthwise, causal, tap K-1 on the current input), and u feeds both the
+ * recurrence and the D_skip term; x is read from HBM once.  Source: "Mamba"
+ * paper review, "Mamba" block description (the input passes through a
+ * convolution and a non-linearity before the SSM) and the NN LAB "Mamba"
+ * page, "Kernel Fusion in On-Chip SRAM" (the causal 1-D convolution fused
+ * with discretisation and scan).  Width, tap order and silu as the
+ * non-linearity are not fixed by the pages; they are this interface's
+ * choice.
+ *
+ *   x              in   (batch, dim, seqlen), dtype           required
+ *   conv_w         in   (dim, conv_width) float32              required
+ *   conv_b         in   (dim) float32                          NULL -> 0
+ *   conv_width     1..4 (SSM_ERR_SHAPE otherwise)
+ *   conv_state_in  in   (batch, dim, conv_width-1) float32: the inputs before
+ *                       t = 0, oldest first                    NULL -> zeros
+ *   conv_state_out out  (batch, dim, conv_width-1) float32: the last
+ *                       conv_width-1 inputs (from conv_state_in where
+ *                       seqlen < conv_width-1)                 NULL -> not written;
+ *                       must not be conv_state_in, y or last_state
+ *   every other argument as for ssm_scan_fwd (y must not be x), with the
+ *   same workspace (ssm_scan_fwd_workspace_bytes).
+ */
+int ssm_conv_scan_fwd(const void* x, const float* conv_w, const float* conv_b, int conv_width,
+                      const float* conv_state_in, float* conv_state_out, const void* delta,
+                      const float* A, const void* B, const void* C, const float* D_skip,
+                      const void* z, const float* delta_bias, int flags, const float* h0, void* y,
+                      float* last_state, int batch, int dim, int dstate, int64_t seqlen, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_conv_state_update -- ssm_state_update with the convolution prologue:
+ * u = silu(conv_b[d] + sum_{k<K-1} conv_w[d,k] * conv_state[b,d,k]
+ *          + conv_w[d,K-1] * x[b,d]),
+ * then conv_state is shifted in place to end with x.  Source as for
+ * ssm_conv_scan_fwd.
+ *
+ *   conv_state     in/out (batch, dim, conv_width-1) float32   required when
+ *                         conv_width > 1; must not be state, x or y
+ *   x              in   (batch, dim), dtype                     required
+ *   conv_w, conv_b, conv_width as for ssm_conv_scan_fwd; every other argument
+ *   as for ssm_state_update.
+ */
+int ssm_conv_state_update(float* conv_state, float* state, const void* x, const float* conv_w,
+                          const float* conv_b, int conv_width, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D_skip, const void* z,
+                          const float* delta_bias, int flags, void* y, int batch, int dim,
+                          int dstate, int dtype, void* stream);
+
 /* ssm_status_string -- a static, human-readable name for a status code. */
 const char* ssm_status_string(int status);
 

@@ -9,12 +9,15 @@ the calls raise instead of falling back to anything else.
     y, last = ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias,
                            delta_softplus=True, h0=None, return_last_state=True)
     y = ssm_state_update(state, u, delta, A, B, C, D, z, delta_bias)
+    y = ssm_conv_scan_fwd(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias)
+    y = ssm_conv_state_update(conv_state, state, x, conv_w, conv_b, delta, A, B, C, D, z,
+                              delta_bias)
 """
 from __future__ import annotations
 
 from ._lib import SSM_BF16, SSM_F32, SsmError, header_functions, load, status_string  # noqa: F401
-from .ops import (ssm_scan_fwd, ssm_scan_fwd_workspace_bytes, ssm_state_update,  # noqa: F401
-                  ssm_status_string)
+from .ops import (ssm_conv_scan_fwd, ssm_conv_state_update, ssm_scan_fwd,  # noqa: F401
+                  ssm_scan_fwd_workspace_bytes, ssm_state_update, ssm_status_string)
 
 __all__ = ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_state_update",
-           "ssm_status_string", "SsmError", "load"]
+           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_status_string", "SsmError", "load"]

@@ -30,6 +30,15 @@
 //    fixed order, D*u and the silu gate applied, and y kept in registers
 //    until the load block ends, then stored so each row line is written
 //    whole.
+//  * Optional convolution prologue ("Mamba" paper review, "Mamba" block
+//    description: the input passes through a convolution and a
+//    non-linearity before the SSM; NN LAB "Mamba" page, "Kernel Fusion in
+//    On-Chip SRAM": a causal 1-D convolution fused with the scan):
+//    u = silu(cb + sum_k w[k] x[t-K+1+k]) per channel, computed in the
+//    staging step from the loaded x.  The K-1 <= 3 inputs before a thread's
+//    run come from the neighbouring run by a lane shuffle (the G runs of a
+//    channel sit in consecutive lanes of one wave), so x is read from HBM
+//    once, as u would be.
 //  * Long sequences with too few channels to fill the GPU are split into
 //    segments.  The affine steps compose associatively ("NN LAB" Mamba page,
 //    "The Associative Property of Linear Recurrence"): a first launch runs
@@ -54,7 +63,26 @@ struct ScanSizes {
   int vec;
   int ncu;           // compute units of the device (blocks launched per "rank")
   int prio_epochs;   // priority rotations per segment (0: no rotation)
+  int conv_k;        // convolution width (CONV variants)
 };
+
+// Convolution prologue operands (CONV variants only).
+struct ConvArgs {
+  const float* w;          // (dim, K)
+  const float* b;          // (dim) nullable
+  const float* state_in;   // (batch, dim, K-1) nullable: inputs before t = 0
+  float* state_out;        // (batch, dim, K-1) nullable: the last K-1 inputs
+};
+
+// Input x of row `row` at step s of a sequence of length L: x itself for
+// s >= 0, else the carried state (K-1 entries, oldest first) or zero.
+template <typename T>
+__device__ __forceinline__ float conv_input(const T* __restrict__ x, const float* __restrict__ st,
+                                            int64_t row, int64_t L, int64_t s, int K) {
+  if (s >= 0) return Elem<T>::load(x + row * L + s);
+  if (st != nullptr && s >= -(int64_t)(K - 1)) return st[row * (K - 1) + (K - 1) + s];
+  return 0.0f;
+}
 
 // ---- B, C -> records (batch, state group, step, [B x NS, C x NS]) -----------
 // Records keep the input type: fp32 inputs give fp32 records, bf16 inputs bf16
@@ -122,13 +150,15 @@ constexpr int load_block_tiles() {
   return kt < 1 ? 1 : (kt > 4 ? 4 : kt);
 }
 
-template <typename T, int NS, int G, int TL, bool AGG, bool ZOH>
+template <typename T, int NS, int G, int TL, bool AGG, int MODE>
 __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
     const float* __restrict__ bias, const float* __restrict__ h0, T* __restrict__ y,
     float* __restrict__ last_state, float* __restrict__ ws_hend, float* __restrict__ ws_sumdt,
-    const ScanSizes p) {
+    const ScanSizes p, const ConvArgs cv) {
+  constexpr bool ZOH = (MODE & kModeZoh) != 0;
+  constexpr bool CONV = (MODE & kModeConv) != 0;
   constexpr int N = NS * G;
   constexpr int E = TL / G;                     // elements per thread, load/store phases
   constexpr int W = E * (int)sizeof(T) / 4;     // their size in 32-bit words
@@ -138,6 +168,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   constexpr int R = 2 * NS;                     // floats per B, C record
   static_assert(TL % G == 0 && (E * (int)sizeof(T)) % 4 == 0, "tile must split into words");
   static_assert(TL % CH == 0, "tile must split into chunks");
+  static_assert(!CONV || E >= kMaxConvWidth - 1, "a run must hold the convolution's history");
 
   __shared__ float2 s_ddu[TL][LDW];                           // (Delta, Delta*u), ZOH: (Delta, u)
   __shared__ float s_y[AGG ? 1 : G][AGG ? 1 : TL][LDW];       // partial readouts
@@ -200,6 +231,26 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   const bool has_z = !AGG && (z != nullptr);
   const bool vec = p.vec != 0;
 
+  // convolution taps of channel cc, right-aligned in 4 (tap 3 on the current
+  // input), its bias, and the last 3 inputs of this thread's previous run
+  float cw[kMaxConvWidth] = {}, cbias = 0.0f, tailp[kMaxConvWidth - 1] = {};
+  if constexpr (CONV) {
+    const int K = p.conv_k;
+    if (ccvalid) {
+#pragma unroll
+      for (int j = 0; j < kMaxConvWidth; ++j) {
+        const int k = j - (kMaxConvWidth - K);
+        if (k >= 0) cw[j] = cv.w[(int64_t)dcc * K + k];
+      }
+      cbias = cv.b != nullptr ? cv.b[dcc] : 0.0f;
+      // before the segment's first tile, every thread's "previous run" ends
+      // at the segment start
+#pragma unroll
+      for (int i = 0; i < kMaxConvWidth - 1; ++i)
+        tailp[i] = conv_input<T>(u, cv.state_in, rowcc, L, seg_begin - (kMaxConvWidth - 1) + i, K);
+    }
+  }
+
   const T* bcw = bc + ((int64_t)b * G + g) * L * R;  // wave-uniform records
 
   // raw words of this thread's runs in the KT tiles of the current load block,
@@ -259,6 +310,29 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
           uu[e] = ok ? Elem<T>::load(u + off) : 0.0f;
           dd[e] = ok ? Elem<T>::load(delta + off) : 0.0f;
           zz[e] = (ok && has_z) ? Elem<T>::load(z + off) : 0.0f;
+        }
+      }
+      if constexpr (CONV) {
+        // the 3 inputs before this run: from the run of the lane before (same
+        // tile), or for a channel's first run from its last run's lane in the
+        // previous tile
+        const int lw = tid & 63;
+        float xw[E + kMaxConvWidth - 1];
+#pragma unroll
+        for (int i = 0; i < kMaxConvWidth - 1; ++i) {
+          const float left = __shfl(uu[E - (kMaxConvWidth - 1) + i], chunk > 0 ? lw - 1 : lw);
+          const float prev = __shfl(tailp[i], chunk == 0 ? lw + G - 1 : lw);
+          xw[i] = chunk > 0 ? left : prev;
+          tailp[i] = uu[E - (kMaxConvWidth - 1) + i];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) xw[kMaxConvWidth - 1 + e] = uu[e];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float sacc = cbias;
+#pragma unroll
+          for (int j = 0; j < kMaxConvWidth; ++j) sacc = __builtin_fmaf(cw[j], xw[e + j], sacc);
+          uu[e] = silu_f32(sacc);
         }
       }
       // Entries of channels past dim, or of steps past the tile end, hold
@@ -390,10 +464,17 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 #pragma unroll
       for (int k = 0; k < NS; ++k) last_state[row * N + g * NS + k] = h[k];
     }
+    if constexpr (CONV) {
+      if (cv.state_out != nullptr && seg == p.nseg - 1 && g == 0) {
+        const int K = p.conv_k;
+        for (int j = 0; j < K - 1; ++j)
+          cv.state_out[row * (K - 1) + j] = conv_input<T>(u, cv.state_in, row, L, L - (K - 1) + j, K);
+      }
+    }
   }
 }
 
-template <typename T, int NS, int G, bool ZOH>
+template <typename T, int NS, int G, int MODE>
 static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   constexpr int TL = kScanTile;
   const T* B = static_cast<const T*>(a.B);
@@ -414,6 +495,8 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   s.vec = a.vec;
   s.ncu = a.ncu > 0 ? a.ncu : 1;
   s.prio_epochs = a.prio_epochs;
+  s.conv_k = a.conv_k;
+  const ConvArgs cv{a.conv_w, a.conv_b, a.conv_state_in, a.conv_state_out};
   const T* u = static_cast<const T*>(a.u);
   const T* dl = static_cast<const T*>(a.delta);
   const T* z = static_cast<const T*>(a.z);
@@ -422,33 +505,43 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   if (a.nseg > 1) {
     s.nseg_launch = a.nseg - 1;
     const unsigned grid = (unsigned)(base * s.nseg_launch);
-    scan_kernel<T, NS, G, TL, true, ZOH><<<grid, 64 * G, 0, stream>>>(
-        u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
+    scan_kernel<T, NS, G, TL, true, MODE><<<grid, 64 * G, 0, stream>>>(
+        u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s, cv);
   }
   s.nseg_launch = a.nseg;
   const unsigned grid = (unsigned)(base * s.nseg_launch);
-  scan_kernel<T, NS, G, TL, false, ZOH><<<grid, 64 * G, 0, stream>>>(
-      u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s);
+  scan_kernel<T, NS, G, TL, false, MODE><<<grid, 64 * G, 0, stream>>>(
+      u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s, cv);
   return hipGetLastError();
 }
 
-template <typename T, bool ZOH>
+template <typename T, int MODE>
 static hipError_t launch_by_state(const ScanLaunch& a, hipStream_t stream) {
   switch (a.dstate) {
-    case 1: return launch_typed<T, 1, 1, ZOH>(a, stream);
-    case 2: return launch_typed<T, 2, 1, ZOH>(a, stream);
-    case 4: return launch_typed<T, 4, 1, ZOH>(a, stream);
-    case 8: return launch_typed<T, 4, 2, ZOH>(a, stream);
-    case 16: return launch_typed<T, 4, 4, ZOH>(a, stream);
+    case 1: return launch_typed<T, 1, 1, MODE>(a, stream);
+    case 2: return launch_typed<T, 2, 1, MODE>(a, stream);
+    case 4: return launch_typed<T, 4, 1, MODE>(a, stream);
+    case 8: return launch_typed<T, 4, 2, MODE>(a, stream);
+    case 16: return launch_typed<T, 4, 4, MODE>(a, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+static hipError_t launch_by_mode(const ScanLaunch& a, hipStream_t stream) {
+  const int mode = (a.zoh ? kModeZoh : 0) | (a.conv_w != nullptr ? kModeConv : 0);
+  switch (mode) {
+    case 0: return launch_by_state<T, 0>(a, stream);
+    case kModeZoh: return launch_by_state<T, kModeZoh>(a, stream);
+    case kModeConv: return launch_by_state<T, kModeConv>(a, stream);
+    default: return launch_by_state<T, kModeZoh | kModeConv>(a, stream);
   }
 }
 
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream) {
   if (a.batch == 0 || a.dim == 0 || a.seqlen == 0) return hipSuccess;
-  if (a.dtype == Dtype::BF16)
-    return a.zoh ? launch_by_state<uint16_t, true>(a, stream) : launch_by_state<uint16_t, false>(a, stream);
-  return a.zoh ? launch_by_state<float, true>(a, stream) : launch_by_state<float, false>(a, stream);
+  if (a.conv_w != nullptr && (a.conv_k < 1 || a.conv_k > kMaxConvWidth)) return hipErrorInvalidValue;
+  return a.dtype == Dtype::BF16 ? launch_by_mode<uint16_t>(a, stream) : launch_by_mode<float>(a, stream);
 }
 
 __global__ void fill_state_kernel(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {

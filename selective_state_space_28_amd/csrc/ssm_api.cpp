@@ -134,30 +134,62 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
       .total;
 }
 
-int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D_skip, const void* z, const float* delta_bias, int flags,
-                 const float* h0, void* y, float* last_state, int batch, int dim, int dstate,
-                 int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Operands of the convolution prologue (all null / zero: no convolution).
+struct ConvIn {
+  const float* w;
+  const float* b;
+  const float* state_in;   // scan only
+  float* state_out;        // scan only
+  float* state;            // decode only, in place
+  int k;
+};
+
+bool conv_aligned(const ConvIn* cv) {
+  return cv == nullptr || (aligned(cv->w, 4) && aligned(cv->b, 4) && aligned(cv->state_in, 4) &&
+                           aligned(cv->state_out, 4) && aligned(cv->state, 4));
+}
+
+int scan_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+              const float* D_skip, const void* z, const float* delta_bias, int flags,
+              const float* h0, void* y, float* last_state, int batch, int dim, int dstate,
+              int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+              const ConvIn* cv) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return SSM_ERR_SHAPE;
+  if (cv != nullptr && (cv->k < 1 || cv->k > ssm::kMaxConvWidth)) return SSM_ERR_SHAPE;
   const bool empty = batch == 0 || dim == 0;
   if (!empty && seqlen > 0 && (!u || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
+  if (!empty && cv != nullptr && cv->w == nullptr) return SSM_ERR_NULL;
   const size_t es = (size_t)elem_bytes(dtype);
   if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
       !aligned(z, es) || !aligned(y, es) || !aligned(A, 4) || !aligned(D_skip, 4) ||
       !aligned(delta_bias, 4) || !aligned(h0, 4) || !aligned(last_state, 4) ||
       !aligned(workspace, 256))
     return SSM_ERR_ALIGN;
+  if (!conv_aligned(cv)) return SSM_ERR_ALIGN;
   if (y != nullptr && (y == u || y == delta || (z != nullptr && y == z))) return SSM_ERR_ALIAS;
+  if (cv != nullptr && cv->state_out != nullptr &&
+      (cv->state_out == cv->state_in || (void*)cv->state_out == y || cv->state_out == last_state))
+    return SSM_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (empty) return SSM_OK;
 
-  if (seqlen == 0) {  // nothing to scan: the state stays h0 (or zero)
-    if (last_state == nullptr) return SSM_OK;
-    const hipError_t e = ssm::launch_fill_state(last_state, h0, (int64_t)batch * dim * dstate, st);
-    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  if (seqlen == 0) {  // nothing to scan: the states stay as they came in (or zero)
+    if (last_state != nullptr) {
+      const hipError_t e = ssm::launch_fill_state(last_state, h0, (int64_t)batch * dim * dstate, st);
+      if (e != hipSuccess) return SSM_ERR_HIP;
+    }
+    if (cv != nullptr && cv->state_out != nullptr && cv->k > 1) {
+      const hipError_t e =
+          ssm::launch_fill_state(cv->state_out, cv->state_in, (int64_t)batch * dim * (cv->k - 1), st);
+      if (e != hipSuccess) return SSM_ERR_HIP;
+    }
+    return SSM_OK;
   }
 
   const SegPlan sp = plan_segments(batch, dim, dstate, seqlen);
@@ -193,6 +225,13 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   a.nseg = sp.nseg;
   a.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
   a.zoh = (flags & SSM_BBAR_ZOH) ? 1 : 0;
+  if (cv != nullptr) {
+    a.conv_w = cv->w;
+    a.conv_b = cv->b;
+    a.conv_state_in = cv->state_in;
+    a.conv_state_out = cv->state_out;
+    a.conv_k = cv->k;
+  }
   const bool rows16 = ((int64_t)es * seqlen) % 16 == 0;
   a.vec = rows16 && aligned(u, 16) && aligned(delta, 16) && aligned(z, 16) && aligned(y, 16);
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
@@ -201,21 +240,28 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   return ssm::launch_scan_fwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
-int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
-                     const void* B, const void* C, const float* D_skip, const void* z,
-                     const float* delta_bias, int flags, void* y, int batch, int dim,
-                     int dstate, int dtype, void* stream) {
+int update_impl(float* state, const void* u, const void* delta, const float* A, const void* B,
+                const void* C, const float* D_skip, const void* z, const float* delta_bias,
+                int flags, void* y, int batch, int dim, int dstate, int dtype, void* stream,
+                const ConvIn* cv) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, 1)) return SSM_ERR_SHAPE;
+  if (cv != nullptr && (cv->k < 1 || cv->k > ssm::kMaxConvWidth)) return SSM_ERR_SHAPE;
   const bool empty = batch == 0 || dim == 0;
   if (!empty && (!state || !u || !delta || !A || !B || !C || !y)) return SSM_ERR_NULL;
+  if (!empty && cv != nullptr && (cv->w == nullptr || (cv->k > 1 && cv->state == nullptr)))
+    return SSM_ERR_NULL;
   const size_t es = (size_t)elem_bytes(dtype);
   if (!aligned(state, 4) || !aligned(u, es) || !aligned(delta, es) || !aligned(B, es) ||
       !aligned(C, es) || !aligned(z, es) || !aligned(y, es) || !aligned(A, 4) ||
       !aligned(D_skip, 4) || !aligned(delta_bias, 4))
     return SSM_ERR_ALIGN;
+  if (!conv_aligned(cv)) return SSM_ERR_ALIGN;
   if (y != nullptr && (y == u || y == delta || y == state || (z != nullptr && y == z)))
+    return SSM_ERR_ALIAS;
+  if (cv != nullptr && cv->state != nullptr &&
+      (cv->state == state || (void*)cv->state == y || (const void*)cv->state == u))
     return SSM_ERR_ALIAS;
   if (empty) return SSM_OK;
   const int64_t threads = (int64_t)batch * dim * (dstate >= 4 ? dstate / 4 : 1);
@@ -237,11 +283,59 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   a.dstate = dstate;
   a.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
   a.zoh = (flags & SSM_BBAR_ZOH) ? 1 : 0;
+  if (cv != nullptr) {
+    a.conv_state = cv->state;
+    a.conv_w = cv->w;
+    a.conv_b = cv->b;
+    a.conv_k = cv->k;
+  }
   // vector path: 16-byte state, A rows and (per lane) B, C pieces
   a.vec = (aligned(state, 16) && aligned(A, 16) && aligned(B, 4 * es) && aligned(C, 4 * es)) ? 1 : 0;
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
   return ssm::launch_state_update(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SSM_OK
                                                                                     : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D_skip, const void* z, const float* delta_bias, int flags,
+                 const float* h0, void* y, float* last_state, int batch, int dim, int dstate,
+                 int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return scan_impl(u, delta, A, B, C, D_skip, z, delta_bias, flags, h0, y, last_state, batch, dim,
+                   dstate, seqlen, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssm_conv_scan_fwd(const void* x, const float* conv_w, const float* conv_b, int conv_width,
+                      const float* conv_state_in, float* conv_state_out, const void* delta,
+                      const float* A, const void* B, const void* C, const float* D_skip,
+                      const void* z, const float* delta_bias, int flags, const float* h0, void* y,
+                      float* last_state, int batch, int dim, int dstate, int64_t seqlen, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const ConvIn cv{conv_w, conv_b, conv_state_in, conv_state_out, nullptr, conv_width};
+  return scan_impl(x, delta, A, B, C, D_skip, z, delta_bias, flags, h0, y, last_state, batch, dim,
+                   dstate, seqlen, dtype, workspace, workspace_bytes, stream, &cv);
+}
+
+int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
+                     const void* B, const void* C, const float* D_skip, const void* z,
+                     const float* delta_bias, int flags, void* y, int batch, int dim,
+                     int dstate, int dtype, void* stream) {
+  return update_impl(state, u, delta, A, B, C, D_skip, z, delta_bias, flags, y, batch, dim, dstate,
+                     dtype, stream, nullptr);
+}
+
+int ssm_conv_state_update(float* conv_state, float* state, const void* x, const float* conv_w,
+                          const float* conv_b, int conv_width, const void* delta, const float* A,
+                          const void* B, const void* C, const float* D_skip, const void* z,
+                          const float* delta_bias, int flags, void* y, int batch, int dim,
+                          int dstate, int dtype, void* stream) {
+  const ConvIn cv{conv_w, conv_b, nullptr, nullptr, conv_state, conv_width};
+  return update_impl(state, x, delta, A, B, C, D_skip, z, delta_bias, flags, y, batch, dim, dstate,
+                     dtype, stream, &cv);
 }
 
 const char* ssm_status_string(int status) {

@@ -13,6 +13,10 @@ constexpr int kScanTile = 16;
 // Storage type of the per-token tensors.
 enum class Dtype { F32 = 0, BF16 = 1 };
 
+// Kernel variants (bits of the MODE template argument).
+constexpr int kModeZoh = 1;   // zero-order-hold input term (else Euler)
+constexpr int kModeConv = 2;  // causal depthwise conv1d + silu applied to the input first
+
 struct ScanLaunch {
   const void* u;
   const void* delta;
@@ -37,6 +41,12 @@ struct ScanLaunch {
   int ncu;                // compute units of the device
   int prio_epochs;        // wave-priority rotations per segment (0: none)
   int zoh;                // zero-order-hold input term (else Euler)
+  // convolution prologue (conv_w null: none); u then holds its input x
+  const float* conv_w;          // (dim, conv_k)
+  const float* conv_b;          // (dim) nullable
+  const float* conv_state_in;   // (batch, dim, conv_k-1) nullable
+  float* conv_state_out;        // (batch, dim, conv_k-1) nullable
+  int conv_k;                   // 1..4
   Dtype dtype;
 };
 
@@ -55,8 +65,16 @@ struct DecodeLaunch {
   int softplus;
   int vec;                // state and A 16-byte aligned, B and C aligned to 4 elements
   int zoh;                // zero-order-hold input term (else Euler)
+  // convolution prologue (conv_w null: none); u then holds the token's x
+  float* conv_state;      // (batch, dim, conv_k-1), shifted in place; null when conv_k == 1
+  const float* conv_w;    // (dim, conv_k)
+  const float* conv_b;    // (dim) nullable
+  int conv_k;             // 1..4
   Dtype dtype;
 };
+
+// Widest convolution the kernels take.
+constexpr int kMaxConvWidth = 4;
 
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);

@@ -12,18 +12,27 @@
 // P = N/NS consecutive lanes per channel, so a wave reads and writes 1 KiB of
 // state contiguously.  The P partial readouts are summed with lane shuffles
 // in a fixed order.
+//
+// Optional convolution prologue (the decode step of the causal depthwise
+// conv1d + silu in front of the SSM): u = silu(cb + sum_k w[k] x[t-K+1+k])
+// from the carried K-1 previous inputs and this token's x; the carried
+// inputs are shifted in place to end with x.
 #include "ssm_kernels.hpp"
 #include "ssm_math.hpp"
 
 namespace ssm {
 
-template <typename T, int N, bool ZOH>
+template <typename T, int N, int MODE>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ u, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
     const float* __restrict__ Dskip, const T* __restrict__ z, const float* __restrict__ bias,
-    T* __restrict__ y, int batch, int dim, int softplus, int vec) {
+    T* __restrict__ y, int batch, int dim, int softplus, int vec,
+    float* __restrict__ conv_state, const float* __restrict__ conv_w,
+    const float* __restrict__ conv_b, int conv_k) {
   // vec: state, A, B and C are aligned for the vector loads below
+  constexpr bool ZOH = (MODE & kModeZoh) != 0;
+  constexpr bool CONV = (MODE & kModeConv) != 0;
   constexpr int NS = N < 4 ? N : 4;
   constexpr int P = N / NS;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -47,7 +56,30 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     for (int k = 0; k < NS; ++k) h[k] = sp[k];
   }
 
-  const float uv = Elem<T>::load(u + row);
+  float uv = Elem<T>::load(u + row);
+  if constexpr (CONV) {
+    // every lane of the channel forms u (a few FMAs); lane 0 shifts the
+    // carried inputs.  The lanes of a channel are in one wave and lane 0
+    // stores values its own loads returned, so the stores follow every
+    // lane's loads of conv_state.
+    const int K = conv_k;
+    float* cs = conv_state + row * (K - 1);
+    float prev[kMaxConvWidth - 1];
+#pragma unroll
+    for (int j = 0; j < kMaxConvWidth - 1; ++j) prev[j] = j < K - 1 ? cs[j] : 0.0f;
+    float sacc = conv_b != nullptr ? conv_b[d] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxConvWidth - 1; ++j)
+      if (j < K - 1) sacc = __builtin_fmaf(conv_w[(int64_t)d * K + j], prev[j], sacc);
+    sacc = __builtin_fmaf(conv_w[(int64_t)d * K + K - 1], uv, sacc);
+    if (part == 0 && K > 1) {
+#pragma unroll
+      for (int j = 0; j < kMaxConvWidth - 2; ++j)
+        if (j < K - 2) cs[j] = prev[j + 1];
+      cs[K - 2] = uv;
+    }
+    uv = silu_f32(sacc);
+  }
   const float x = Elem<T>::load(delta + row) + (bias != nullptr ? bias[d] : 0.0f);
   const float dt = softplus ? softplus_f32(x) : x;
   const float du = dt * uv;
@@ -107,37 +139,47 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   }
 }
 
-template <typename T, int N, bool ZOH>
+template <typename T, int N, int MODE>
 static hipError_t launch_n(const DecodeLaunch& a, hipStream_t stream) {
   constexpr int NS = N < 4 ? N : 4;
   constexpr int P = N / NS;
   const int64_t threads = (int64_t)a.batch * a.dim * P;
   const unsigned grid = (unsigned)((threads + 255) / 256);
-  state_update_kernel<T, N, ZOH><<<grid, 256, 0, stream>>>(
+  state_update_kernel<T, N, MODE><<<grid, 256, 0, stream>>>(
       a.state, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A,
       static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.Dskip,
       static_cast<const T*>(a.z), a.bias, static_cast<T*>(a.y), a.batch, a.dim, a.softplus,
-      a.vec);
+      a.vec, a.conv_state, a.conv_w, a.conv_b, a.conv_k);
   return hipGetLastError();
 }
 
-template <typename T, bool ZOH>
+template <typename T, int MODE>
 static hipError_t launch_t(const DecodeLaunch& a, hipStream_t stream) {
   switch (a.dstate) {
-    case 1: return launch_n<T, 1, ZOH>(a, stream);
-    case 2: return launch_n<T, 2, ZOH>(a, stream);
-    case 4: return launch_n<T, 4, ZOH>(a, stream);
-    case 8: return launch_n<T, 8, ZOH>(a, stream);
-    case 16: return launch_n<T, 16, ZOH>(a, stream);
+    case 1: return launch_n<T, 1, MODE>(a, stream);
+    case 2: return launch_n<T, 2, MODE>(a, stream);
+    case 4: return launch_n<T, 4, MODE>(a, stream);
+    case 8: return launch_n<T, 8, MODE>(a, stream);
+    case 16: return launch_n<T, 16, MODE>(a, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+static hipError_t launch_mode(const DecodeLaunch& a, hipStream_t stream) {
+  const int mode = (a.zoh ? kModeZoh : 0) | (a.conv_w != nullptr ? kModeConv : 0);
+  switch (mode) {
+    case 0: return launch_t<T, 0>(a, stream);
+    case kModeZoh: return launch_t<T, kModeZoh>(a, stream);
+    case kModeConv: return launch_t<T, kModeConv>(a, stream);
+    default: return launch_t<T, kModeZoh | kModeConv>(a, stream);
   }
 }
 
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream) {
   if (a.batch == 0 || a.dim == 0) return hipSuccess;
-  if (a.dtype == Dtype::BF16)
-    return a.zoh ? launch_t<uint16_t, true>(a, stream) : launch_t<uint16_t, false>(a, stream);
-  return a.zoh ? launch_t<float, true>(a, stream) : launch_t<float, false>(a, stream);
+  if (a.conv_w != nullptr && (a.conv_k < 1 || a.conv_k > kMaxConvWidth)) return hipErrorInvalidValue;
+  return a.dtype == Dtype::BF16 ? launch_mode<uint16_t>(a, stream) : launch_mode<float>(a, stream);
 }
 
 }  // namespace ssm

@@ -48,16 +48,8 @@ def ssm_scan_fwd_workspace_bytes(batch: int, dim: int, dstate: int, seqlen: int,
     return int(load().ssm_scan_fwd_workspace_bytes(batch, dim, dstate, seqlen, _DTYPES[dtype]))
 
 
-def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                 h0=None, *, bbar="euler", return_last_state=False, out=None, workspace=None):
-    """Selective scan over (batch, dim, L) inputs; see include/ssm.h.
-    bbar: 'euler' (input term Delta*B*u) or 'zoh' ((exp(Delta*A) - 1)/A*B*u,
-    A nonzero).
-
-    u, delta, z: (batch, dim, L) float32 or bfloat16 (one dtype for all);
-    B, C: (batch, N, L) same dtype; A: (dim, N) float32; D, delta_bias: (dim,)
-    float32; h0: (batch, dim, N) float32.  Returns y (batch, dim, L) in the
-    input dtype, and (y, last_state) when return_last_state is set."""
+def _scan(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, bbar, return_last_state, out,
+          workspace, conv):
     lib = load()
     dev = u.device
     if dev.type != "cuda":
@@ -66,7 +58,8 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     code = _code(u)
     batch, dim, L = u.shape
     N = A.shape[1] if A.dim() == 2 else -1
-    _check("u", u, (batch, dim, L), dt, dev)
+    name = "x" if conv is not None else "u"
+    _check(name, u, (batch, dim, L), dt, dev)
     _check("delta", delta, (batch, dim, L), dt, dev)
     _check("A", A, (dim, N), torch.float32, dev)
     _check("B", B, (batch, N, L), dt, dev)
@@ -87,18 +80,61 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     else:
         workspace = None
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(y),
-                          _ptr(last), batch, dim, N, L, code, _ptr(workspace), ws_bytes, stream)
+    flags = _flags(delta_softplus, bbar)
+    if conv is None:
+        rc = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(delta_bias), flags, _ptr(h0), _ptr(y), _ptr(last), batch, dim, N,
+                              L, code, _ptr(workspace), ws_bytes, stream)
+        if rc != 0:
+            raise SsmError(rc, "ssm_scan_fwd")
+        return (y, last) if return_last_state else y
+    w, cb, st_in, want_state = conv
+    K = w.shape[1] if w.dim() == 2 else -1
+    _check("conv_w", w, (dim, K), torch.float32, dev)
+    _check("conv_b", cb, (dim,), torch.float32, dev, required=False)
+    _check("conv_state_in", st_in, (batch, dim, K - 1), torch.float32, dev, required=False)
+    st_out = (torch.empty((batch, dim, max(K - 1, 0)), dtype=torch.float32, device=dev)
+              if want_state else None)
+    rc = lib.ssm_conv_scan_fwd(_ptr(u), _ptr(w), _ptr(cb), K, _ptr(st_in),
+                               _ptr(st_out) if K > 1 else None, _ptr(delta), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), flags, _ptr(h0), _ptr(y),
+                               _ptr(last), batch, dim, N, L, code, _ptr(workspace), ws_bytes, stream)
     if rc != 0:
-        raise SsmError(rc, "ssm_scan_fwd")
-    return (y, last) if return_last_state else y
+        raise SsmError(rc, "ssm_conv_scan_fwd")
+    res = (y,)
+    if return_last_state:
+        res += (last,)
+    if want_state:
+        res += (st_out,)
+    return res[0] if len(res) == 1 else res
 
 
-def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                     delta_softplus=True, *, bbar="euler", out=None):
-    """One decode step; `state` (batch, dim, N) float32 is updated in place.
-    u, delta, z: (batch, dim); B, C: (batch, N); returns y (batch, dim)."""
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 h0=None, *, bbar="euler", return_last_state=False, out=None, workspace=None):
+    """Selective scan over (batch, dim, L) inputs; see include/ssm.h.
+    bbar: 'euler' (input term Delta*B*u) or 'zoh' ((exp(Delta*A) - 1)/A*B*u).
+
+    u, delta, z: (batch, dim, L) float32 or bfloat16 (one dtype for all);
+    B, C: (batch, N, L) same dtype; A: (dim, N) float32; D, delta_bias: (dim,)
+    float32; h0: (batch, dim, N) float32.  Returns y (batch, dim, L) in the
+    input dtype, and (y, last_state) when return_last_state is set."""
+    return _scan(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, bbar, return_last_state,
+                 out, workspace, None)
+
+
+def ssm_conv_scan_fwd(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                      delta_softplus=True, h0=None, *, conv_state_in=None, return_conv_state=False,
+                      bbar="euler", return_last_state=False, out=None, workspace=None):
+    """The scan with the causal depthwise conv1d + silu prologue fused in:
+    u = silu(conv_b + causal conv of x with conv_w (dim, K), K in 1..4).
+    conv_state_in: (batch, dim, K-1) float32, the inputs before t = 0.
+    Returns y, then last_state (if return_last_state), then the new conv
+    state (if return_conv_state)."""
+    return _scan(x, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, bbar, return_last_state,
+                 out, workspace, (conv_w, conv_b, conv_state_in, return_conv_state))
+
+
+def _update(state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, bbar, out, conv):
     lib = load()
     dev = state.device
     if dev.type != "cuda":
@@ -107,7 +143,7 @@ def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     code = _code(u)
     batch, dim, N = state.shape
     _check("state", state, (batch, dim, N), torch.float32, dev)
-    _check("u", u, (batch, dim), dt, dev)
+    _check("x" if conv is not None else "u", u, (batch, dim), dt, dev)
     _check("delta", delta, (batch, dim), dt, dev)
     _check("A", A, (dim, N), torch.float32, dev)
     _check("B", B, (batch, N), dt, dev)
@@ -118,9 +154,38 @@ def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     y = out if out is not None else torch.empty_like(u)
     _check("out", y, (batch, dim), dt, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                              _ptr(D), _ptr(z), _ptr(delta_bias), _flags(delta_softplus, bbar),
-                              _ptr(y), batch, dim, N, code, stream)
+    flags = _flags(delta_softplus, bbar)
+    if conv is None:
+        rc = lib.ssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                  _ptr(D), _ptr(z), _ptr(delta_bias), flags, _ptr(y), batch, dim, N,
+                                  code, stream)
+        if rc != 0:
+            raise SsmError(rc, "ssm_state_update")
+        return y
+    cs, w, cb = conv
+    K = w.shape[1] if w.dim() == 2 else -1
+    _check("conv_w", w, (dim, K), torch.float32, dev)
+    _check("conv_b", cb, (dim,), torch.float32, dev, required=False)
+    _check("conv_state", cs, (batch, dim, K - 1), torch.float32, dev, required=K > 1)
+    rc = lib.ssm_conv_state_update(_ptr(cs) if K > 1 else None, _ptr(state), _ptr(u), _ptr(w),
+                                   _ptr(cb), K, _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(z), _ptr(delta_bias), flags, _ptr(y), batch, dim, N, code,
+                                   stream)
     if rc != 0:
-        raise SsmError(rc, "ssm_state_update")
+        raise SsmError(rc, "ssm_conv_state_update")
     return y
+
+
+def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                     delta_softplus=True, *, bbar="euler", out=None):
+    """One decode step; `state` (batch, dim, N) float32 is updated in place.
+    u, delta, z: (batch, dim); B, C: (batch, N); returns y (batch, dim)."""
+    return _update(state, u, delta, A, B, C, D, z, delta_bias, delta_softplus, bbar, out, None)
+
+
+def ssm_conv_state_update(conv_state, state, x, conv_w, conv_b, delta, A, B, C, D=None, z=None,
+                          delta_bias=None, delta_softplus=True, *, bbar="euler", out=None):
+    """One decode step with the convolution prologue; conv_state
+    (batch, dim, K-1) and state (batch, dim, N) are updated in place."""
+    return _update(state, x, delta, A, B, C, D, z, delta_bias, delta_softplus, bbar, out,
+                   (conv_state, conv_w, conv_b))

@@ -16,8 +16,12 @@ Fixed draw order from ``default_rng(seed)``:
   A jitter -> dt (-> bias) -> D -> delta_raw -> u -> B -> C -> z
 and for the decode workload, after D: h0; each decode step s then draws
   delta_raw -> u -> B -> C -> z  from ``default_rng([seed, s])``.
+The convolution prologue's taps, bias and carried state come from
+``default_rng([seed, 1_000_003])`` (make_conv_params), a key no decode
+step uses; its input x is the workload's u draw.
 """
 from .configs import (ScanConfig, DecodeConfig, SCAN_CONFIGS, DECODE_CONFIG,  # noqa: F401
                       CONFIGS, get_config)
 from .inputs import (bf16_bits, bf16_to_f32, make_scan_inputs, make_decode_params,  # noqa: F401
-                     make_decode_step, impulse_inputs, widen, inv_softplus_bias)
+                     make_decode_step, impulse_inputs, widen, inv_softplus_bias,
+                     make_conv_params)

@@ -109,3 +109,20 @@ def impulse_inputs() -> dict:
     C = np.array([[[2.0] * L, [-1.0] * L]], dtype=np.float32)
     bias = np.array([math.log(math.e - 1.0)], dtype=np.float32)
     return dict(u=u, delta=delta, A=A, B=B, C=C, D=None, z=None, delta_bias=bias, dtype="f32")
+
+
+def make_conv_params(dim: int, width: int, seed: int, state_batch: int | None = None) -> dict:
+    """Convolution prologue parameters, drawn from ``default_rng([seed, 1_000_003])``
+    in the order w -> b (-> state): taps w (dim, width) and bias b (dim,)
+    uniform in +-1/sqrt(width) (the fan-in of a depthwise filter), and when
+    state_batch is given a carried input state (state_batch, dim, width-1)
+    ~ N(0, 1).  All float32."""
+    rng = np.random.default_rng([seed, 1_000_003])
+    bound = 1.0 / math.sqrt(width)
+    w = rng.uniform(-bound, bound, size=(dim, width)).astype(np.float32)
+    b = rng.uniform(-bound, bound, size=dim).astype(np.float32)
+    out = dict(conv_w=w, conv_b=b, conv_state=None)
+    if state_batch is not None:
+        out["conv_state"] = rng.standard_normal(size=(state_batch, dim, width - 1),
+                                                dtype=np.float32)
+    return out

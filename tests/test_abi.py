@@ -14,7 +14,7 @@ P = 0x10000  # a 256-byte aligned fake device address, never dereferenced
 def test_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) == {"ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
-                          "ssm_status_string"}
+                          "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_status_string"}
     lib = ctypes.CDLL(load()._name)
     for n in names:
         assert hasattr(lib, n), n
@@ -113,3 +113,56 @@ def test_python_bbar_mode_is_checked():
     assert _flags(True, "zoh") == 3 and _flags(False, "zoh") == 2
     with pytest.raises(ValueError):
         _flags(True, "bilinear")
+
+
+def _cscan(**kw):
+    a = dict(x=P, w=P + 0x200000, cb=None, K=4, sin=None, sout=None, delta=P, A=P, B=P, C=P, D=None,
+             z=None, bias=None, fl=1, h0=None, y=P + 0x100000, last=None, batch=1, dim=64,
+             dstate=16, L=2048, dtype=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return load().ssm_conv_scan_fwd(a["x"], a["w"], a["cb"], a["K"], a["sin"], a["sout"], a["delta"],
+                                    a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["fl"],
+                                    a["h0"], a["y"], a["last"], a["batch"], a["dim"], a["dstate"],
+                                    a["L"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+def _cupd(**kw):
+    a = dict(cs=P + 0x300000, state=P, x=P, w=P + 0x200000, cb=None, K=4, delta=P, A=P, B=P, C=P,
+             D=None, z=None, bias=None, fl=1, y=P + 0x100000, batch=4, dim=64, dstate=16, dtype=1,
+             stream=None)
+    a.update(kw)
+    return load().ssm_conv_state_update(a["cs"], a["state"], a["x"], a["w"], a["cb"], a["K"],
+                                        a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                        a["bias"], a["fl"], a["y"], a["batch"], a["dim"],
+                                        a["dstate"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), SHAPE), (dict(K=5), SHAPE), (dict(K=-1), SHAPE),
+    (dict(w=None), NULL), (dict(x=None), NULL),
+    (dict(w=P + 0x200002), ALIGN), (dict(cb=P + 1), ALIGN), (dict(sin=P + 2), ALIGN),
+    (dict(sout=P + 3), ALIGN),
+    (dict(sin=P + 0x400000, sout=P + 0x400000), ALIAS), (dict(sout=P + 0x100000), ALIAS),
+    (dict(y=P), ALIAS), (dict(fl=4), FLAGS), (dict(dtype=3), DTYPE), (dict(dstate=5), SHAPE),
+])
+def test_conv_scan_validation(kw, code):
+    assert _cscan(**kw) == code
+
+
+def test_conv_scan_workspace_checked_before_launch():
+    assert _cscan(ws=None, wsb=0) == WS
+    assert _cscan(batch=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), SHAPE), (dict(K=7), SHAPE), (dict(w=None), NULL), (dict(cs=None), NULL),
+    (dict(cs=P + 0x300002), ALIGN), (dict(cs=P), ALIAS), (dict(cs=P + 0x100000), ALIAS),
+    (dict(fl=8), FLAGS), (dict(state=None), NULL),
+])
+def test_conv_update_validation(kw, code):
+    assert _cupd(**kw) == code
+
+
+def test_conv_update_width_one_needs_no_state():
+    # K = 1: no carried inputs; an empty problem returns before any launch
+    assert _cupd(cs=None, K=1, batch=0) == OK
