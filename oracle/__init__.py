@@ -17,7 +17,8 @@ state them): parity unpinned by the pages for those two terms.  The
 convolution prologue (causal_conv1d_silu, conv_step) is pinned against numpy's
 convolution with the taps reversed, its identity and delay special cases,
 and its own chunking and decode identities; its tap order, width and
-non-linearity are readings of the pages, not printed on them.
+non-linearity are readings of the pages, not printed on them.  The backward
+(scan_bwd) is pinned by central finite differences of the forward, in fp64.
 """
 from .oracle import (build, causal_conv1d_silu, conv_scan_fwd, conv_step,  # noqa: F401
-                     lib_path, scan_fwd, state_update)
+                     lib_path, scan_bwd, scan_fwd, state_update)

@@ -47,6 +47,10 @@ def _load():
     lib.oracle_state_update.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
                                         ctypes.c_int, dp, L, L, L]
     lib.oracle_state_update.restype = ctypes.c_int
+    lib.oracle_scan_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,
+                                    dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, L, L, L, L,
+                                    ctypes.c_int]
+    lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_causal_conv1d_silu.argtypes = [dp, dp, dp, L, dp, dp, dp, L, L, L]
     lib.oracle_causal_conv1d_silu.restype = ctypes.c_int
     lib.oracle_conv_step.argtypes = [dp, dp, dp, dp, L, dp, L, L]
@@ -120,6 +124,32 @@ def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise RuntimeError(f"oracle_state_update failed with {rc}")
     return y, st
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, h0=None,
+             dy=None, dlast=None, nthreads=1, bbar="euler"):
+    """Gradients of L = sum(dy * y) + sum(dlast * last_state) for scan_fwd
+    with the same arguments.  Returns a dict of float64 arrays: du, ddelta,
+    dA, dB, dC, dD, dz (None without a gate), ddelta_bias, dh0."""
+    u, delta, A, B, C = map(_f64, (u, delta, A, B, C))
+    D, z, delta_bias, h0, dy, dlast = map(_f64, (D, z, delta_bias, h0, dy, dlast))
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    assert dy is not None and dy.shape == u.shape
+    assert dlast is None or dlast.shape == (batch, dim, N)
+    out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA=np.empty((dim, N)),
+               dB=np.empty((batch, N, L)), dC=np.empty((batch, N, L)), dD=np.empty(dim),
+               dz=np.empty_like(u) if z is not None else None, ddelta_bias=np.empty(dim),
+               dh0=np.empty((batch, dim, N)))
+    rc = _load().oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(delta_bias), int(bool(delta_softplus)), _zoh(bbar), _ptr(h0),
+                                 _ptr(dy), _ptr(dlast), _ptr(out["du"]), _ptr(out["ddelta"]),
+                                 _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                                 _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+                                 batch, dim, N, L, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan_bwd failed with {rc}")
+    return out
 
 
 def causal_conv1d_silu(x, w, cb=None, state_in=None):

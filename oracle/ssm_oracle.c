@@ -45,6 +45,14 @@
  *    zero).  oracle_causal_conv1d_silu computes it on its own; its output is
  *    the u of the scan.
  *
+ * Backward (oracle_scan_bwd): the gradients of L = sum_t dy_t . y_t (plus
+ * dlast . last_state) with respect to every input, by the chain rule through
+ * the same sequential definition -- the recomputation the "Mamba" paper
+ * review describes under "Optimization" (the intermediate states are
+ * recomputed from the inputs, not stored).  Per channel: a forward sweep
+ * keeps every h_t, then a reverse sweep carries the adjoint
+ * lambda_t = dL/dh_t = ds_t C_t + Abar_{t+1} lambda_{t+1}.
+ *
  * Precision: every input is widened to double before use and all arithmetic
  * is double.  No blocking, fusion or reordering beyond the sequential
  * definition: each row walks t = 0..L-1 in order, and within a step the
@@ -270,4 +278,164 @@ int oracle_conv_step(double *conv_state, const double *x, const double *w, const
     if (H > 0) cs[H - 1] = x[row];
   }
   return 0;
+}
+
+/* silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))) */
+static double silu_grad(double z) {
+  const double sg = 1.0 / (1.0 + exp(-z));
+  return sg * (1.0 + z * (1.0 - sg));
+}
+
+/* d Bbar / d Delta and d Bbar / d A for the input coefficient of bbar(). */
+static double bbar_d_dt(double dt, double a, int zoh) {
+  if (!zoh) return 1.0;
+  return exp(dt * a); /* d/dDelta (e^{Delta A} - 1)/A = e^{Delta A}, also at A = 0 */
+}
+static double bbar_d_a(double dt, double a, int zoh) {
+  if (!zoh) return 0.0;
+  if (a == 0.0) return 0.5 * dt * dt; /* limit of (Delta A e^{Delta A} - (e^{Delta A} - 1))/A^2 */
+  const double e = exp(dt * a);
+  return (dt * a * e - expm1(dt * a)) / (a * a);
+}
+
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *Dskip, *z, *bias, *h0, *dy, *dlast;
+  int softplus_on, zoh;
+  long batch, dim, dstate, seqlen;
+  long row_begin, row_end;
+  /* outputs: per-element ones written directly, reduced ones per job */
+  double *du, *ddelta, *dz, *dh0;
+  double *dA, *dB, *dC, *dD, *dbias; /* this job's private sums */
+} bwd_job;
+
+static void *bwd_worker(void *arg) {
+  bwd_job *j = (bwd_job *)arg;
+  const long N = j->dstate, L = j->seqlen, dim = j->dim;
+  double *hs = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));
+  double *dts = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double *ss = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  double *lam = (double *)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !dts || !ss || !lam) { free(hs); free(dts); free(ss); free(lam); return (void *)1; }
+  for (long row = j->row_begin; row < j->row_end; ++row) {
+    const long b = row / dim, d = row % dim;
+    const double *u = j->u + row * L, *dr = j->delta + row * L;
+    const double *z = j->z ? j->z + row * L : NULL;
+    const double *gy = j->dy + row * L;
+    const double *Bb = j->B + b * N * L, *Cb = j->C + b * N * L, *Ad = j->A + d * N;
+    const double bias = j->bias ? j->bias[d] : 0.0;
+    const double Dd = j->Dskip ? j->Dskip[d] : 0.0;
+    /* forward sweep: hs[(t+1)*N + n] = h_t, hs[n] = h_{-1} */
+    for (long n = 0; n < N; ++n) hs[n] = j->h0 ? j->h0[row * N + n] : 0.0;
+    for (long t = 0; t < L; ++t) {
+      const double x = dr[t] + bias;
+      const double dt = j->softplus_on ? softplus(x) : x;
+      dts[t] = dt;
+      double acc = 0.0;
+      for (long n = 0; n < N; ++n) {
+        const double h = exp(dt * Ad[n]) * hs[t * N + n] + bbar(dt, Ad[n], j->zoh) * Bb[n * L + t] * u[t];
+        hs[(t + 1) * N + n] = h;
+        acc += Cb[n * L + t] * h;
+      }
+      ss[t] = acc + Dd * u[t]; /* the output before the gate */
+    }
+    /* reverse sweep */
+    for (long n = 0; n < N; ++n) lam[n] = j->dlast ? j->dlast[row * N + n] : 0.0;
+    for (long t = L - 1; t >= 0; --t) {
+      const double dt = dts[t];
+      double ds = gy[t];
+      if (z) {
+        j->dz[row * L + t] = gy[t] * ss[t] * silu_grad(z[t]);
+        ds = gy[t] * silu(z[t]);
+      }
+      j->dD[d] += ds * u[t];
+      double du = ds * Dd, ddt = 0.0;
+      for (long n = 0; n < N; ++n) {
+        const double h = hs[(t + 1) * N + n], hp = hs[t * N + n];
+        const double a = exp(dt * Ad[n]);
+        const double bb = bbar(dt, Ad[n], j->zoh);
+        const double bu = Bb[n * L + t] * u[t];
+        lam[n] += ds * Cb[n * L + t];            /* dL/dh_t */
+        j->dC[b * N * L + n * L + t] += ds * h;
+        ddt += lam[n] * (hp * a * Ad[n] + bbar_d_dt(dt, Ad[n], j->zoh) * bu);
+        j->dA[d * N + n] += lam[n] * (hp * a * dt + bbar_d_a(dt, Ad[n], j->zoh) * bu);
+        j->dB[b * N * L + n * L + t] += lam[n] * bb * u[t];
+        du += lam[n] * bb * Bb[n * L + t];
+        lam[n] *= a;                             /* dL/dh_{t-1} */
+      }
+      j->du[row * L + t] = du;
+      const double x = dr[t] + bias;
+      const double dx = j->softplus_on ? ddt / (1.0 + exp(-x)) : ddt; /* softplus' = sigmoid */
+      j->ddelta[row * L + t] = dx;
+      j->dbias[d] += dx;
+    }
+    if (j->dh0)
+      for (long n = 0; n < N; ++n) j->dh0[row * N + n] = lam[n];
+  }
+  free(hs); free(dts); free(ss); free(lam);
+  return NULL;
+}
+
+/*
+ * oracle_scan_bwd: gradients of L = sum(dy * y) + sum(dlast * last_state)
+ * for the forward scan of oracle_scan_fwd (same arguments and layouts).
+ *   dy        : (batch, dim, seqlen)           required
+ *   dlast     : (batch, dim, dstate) or NULL   (NULL -> 0)
+ *   du, ddelta: (batch, dim, seqlen)           written
+ *   dz        : (batch, dim, seqlen)           written when z is given
+ *   dA        : (dim, dstate); dB, dC: (batch, dstate, seqlen);
+ *   dD, dbias : (dim,); dh0: (batch, dim, dstate) or NULL -- all written
+ * Rows are split over nthreads workers; the reduced gradients are summed
+ * per worker and then over workers in worker order.
+ */
+int oracle_scan_bwd(const double *u, const double *delta, const double *A, const double *B,
+                    const double *C, const double *Dskip, const double *z, const double *bias,
+                    int softplus_on, int zoh, const double *h0, const double *dy,
+                    const double *dlast, double *du, double *ddelta, double *dA, double *dB,
+                    double *dC, double *dD, double *dz, double *dbias, double *dh0, long batch,
+                    long dim, long dstate, long seqlen, int nthreads) {
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC || !dD ||
+      !dbias || (z && !dz))
+    return -1;
+  if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0) return -1;
+  const long rows = batch * dim, N = dstate, L = seqlen;
+  const size_t nA = (size_t)(dim * N), nBC = (size_t)(batch * N * L), nd = (size_t)dim;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > rows && rows > 0) nthreads = (int)rows;
+  double *priv = (double *)calloc((size_t)nthreads * (nA + 2 * nBC + 2 * nd) + 1, sizeof(double));
+  bwd_job *jobs = (bwd_job *)malloc(sizeof(bwd_job) * (size_t)nthreads);
+  pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!priv || !jobs || !tid) { free(priv); free(jobs); free(tid); return -2; }
+  int rc = 0, started = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    double *p = priv + (size_t)i * (nA + 2 * nBC + 2 * nd);
+    bwd_job jb = {u, delta, A, B, C, Dskip, z, bias, h0, dy, dlast, softplus_on, zoh,
+                  batch, dim, dstate, seqlen, rows * i / nthreads, rows * (i + 1) / nthreads,
+                  du, ddelta, dz, dh0, p, p + nA, p + nA + nBC, p + nA + 2 * nBC,
+                  p + nA + 2 * nBC + nd};
+    jobs[i] = jb;
+  }
+  if (nthreads == 1) {
+    rc = bwd_worker(&jobs[0]) ? -2 : 0;
+  } else {
+    for (int i = 0; i < nthreads; ++i) {
+      if (pthread_create(&tid[i], NULL, bwd_worker, &jobs[i]) != 0) { rc = -2; break; }
+      ++started;
+    }
+    for (int i = 0; i < started; ++i) {
+      void *ret = NULL;
+      pthread_join(tid[i], &ret);
+      if (ret) rc = -2;
+    }
+  }
+  for (size_t k = 0; k < nA; ++k) dA[k] = 0.0;
+  for (size_t k = 0; k < nBC; ++k) dB[k] = dC[k] = 0.0;
+  for (size_t k = 0; k < nd; ++k) dD[k] = dbias[k] = 0.0;
+  for (int i = 0; i < nthreads; ++i) {
+    const bwd_job *jb = &jobs[i];
+    for (size_t k = 0; k < nA; ++k) dA[k] += jb->dA[k];
+    for (size_t k = 0; k < nBC; ++k) { dB[k] += jb->dB[k]; dC[k] += jb->dC[k]; }
+    for (size_t k = 0; k < nd; ++k) { dD[k] += jb->dD[k]; dbias[k] += jb->dbias[k]; }
+  }
+  free(priv); free(jobs); free(tid);
+  return rc;
 }

@@ -538,3 +538,91 @@ def test_conv_scan_is_conv_then_scan():
                                 kw["delta_bias"])
     np.testing.assert_allclose(y, y2, rtol=1e-14, atol=1e-15)
     np.testing.assert_allclose(last, last2, rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- backward
+# "Mamba" paper review, "Optimization": the backward pass recomputes the
+# intermediate states from the inputs.  The oracle's gradients are pinned by
+# central finite differences of its own forward pass (fp64): a dropped term,
+# a wrong sign or a transposed index in any gradient fails them.
+
+def _loss(kw, dy, dlast, bbar, softplus=True):
+    y, last = oracle.scan_fwd(**kw, delta_softplus=softplus, bbar=bbar)
+    return float(np.sum(dy * y) + (np.sum(dlast * last) if dlast is not None else 0.0))
+
+
+def _fd_check(kw, dy, dlast, bbar, softplus=True, rel=2e-7):
+    g = oracle.scan_bwd(**kw, delta_softplus=softplus, dy=dy, dlast=dlast, bbar=bbar)
+    names = dict(u="du", delta="ddelta", A="dA", B="dB", C="dC", D="dD", z="dz",
+                 delta_bias="ddelta_bias", h0="dh0")
+    for key, gname in names.items():
+        if kw.get(key) is None:
+            continue
+        x = kw[key]
+        fd = np.empty_like(x)
+        for i in np.ndindex(x.shape):
+            old = x[i]
+            eps = 1e-6 * max(1.0, abs(old))
+            x[i] = old + eps
+            lp = _loss(kw, dy, dlast, bbar, softplus)
+            x[i] = old - eps
+            lm = _loss(kw, dy, dlast, bbar, softplus)
+            x[i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        scale = max(np.abs(fd).max(), 1e-300)
+        err = np.abs(g[gname] - fd).max() / scale
+        assert err <= rel, (gname, bbar, err)
+    return g
+
+
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+@pytest.mark.parametrize("gate,dskip,h0,dlast", [(True, True, True, True), (False, False, False, False),
+                                                 (True, False, False, True)])
+def test_backward_equals_finite_differences(bbar, gate, dskip, h0, dlast):
+    rng = np.random.default_rng(200)
+    kw = _tiny_case(rng, batch=2, dim=3, N=4, L=9, gate=gate, dskip=dskip, h0=h0)
+    dy = rng.standard_normal(kw["u"].shape)
+    dl = rng.standard_normal((2, 3, 4)) if dlast else None
+    _fd_check(kw, dy, dl, bbar)
+
+
+def test_backward_without_softplus_and_near_zero_A():
+    rng = np.random.default_rng(201)
+    kw = _tiny_case(rng, batch=1, dim=2, N=3, L=7, h0=True)
+    kw["delta"] = np.abs(kw["delta"]) * 0.3
+    kw["delta_bias"] = None
+    kw["A"][0, 0] = 0.0          # the zero-order-hold coefficient at its A = 0 limit
+    kw["A"][1, 1] = -1e-4
+    dy = rng.standard_normal(kw["u"].shape)
+    for bbar in ("euler", "zoh"):
+        _fd_check(kw, dy, None, bbar, softplus=False, rel=1e-6)
+
+
+def test_backward_threads_do_not_change_results():
+    rng = np.random.default_rng(202)
+    kw = _tiny_case(rng, batch=3, dim=5, N=4, L=20, h0=True)
+    dy = rng.standard_normal(kw["u"].shape)
+    g1 = oracle.scan_bwd(**kw, dy=dy, nthreads=1)
+    g4 = oracle.scan_bwd(**kw, dy=dy, nthreads=4)
+    for k in g1:
+        if g1[k] is not None:
+            np.testing.assert_allclose(g4[k], g1[k], rtol=1e-13, atol=1e-14)
+
+
+def test_backward_of_linear_special_case():
+    """A = 0, no gate, no D, softplus off: y_t = sum_{s<=t} (C_t . B_s) Delta_s u_s,
+    so dC[:, t] = sum_{s<=t} B_s Delta_s u_s dy_t and du_s = Delta_s sum_{t>=s} dy_t (C_t . B_s)."""
+    rng = np.random.default_rng(203)
+    N, L = 3, 12
+    u = rng.standard_normal(L)
+    dl = rng.uniform(0.1, 0.9, size=L)
+    B = rng.standard_normal((N, L))
+    C = rng.standard_normal((N, L))
+    dy = rng.standard_normal(L)
+    g = oracle.scan_bwd(u.reshape(1, 1, L), dl.reshape(1, 1, L), np.zeros((1, N)),
+                        B.reshape(1, N, L), C.reshape(1, N, L), delta_softplus=False,
+                        dy=dy.reshape(1, 1, L))
+    S = np.cumsum(B * (dl * u)[None, :], axis=1)
+    np.testing.assert_allclose(g["dC"][0], S * dy[None, :], rtol=1e-12, atol=1e-13)
+    M = np.tril(C.T @ B)          # M[t, s] = C_t . B_s for s <= t
+    np.testing.assert_allclose(g["du"][0, 0], dl * (M.T @ dy), rtol=1e-12, atol=1e-13)
