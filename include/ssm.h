@@ -205,6 +205,52 @@ int ssm_conv_state_update(float* conv_state, float* state, const void* x, const 
                           const float* delta_bias, int flags, void* y, int batch, int dim,
                           int dstate, int dtype, void* stream);
 
+/*
+ * ssm_scan_bwd_workspace_bytes -- bytes of device workspace ssm_scan_bwd
+ * needs: the forward workspace, the state entering every 16-step tile
+ * (batch * ceil(seqlen/16) * dstate * dim floats), partial sums of dB and dC
+ * per 64-channel group (batch * ceil(dim/64) * 2 * dstate * seqlen floats),
+ * and small per-segment terms.  Pure host function; 0 for an empty problem
+ * and for arguments ssm_scan_bwd would reject.
+ */
+size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int dstate, int64_t seqlen, int dtype);
+
+/*
+ * ssm_scan_bwd -- gradients of a loss L through ssm_scan_fwd, given
+ * dy = dL/dy and optionally dlast_state = dL/dlast_state.  The states are
+ * recomputed from the inputs, not read from a saved forward pass: the
+ * "Mamba" paper review, "Optimization" (recomputation for backpropagation).
+ * Per channel the adjoint lambda_t = dL/dh_t runs backwards,
+ * lambda_t = ds_t C_t + Abar_{t+1} lambda_{t+1} with ds_t = dy_t silu(z_t),
+ * and every gradient is the chain rule through the formula at the top.
+ *
+ *   u .. h0          in   as for ssm_scan_fwd (same layouts and dtype)
+ *   flags            SSM_DELTA_SOFTPLUS only: the backward covers the Euler
+ *                    input term (SSM_BBAR_ZOH returns SSM_ERR_FLAGS)
+ *   dy               in   (batch, dim, seqlen), dtype          required
+ *   dlast_state      in   (batch, dim, dstate) float32         NULL -> 0
+ *   du, ddelta       out  (batch, dim, seqlen), dtype          required
+ *                         (ddelta is dL/d(delta), before the bias and softplus)
+ *   dA               out  (dim, dstate) float32                required
+ *   dB, dC           out  (batch, dstate, seqlen), dtype       required
+ *   dD               out  (dim) float32                        NULL -> not written
+ *   dz               out  (batch, dim, seqlen), dtype          required when z is given
+ *   ddelta_bias      out  (dim) float32                        NULL -> not written
+ *   dh0              out  (batch, dim, dstate) float32         NULL -> not written
+ *                         (dL/dh0, also when h0 is NULL)
+ *   workspace        at least ssm_scan_bwd_workspace_bytes(...) bytes, 256-byte
+ *                    aligned, owned by the caller.
+ * Outputs must not alias the per-token inputs (SSM_ERR_ALIAS).  dA, dB, dC,
+ * dD and ddelta_bias are sums formed in float32 in a fixed order: the same
+ * inputs give the same bits.  seqlen == 0 writes zeros and dh0 = dlast_state.
+ */
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D_skip, const void* z, const float* delta_bias, int flags,
+                 const float* h0, const void* dy, const float* dlast_state, void* du, void* ddelta,
+                 float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                 float* dh0, int batch, int dim, int dstate, int64_t seqlen, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ssm_status_string -- a static, human-readable name for a status code. */
 const char* ssm_status_string(int status);
 

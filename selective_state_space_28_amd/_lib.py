@@ -51,6 +51,11 @@ def load():
     lib.ssm_conv_state_update.argtypes = [fp, fp, vp, fp, fp, i32, vp, fp, vp, vp, fp, vp, fp, i32,
                                           vp, i32, i32, i32, i32, vp]
     lib.ssm_conv_state_update.restype = i32
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
+    lib.ssm_scan_bwd_workspace_bytes.restype = sz
+    lib.ssm_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, vp, vp, fp, vp,
+                                 vp, fp, vp, fp, fp, i32, i32, i32, i64, i32, vp, sz, vp]
+    lib.ssm_scan_bwd.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     _lib = lib

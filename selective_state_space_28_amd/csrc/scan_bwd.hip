@@ -1,0 +1,520 @@
+// scan_bwd.hip -- backward pass of the selective scan for gfx950.
+//
+// Gradients of a loss L through y = scan(u, delta, A, B, C, D, z, bias, h0)
+// given dy = dL/dy (and optionally dL/dlast_state), by recomputation: the
+// "Mamba" paper review ("Optimization") notes that the intermediate states
+// needed for backpropagation are cheaper to recompute from the inputs than
+// to store (B*L*D*N elements).  Here:
+//
+//  1. The forward kernel's checkpoint pass (scan_fwd.hip) stores the state
+//     entering every 16-step tile: 1/16 of the states, (batch, tile, N, dim).
+//  2. The adjoint lambda_t = dL/dh_t obeys its own linear recurrence
+//     backwards in time, lambda_t = ds_t C_t + Abar_{t+1} lambda_{t+1}
+//     (ds_t = dL/d(pre-gate output)), independent of h.  When the sequence
+//     is split into segments, bwd_agg_kernel runs each segment but the first
+//     from a zero carry; the carry entering segment s from the right is then
+//     the composition mu_s = exp(A SumDelta_{s+1}) mu_{s+1} + Q_{s+1} -- the
+//     associative affine step of the NN LAB "Mamba" page, run in reverse.
+//  3. bwd_kernel walks each segment's tiles from last to first: it
+//     recomputes the tile's 16 states from the checkpoint into registers,
+//     then sweeps the steps in reverse, carrying lambda per state and
+//     forming every gradient term.  dB and dC are sums over channels; they
+//     are reduced over the workgroup's 64 channels through LDS in groups of
+//     4 steps and written as per-channel-group partials.  dA, dD and the
+//     bias gradient are per-workgroup partials.
+//  4. Small kernels sum the partials in a fixed order, so results are
+//     deterministic.
+//
+// Per (element, state) the gradient terms are (Euler input term):
+//   lambda = ds C + carry;  carry' = Abar lambda
+//   dA    += lambda h_{t-1} Abar Delta
+//   dDelta += lambda (h_{t-1} Abar A + B u)
+//   du    += lambda Delta B;   dB += lambda Delta u;   dC += ds h_t
+// and per element du += ds D, dD += ds u, d(delta) = dDelta softplus'(x),
+// dz = dy (C.h + D u) silu'(z), ds = dy silu(z).
+#include "ssm_kernels.hpp"
+#include "ssm_math.hpp"
+
+namespace ssm {
+
+struct BwdSizes {
+  int batch, dim;
+  int64_t seqlen, seglen;
+  int nseg;
+  int ncg;
+  int softplus;
+  int vec;
+};
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+// Value q of a B, C record (scalar loads; see scan_fwd.hip for the layout).
+template <typename T>
+__device__ __forceinline__ float bwd_rec(const T* __restrict__ p, int q);
+template <>
+__device__ __forceinline__ float bwd_rec<float>(const float* __restrict__ p, int q) { return p[q]; }
+template <>
+__device__ __forceinline__ float bwd_rec<uint16_t>(const uint16_t* __restrict__ p, int q) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(p)[q >> 1];
+  return (q & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// E consecutive elements of one row starting at off: a vector load when the
+// run is whole and aligned, else element loads (zeros past `valid`).
+template <typename T, int E>
+__device__ __forceinline__ void load_run(const T* __restrict__ base, int64_t off, bool vec_ok, int valid,
+                                         float (&f)[E]) {
+  constexpr int W = E * (int)sizeof(T) / 4;
+  if (vec_ok) {
+    uint32_t w[W];
+    load_words<W>(base + off, w);
+    words_to_floats<T, E>(w, f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = e < valid ? Elem<T>::load(base + off + e) : 0.0f;
+  }
+}
+
+template <typename T, int E>
+__device__ __forceinline__ void store_run(T* __restrict__ base, int64_t off, bool vec_ok, int valid,
+                                          const float (&f)[E]) {
+  if (vec_ok) {
+    store_floats<T, E>(base + off, f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e < valid) Elem<T>::store(base + off + e, f[e]);
+  }
+}
+
+// ---- 2. reverse aggregates of segments 1 .. nseg-1 ------------------------------
+template <typename T, int NS, int G, int TL>
+__global__ __launch_bounds__(64 * G) void bwd_agg_kernel(
+    const T* __restrict__ delta, const float* __restrict__ A, const T* __restrict__ bc,
+    const T* __restrict__ z, const float* __restrict__ bias, const T* __restrict__ dy,
+    float* __restrict__ lagg, float* __restrict__ lsum, const BwdSizes p) {
+  constexpr int N = NS * G;
+  constexpr int E = TL / G;
+  constexpr int LDW = 65;
+  constexpr int R = 2 * NS;
+  __shared__ float2 s_v[TL][LDW];  // (Delta, ds)
+
+  const int nlaunch = p.nseg - 1;
+  const int seg = 1 + (int)(blockIdx.x % nlaunch);
+  const int rest = (int)(blockIdx.x / nlaunch);
+  const int cg = rest % p.ncg;
+  const int b = rest / p.ncg;
+  const int tid = threadIdx.x;
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int64_t L = p.seqlen;
+  const int d = cg * 64 + lane;
+  const bool dvalid = d < p.dim;
+  const int64_t row = (int64_t)b * p.dim + d;
+  const int64_t seg_begin = (int64_t)seg * p.seglen;
+  const int64_t seg_end = seg_begin + p.seglen < L ? seg_begin + p.seglen : L;
+
+  float A2[NS], carry[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    A2[k] = dvalid ? A[(int64_t)d * N + g * NS + k] * kLog2e : 0.0f;
+    carry[k] = 0.0f;
+  }
+  const int cc = tid / G;
+  const int r0 = (tid % G) * E;
+  const int dcc = cg * 64 + cc;
+  const bool ccvalid = dcc < p.dim;
+  const int64_t rowcc = (int64_t)b * p.dim + (ccvalid ? dcc : 0);
+  const float bias_cc = (bias != nullptr && ccvalid) ? bias[dcc] : 0.0f;
+  const T* bcw = bc + ((int64_t)b * G + g) * L * R;
+  double sumdt = 0.0;
+
+  for (int64_t t0 = ((seg_end - 1) / TL) * TL; t0 >= seg_begin; t0 -= TL) {
+    const int tvalid = (int)((seg_end - t0) < TL ? (seg_end - t0) : TL);
+    {
+      const int valid = ccvalid ? (tvalid - r0 < 0 ? 0 : (tvalid - r0 > E ? E : tvalid - r0)) : 0;
+      const bool vec_ok = p.vec && valid == E;
+      const int64_t off = rowcc * L + t0 + r0;
+      float dd[E], gg[E], zz[E];
+      load_run<T, E>(delta, off, vec_ok, valid, dd);
+      load_run<T, E>(dy, off, vec_ok, valid, gg);
+      if (z != nullptr) load_run<T, E>(z, off, vec_ok, valid, zz);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float x = dd[e] + bias_cc;
+        const float dt = p.softplus ? softplus_f32(x) : x;
+        const float ds = z != nullptr ? gg[e] * silu_f32(zz[e]) : gg[e];
+        s_v[r0 + e][cc] = make_float2(dt, e < valid ? ds : 0.0f);
+      }
+    }
+    __syncthreads();
+    const T* bct = bcw + t0 * R;
+    for (int t = tvalid - 1; t >= 0; --t) {
+      const float2 v = s_v[t][lane];
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const float lam = __builtin_fmaf(v.y, bwd_rec<T>(bct + t * R, NS + k), carry[k]);
+        carry[k] = exp2_hw(v.x * A2[k]) * lam;
+      }
+      if (g == 0) sumdt += (double)v.x;
+    }
+    __syncthreads();
+  }
+  if (!dvalid) return;
+  const int64_t plane = (int64_t)p.batch * p.dim;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) lagg[((int64_t)(seg - 1) * plane + row) * N + g * NS + k] = carry[k];
+  if (g == 0) lsum[(int64_t)(seg - 1) * plane + row] = (float)sumdt;
+}
+
+// ---- 3. the main backward sweep --------------------------------------------------
+template <typename T, int NS, int G, int TL>
+__global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
+    const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
+    const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
+    const float* __restrict__ bias, const T* __restrict__ dy, const float* __restrict__ dlast,
+    const float* __restrict__ ckpt, const float* __restrict__ lagg, const float* __restrict__ lsum,
+    T* __restrict__ du, T* __restrict__ ddelta, T* __restrict__ dz, float* __restrict__ dh0,
+    float* __restrict__ part_bc, float* __restrict__ part_a, float* __restrict__ part_d,
+    float* __restrict__ part_bias, const BwdSizes p) {
+  constexpr int N = NS * G;
+  constexpr int E = TL / G;                   // elements per thread, element role
+  constexpr int TR = 4;                       // steps per dB/dC reduction group
+  constexpr int LDW = 65;                     // padded row, float/float2/float4 arrays
+  constexpr int RW = 68;                      // padded row of the dB/dC terms (16-byte rows)
+  constexpr int R = 2 * NS;
+  constexpr int NRED = TR * 2 * N * RW;       // dB/dC terms of one group
+  constexpr int NY = G * TL * LDW;            // readout partials of one tile
+  static_assert(TL % TR == 0, "tile must split into reduction groups");
+
+  __shared__ float4 s_in[TL][LDW];            // (Delta, Delta*u, ds, u) per (step, channel)
+  __shared__ __align__(16) float s_buf[NRED > NY ? NRED : NY];  // readout partials, then dB/dC terms
+  __shared__ float2 s_p[G][TR][LDW];          // per wave and step: (sum lambda B, sum dDelta part)
+  float(*s_y)[TL][LDW] = reinterpret_cast<float(*)[TL][LDW]>(s_buf);
+  float(*s_red)[2][N][RW] = reinterpret_cast<float(*)[2][N][RW]>(s_buf);
+
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int seg = bid % p.nseg;
+  const int rest = bid / p.nseg;
+  const int cg = rest % p.ncg;
+  const int b = rest / p.ncg;
+
+  const int tid = threadIdx.x;
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int64_t L = p.seqlen;
+  const int d = cg * 64 + lane;
+  const bool dvalid = d < p.dim;
+  const int64_t row = (int64_t)b * p.dim + d;
+  const int64_t seg_begin = (int64_t)seg * p.seglen;
+  const int64_t seg_end = seg_begin + p.seglen < L ? seg_begin + p.seglen : L;
+  const int64_t ntiles = (L + TL - 1) / TL;
+  const int64_t plane = (int64_t)p.batch * p.dim;
+
+  // ---- recurrence role: parameters and the carry entering the segment's end --
+  float A2[NS], carry[NS], dA[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int n = g * NS + k;
+    A2[k] = dvalid ? A[(int64_t)d * N + n] * kLog2e : 0.0f;
+    carry[k] = (dvalid && dlast != nullptr) ? dlast[row * N + n] : 0.0f;
+    dA[k] = 0.0f;
+  }
+  if (dvalid) {
+    for (int j = p.nseg - 1; j > seg; --j) {
+      const float sdt = lsum[(int64_t)(j - 1) * plane + row];
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+        carry[k] = __builtin_fmaf(exp2_hw(sdt * A2[k]), carry[k],
+                                  lagg[((int64_t)(j - 1) * plane + row) * N + g * NS + k]);
+    }
+  }
+
+  // ---- element role: thread -> (channel cc, run of E steps) --------------------
+  const int cc = tid / G;
+  const int chunk = tid % G;
+  const int r0 = chunk * E;
+  const int dcc = cg * 64 + cc;
+  const bool ccvalid = dcc < p.dim;
+  const int64_t rowcc = (int64_t)b * p.dim + (ccvalid ? dcc : 0);
+  const float bias_cc = (bias != nullptr && ccvalid) ? bias[dcc] : 0.0f;
+  const float D_cc = (Dskip != nullptr && ccvalid) ? Dskip[dcc] : 0.0f;
+  const bool has_z = z != nullptr;
+  float accD = 0.0f, accBias = 0.0f;
+
+  // ---- reduction role (dB/dC): thread -> (output, part of the 64 lanes) --------
+  constexpr int NOUT = TR * 2 * N;
+  constexpr int TPO = (64 * G) / NOUT;        // threads per output
+  constexpr int LPT = 64 / TPO;               // lanes each of them sums
+  static_assert(TPO >= 1 && TPO * NOUT == 64 * G && LPT % 4 == 0, "reduction layout");
+  const int ro = tid / TPO;
+  const int rpart = tid % TPO;
+  const int ri = ro % TR;
+  const int rn = (ro / TR) % N;
+  const int rw = ro / (TR * N);
+
+  const T* bcw = bc + ((int64_t)b * G + g) * L * R;
+  float hist[TL][NS];
+
+  for (int64_t t0 = ((seg_end - 1) / TL) * TL; t0 >= seg_begin; t0 -= TL) {
+    const int tvalid = (int)((seg_end - t0) < TL ? (seg_end - t0) : TL);
+    const int valid = ccvalid ? (tvalid - r0 < 0 ? 0 : (tvalid - r0 > E ? E : tvalid - r0)) : 0;
+    const bool vec_ok = p.vec && valid == E;
+    const int64_t eoff = rowcc * L + t0 + r0;
+
+    // ---- stage: Delta, Delta*u, ds, u -------------------------------------------
+    float e_u[E], e_ds[E], e_sg[E], e_gz[E], e_dt[E];
+    {
+      float uu[E], dd[E], gg[E], zz[E];
+      load_run<T, E>(u, eoff, vec_ok, valid, uu);
+      load_run<T, E>(delta, eoff, vec_ok, valid, dd);
+      load_run<T, E>(dy, eoff, vec_ok, valid, gg);
+      if (has_z) load_run<T, E>(z, eoff, vec_ok, valid, zz);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float x = dd[e] + bias_cc;
+        const float dt = p.softplus ? softplus_f32(x) : x;
+        float ds = gg[e], gz = 0.0f;
+        if (has_z) {
+          const float sz = sigmoid_f32(zz[e]);
+          ds = gg[e] * (zz[e] * sz);
+          gz = gg[e] * sz * __builtin_fmaf(zz[e], 1.0f - sz, 1.0f);
+        }
+        if (e >= valid) ds = 0.0f;
+        e_u[e] = uu[e];
+        e_ds[e] = ds;
+        e_sg[e] = p.softplus ? sigmoid_f32(x) : 1.0f;
+        e_gz[e] = gz;
+        e_dt[e] = dt;
+        s_in[r0 + e][cc] = make_float4(dt, dt * uu[e], ds, uu[e]);
+      }
+    }
+    __syncthreads();
+
+    // ---- recompute the tile's states from its checkpoint ------------------------
+    const T* bct = bcw + t0 * R;
+    float hp0[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+      hp0[k] = dvalid ? ckpt[(((int64_t)b * ntiles + t0 / TL) * N + g * NS + k) * p.dim + d] : 0.0f;
+    {
+      float h[NS];
+#pragma unroll
+      for (int k = 0; k < NS; ++k) h[k] = hp0[k];
+#pragma unroll
+      for (int t = 0; t < TL; ++t) {
+        if (t < tvalid) {
+          const float4 v = s_in[t][lane];
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < NS; ++k) {
+            const float a = exp2_hw(v.x * A2[k]);
+            h[k] = __builtin_fmaf(a, h[k], v.y * bwd_rec<T>(bct + t * R, k));
+            hist[t][k] = h[k];
+            acc = __builtin_fmaf(bwd_rec<T>(bct + t * R, NS + k), h[k], acc);
+          }
+          s_y[g][t][lane] = acc;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- dz = dy (C.h + D u) silu'(z) ---------------------------------------------
+    if (has_z) {
+      float zo[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float s = 0.0f;
+        if (e < valid) {
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) s += s_y[gg][r0 + e][cc];
+        }
+        zo[e] = e_gz[e] * __builtin_fmaf(D_cc, e_u[e], s);
+      }
+      if (valid > 0) store_run<T, E>(dz, eoff, vec_ok, valid, zo);
+    }
+    __syncthreads();  // the readout partials share their memory with the dB/dC terms
+
+    // ---- reverse sweep, in groups of TR steps ------------------------------------
+    float e_du[E], e_dd[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) e_du[e] = e_dd[e] = 0.0f;
+#pragma unroll
+    for (int grp = TL / TR - 1; grp >= 0; --grp) {
+      if (grp * TR >= tvalid) continue;  // uniform: a ragged last tile
+#pragma unroll
+      for (int i = TR - 1; i >= 0; --i) {
+        const int t = grp * TR + i;
+        float lb = 0.0f, dd = 0.0f;
+        if (t < tvalid) {
+          const float4 v = s_in[t][lane];
+#pragma unroll
+          for (int k = 0; k < NS; ++k) {
+            const float a = exp2_hw(v.x * A2[k]);
+            const float lam = __builtin_fmaf(v.z, bwd_rec<T>(bct + t * R, NS + k), carry[k]);
+            const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hp0[k];
+            const float gh = lam * hp * a;
+            dA[k] = __builtin_fmaf(gh, v.x, dA[k]);
+            dd = __builtin_fmaf(gh, A2[k], dd);
+            lb = __builtin_fmaf(lam, bwd_rec<T>(bct + t * R, k), lb);
+            s_red[i][0][g * NS + k][lane] = lam * v.y;        // dB term
+            s_red[i][1][g * NS + k][lane] = v.z * hist[t][k];  // dC term
+            carry[k] = a * lam;
+          }
+        }
+        s_p[g][i][lane] = make_float2(lb, dd * kLn2);
+      }
+      __syncthreads();
+
+      // dB, dC of this group's steps: the sum over the 64 channels
+      {
+        const float* src = &s_red[ri][rw][rn][rpart * LPT];
+        float sacc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < LPT; q += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(src + q);
+          sacc += (v4.x + v4.y) + (v4.z + v4.w);
+        }
+#pragma unroll
+        for (int off = 1; off < TPO; off <<= 1) sacc += __shfl_xor(sacc, off);
+        const int t = grp * TR + ri;
+        if (rpart == 0 && t < tvalid)
+          part_bc[((((int64_t)b * p.ncg + cg) * 2 + rw) * N + rn) * L + t0 + t] = sacc;
+      }
+      // du and d(delta) of this group's steps, for this thread's elements
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int t = r0 + e;
+        if (t / TR == grp && e < valid) {
+          float slb = 0.0f, sdd = 0.0f;
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) {
+            const float2 q = s_p[gg][t - grp * TR][cc];
+            slb += q.x;
+            sdd += q.y;
+          }
+          e_du[e] = __builtin_fmaf(e_ds[e], D_cc, e_dt[e] * slb);
+          const float ddx = __builtin_fmaf(e_u[e], slb, sdd) * e_sg[e];
+          e_dd[e] = ddx;
+          accD = __builtin_fmaf(e_ds[e], e_u[e], accD);
+          accBias += ddx;
+        }
+      }
+      __syncthreads();
+    }
+    if (valid > 0) {
+      store_run<T, E>(du, eoff, vec_ok, valid, e_du);
+      store_run<T, E>(ddelta, eoff, vec_ok, valid, e_dd);
+    }
+  }
+
+  // ---- per-workgroup results ------------------------------------------------------
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) {
+    accD += __shfl_xor(accD, off);
+    accBias += __shfl_xor(accBias, off);
+  }
+  if (chunk == 0 && ccvalid) {
+    part_d[((int64_t)b * p.nseg + seg) * p.dim + dcc] = accD;
+    part_bias[((int64_t)b * p.nseg + seg) * p.dim + dcc] = accBias;
+  }
+  if (!dvalid) return;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    part_a[(((int64_t)b * p.nseg + seg) * p.dim + d) * N + g * NS + k] = dA[k];
+    if (seg == 0 && dh0 != nullptr) dh0[row * N + g * NS + k] = carry[k];
+  }
+}
+
+// ---- 4. fixed-order sums of the partials ------------------------------------------
+// dB, dC: out[w][(b*N + n)*L + t] = sum over channel groups.
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_bc_kernel(const float* __restrict__ part, T* __restrict__ dB,
+                                                        T* __restrict__ dC, int batch, int ncg, int N,
+                                                        int64_t L) {
+  const int64_t per = (int64_t)N * L;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * batch * per) return;
+  const int w = (int)(i / (batch * per));
+  const int64_t j = i % (batch * per);
+  const int b = (int)(j / per);
+  const int64_t nt = j % per;
+  const float* src = part + (((int64_t)b * ncg) * 2 + w) * per + nt;
+  float s = 0.0f;
+  for (int c = 0; c < ncg; ++c) s += src[(int64_t)c * 2 * per];
+  Elem<T>::store((w == 0 ? dB : dC) + j, s);
+}
+
+// out[i] = sum_j src[j * n + i], j < terms (dA, dD, d(bias) over batch rows and segments).
+__global__ __launch_bounds__(256) void reduce_terms_kernel(const float* __restrict__ src, float* __restrict__ out,
+                                                           int64_t n, int terms) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int j = 0; j < terms; ++j) s += src[(int64_t)j * n + i];
+  out[i] = s;
+}
+
+template <typename T, int NS, int G>
+static hipError_t launch_bwd_typed(const BwdLaunch& a, hipStream_t stream) {
+  constexpr int TL = kScanTile;
+  BwdSizes s;
+  s.batch = a.batch;
+  s.dim = a.dim;
+  s.seqlen = a.seqlen;
+  s.seglen = a.seglen;
+  s.nseg = a.nseg;
+  s.ncg = (a.dim + 63) / 64;
+  s.softplus = a.softplus;
+  s.vec = a.vec;
+  const T* u = static_cast<const T*>(a.u);
+  const T* dl = static_cast<const T*>(a.delta);
+  const T* z = static_cast<const T*>(a.z);
+  const T* gy = static_cast<const T*>(a.dy);
+  const T* bc = static_cast<const T*>(a.ws_bc);
+  const int64_t base = (int64_t)a.batch * s.ncg;
+  if (a.nseg > 1) {
+    bwd_agg_kernel<T, NS, G, TL><<<(unsigned)(base * (a.nseg - 1)), 64 * G, 0, stream>>>(
+        dl, a.A, bc, z, a.bias, gy, a.ws_lagg, a.ws_lsum, s);
+  }
+  bwd_kernel<T, NS, G, TL><<<(unsigned)(base * a.nseg), 64 * G, 0, stream>>>(
+      u, dl, a.A, bc, a.Dskip, z, a.bias, gy, a.dlast, a.ws_ckpt, a.ws_lagg, a.ws_lsum,
+      static_cast<T*>(a.du), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), a.dh0, a.ws_part_bc,
+      a.ws_part_a, a.ws_part_d, a.ws_part_bias, s);
+  const int N = NS * G;
+  const int64_t nbc = 2 * (int64_t)a.batch * N * a.seqlen;
+  reduce_bc_kernel<T><<<(unsigned)((nbc + 255) / 256), 256, 0, stream>>>(
+      a.ws_part_bc, static_cast<T*>(a.dB), static_cast<T*>(a.dC), a.batch, s.ncg, N, a.seqlen);
+  const int terms = a.batch * a.nseg;
+  const int64_t na = (int64_t)a.dim * N;
+  reduce_terms_kernel<<<(unsigned)((na + 255) / 256), 256, 0, stream>>>(a.ws_part_a, a.dA, na, terms);
+  if (a.dD != nullptr)
+    reduce_terms_kernel<<<(unsigned)((a.dim + 255) / 256), 256, 0, stream>>>(a.ws_part_d, a.dD, a.dim,
+                                                                            terms);
+  if (a.dbias != nullptr)
+    reduce_terms_kernel<<<(unsigned)((a.dim + 255) / 256), 256, 0, stream>>>(a.ws_part_bias, a.dbias,
+                                                                            a.dim, terms);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_bwd_state(const BwdLaunch& a, hipStream_t stream) {
+  switch (a.dstate) {
+    case 1: return launch_bwd_typed<T, 1, 1>(a, stream);
+    case 2: return launch_bwd_typed<T, 2, 1>(a, stream);
+    case 4: return launch_bwd_typed<T, 4, 1>(a, stream);
+    case 8: return launch_bwd_typed<T, 4, 2>(a, stream);
+    case 16: return launch_bwd_typed<T, 4, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_bwd(const BwdLaunch& a, hipStream_t stream) {
+  if (a.batch == 0 || a.dim == 0 || a.seqlen == 0) return hipSuccess;
+  return a.dtype == Dtype::BF16 ? launch_bwd_state<uint16_t>(a, stream)
+                                : launch_bwd_state<float>(a, stream);
+}
+
+}  // namespace ssm

@@ -150,13 +150,20 @@ constexpr int load_block_tiles() {
   return kt < 1 ? 1 : (kt > 4 ? 4 : kt);
 }
 
-template <typename T, int NS, int G, int TL, bool AGG, int MODE>
+// PASS: kPassMain computes y (and last_state); kPassAgg runs every segment
+// but the last from a zero state and records its end state and Delta sum;
+// kPassCkpt runs like the main pass but, instead of y, records the state
+// entering every tile (the checkpoints the backward pass starts from).
+template <typename T, int NS, int G, int TL, int PASS, int MODE>
 __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
     const float* __restrict__ bias, const float* __restrict__ h0, T* __restrict__ y,
     float* __restrict__ last_state, float* __restrict__ ws_hend, float* __restrict__ ws_sumdt,
-    const ScanSizes p, const ConvArgs cv) {
+    float* __restrict__ ws_ckpt, const ScanSizes p, const ConvArgs cv) {
+  constexpr bool AGG = PASS == kPassAgg;
+  constexpr bool READOUT = PASS == kPassMain;
+  constexpr bool CKPT = PASS == kPassCkpt;
   constexpr bool ZOH = (MODE & kModeZoh) != 0;
   constexpr bool CONV = (MODE & kModeConv) != 0;
   constexpr int N = NS * G;
@@ -171,7 +178,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   static_assert(!CONV || E >= kMaxConvWidth - 1, "a run must hold the convolution's history");
 
   __shared__ float2 s_ddu[TL][LDW];                           // (Delta, Delta*u), ZOH: (Delta, u)
-  __shared__ float s_y[AGG ? 1 : G][AGG ? 1 : TL][LDW];       // partial readouts
+  __shared__ float s_y[READOUT ? G : 1][READOUT ? TL : 1][LDW];  // partial readouts
 
   // ---- block -> (batch row, channel group, segment) --------------------------
   // Consecutive block ids go to different XCDs; regroup so that the blocks an
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   const int64_t rowcc = (int64_t)b * p.dim + (ccvalid ? dcc : 0);
   const float bias_cc = (bias != nullptr && ccvalid) ? bias[dcc] : 0.0f;
   const float D_cc = (Dskip != nullptr && ccvalid) ? Dskip[dcc] : 0.0f;
-  const bool has_z = !AGG && (z != nullptr);
+  const bool has_z = READOUT && (z != nullptr);
   const bool vec = p.vec != 0;
 
   // convolution taps of channel cc, right-aligned in 4 (tap 3 on the current
@@ -352,6 +359,16 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
         if (ccvalid && tn < seg_end && block_full(tn)) fetch_block(tn);
       }
 
+      // ---- checkpoint: the state entering this tile, (batch, tile, N, dim) ----
+      if constexpr (CKPT) {
+        if (dvalid) {
+          const int64_t ntiles = (L + TL - 1) / TL;
+          float* cp = ws_ckpt + (((int64_t)b * ntiles + t0 / TL) * N + g * NS) * p.dim + d;
+#pragma unroll
+          for (int k = 0; k < NS; ++k) cp[(int64_t)k * p.dim] = h[k];
+        }
+      }
+
       // ---- the recurrence: TL steps x NS states per lane ---------------------
       const T* bct = bcw + t0 * R;
       if (tvalid == TL) {
@@ -385,9 +402,9 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
               h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, vc[i].x, vc[i].y * rc[i][k], rA[k]));
               acc = __builtin_fmaf(rc[i][NS + k], h[k], acc);
             }
-            if constexpr (!AGG) {
+            if constexpr (READOUT) {
               s_y[g][c * CH + i][lane] = acc;
-            } else {
+            } else if constexpr (AGG) {
               if (g == 0) sumdt += (double)vc[i].x;
             }
           }
@@ -411,9 +428,9 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
             h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, v.x, v.y * rec_value<T>(bct + t * R, k), rA[k]));
             acc = __builtin_fmaf(rec_value<T>(bct + t * R, NS + k), h[k], acc);
           }
-          if constexpr (!AGG) {
+          if constexpr (READOUT) {
             s_y[g][t][lane] = acc;
-          } else {
+          } else if constexpr (AGG) {
             if (g == 0) sumdt += (double)v.x;
           }
         }
@@ -421,7 +438,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
       __syncthreads();
 
       // ---- readout: sum the G partials, D-skip, gate, store y ------------------
-      if constexpr (!AGG) {
+      if constexpr (READOUT) {
         float yv[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -459,7 +476,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 #pragma unroll
     for (int k = 0; k < NS; ++k) ws_hend[(seg * plane + row) * N + g * NS + k] = h[k];
     if (g == 0) ws_sumdt[seg * plane + row] = (float)sumdt;
-  } else {
+  } else if constexpr (READOUT) {
     if (last_state != nullptr && seg == p.nseg - 1) {
 #pragma unroll
       for (int k = 0; k < NS; ++k) last_state[row * N + g * NS + k] = h[k];
@@ -505,13 +522,23 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   if (a.nseg > 1) {
     s.nseg_launch = a.nseg - 1;
     const unsigned grid = (unsigned)(base * s.nseg_launch);
-    scan_kernel<T, NS, G, TL, true, MODE><<<grid, 64 * G, 0, stream>>>(
-        u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s, cv);
+    scan_kernel<T, NS, G, TL, kPassAgg, MODE><<<grid, 64 * G, 0, stream>>>(
+        u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, nullptr,
+        s, cv);
   }
   s.nseg_launch = a.nseg;
   const unsigned grid = (unsigned)(base * s.nseg_launch);
-  scan_kernel<T, NS, G, TL, false, MODE><<<grid, 64 * G, 0, stream>>>(
-      u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, s, cv);
+  if constexpr (MODE == 0) {  // the backward pass exists for the plain variant only
+    if (a.ws_ckpt != nullptr) {
+      scan_kernel<T, NS, G, TL, kPassCkpt, MODE><<<grid, 64 * G, 0, stream>>>(
+          u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt,
+          a.ws_ckpt, s, cv);
+      return hipGetLastError();
+    }
+  }
+  scan_kernel<T, NS, G, TL, kPassMain, MODE><<<grid, 64 * G, 0, stream>>>(
+      u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, nullptr,
+      s, cv);
   return hipGetLastError();
 }
 
@@ -541,6 +568,7 @@ static hipError_t launch_by_mode(const ScanLaunch& a, hipStream_t stream) {
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream) {
   if (a.batch == 0 || a.dim == 0 || a.seqlen == 0) return hipSuccess;
   if (a.conv_w != nullptr && (a.conv_k < 1 || a.conv_k > kMaxConvWidth)) return hipErrorInvalidValue;
+  if (a.ws_ckpt != nullptr && (a.zoh || a.conv_w != nullptr)) return hipErrorInvalidValue;
   return a.dtype == Dtype::BF16 ? launch_by_mode<uint16_t>(a, stream) : launch_by_mode<float>(a, stream);
 }
 

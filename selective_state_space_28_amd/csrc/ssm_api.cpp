@@ -114,6 +114,39 @@ WsLayout workspace_layout(int batch, int dim, int dstate, int64_t L, int dtype, 
   return w;
 }
 
+// Backward workspace: the forward layout first (records, segment aggregates),
+// then the tile checkpoints, the reverse aggregates and the partial sums.
+struct BwdWsLayout {
+  WsLayout fwd;
+  size_t ckpt, lagg, lsum, part_bc, part_a, part_d, part_bias, total;
+};
+
+BwdWsLayout bwd_workspace_layout(int batch, int dim, int dstate, int64_t L, int dtype, const SegPlan& sp) {
+  BwdWsLayout w{};
+  w.fwd = workspace_layout(batch, dim, dstate, L, dtype, sp);
+  const size_t plane = (size_t)batch * (size_t)dim;
+  const size_t ntiles = (size_t)((L + ssm::kScanTile - 1) / ssm::kScanTile);
+  const size_t ncg = (size_t)((dim + 63) / 64);
+  const size_t segs = (size_t)sp.nseg;
+  size_t off = round256(w.fwd.total);
+  w.ckpt = off;
+  off += round256((size_t)batch * ntiles * (size_t)dstate * (size_t)dim * sizeof(float));
+  w.lagg = off;
+  off += round256((segs - 1) * plane * (size_t)dstate * sizeof(float));
+  w.lsum = off;
+  off += round256((segs - 1) * plane * sizeof(float));
+  w.part_bc = off;
+  off += round256((size_t)batch * ncg * 2 * (size_t)dstate * (size_t)L * sizeof(float));
+  w.part_a = off;
+  off += round256((size_t)batch * segs * (size_t)dim * (size_t)dstate * sizeof(float));
+  w.part_d = off;
+  off += round256((size_t)batch * segs * (size_t)dim * sizeof(float));
+  w.part_bias = off;
+  off += round256((size_t)batch * segs * (size_t)dim * sizeof(float));
+  w.total = off;
+  return w;
+}
+
 bool aligned(const void* p, size_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool shapes_fit(int batch, int dim, int64_t seqlen) {
@@ -336,6 +369,138 @@ int ssm_conv_state_update(float* conv_state, float* state, const void* x, const 
   const ConvIn cv{conv_w, conv_b, nullptr, nullptr, conv_state, conv_width};
   return update_impl(state, x, delta, A, B, C, D_skip, z, delta_bias, flags, y, batch, dim, dstate,
                      dtype, stream, &cv);
+}
+
+size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int dstate, int64_t seqlen, int dtype) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
+  if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return 0;
+  if (batch == 0 || dim == 0 || seqlen == 0) return 0;
+  return bwd_workspace_layout(batch, dim, dstate, seqlen, dtype,
+                              plan_segments(batch, dim, dstate, seqlen))
+      .total;
+}
+
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D_skip, const void* z, const float* delta_bias, int flags,
+                 const float* h0, const void* dy, const float* dlast_state, void* du, void* ddelta,
+                 float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                 float* dh0, int batch, int dim, int dstate, int64_t seqlen, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if ((flags & ~SSM_DELTA_SOFTPLUS) != 0) return SSM_ERR_FLAGS;  // Euler input term only
+  if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return SSM_ERR_SHAPE;
+  const bool empty = batch == 0 || dim == 0;
+  if (!empty && (!A || !dA)) return SSM_ERR_NULL;
+  if (!empty && seqlen > 0 &&
+      (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC || (z != nullptr && !dz)))
+    return SSM_ERR_NULL;
+  const size_t es = (size_t)elem_bytes(dtype);
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
+      !aligned(z, es) || !aligned(dy, es) || !aligned(du, es) || !aligned(ddelta, es) ||
+      !aligned(dB, es) || !aligned(dC, es) || !aligned(dz, es) || !aligned(A, 4) ||
+      !aligned(D_skip, 4) || !aligned(delta_bias, 4) || !aligned(h0, 4) || !aligned(dlast_state, 4) ||
+      !aligned(dA, 4) || !aligned(dD, 4) || !aligned(ddelta_bias, 4) || !aligned(dh0, 4) ||
+      !aligned(workspace, 256))
+    return SSM_ERR_ALIGN;
+  {
+    const void* ins[] = {u, delta, B, C, z, dy};
+    const void* outs[] = {du, ddelta, dB, dC, dz};
+    for (const void* o : outs) {
+      if (o == nullptr) continue;
+      for (const void* i : ins)
+        if (o == i) return SSM_ERR_ALIAS;
+    }
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (empty) return SSM_OK;
+
+  if (seqlen == 0) {  // no steps: zero parameter gradients, dh0 = dlast
+    hipError_t e = ssm::launch_fill_state(dA, nullptr, (int64_t)dim * dstate, st);
+    if (e == hipSuccess && dD != nullptr) e = ssm::launch_fill_state(dD, nullptr, dim, st);
+    if (e == hipSuccess && ddelta_bias != nullptr)
+      e = ssm::launch_fill_state(ddelta_bias, nullptr, dim, st);
+    if (e == hipSuccess && dh0 != nullptr)
+      e = ssm::launch_fill_state(dh0, dlast_state, (int64_t)batch * dim * dstate, st);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+
+  const SegPlan sp = plan_segments(batch, dim, dstate, seqlen);
+  const int64_t blocks = (int64_t)batch * ((dim + 63) / 64) * sp.nseg;
+  const int64_t pack_blocks = (int64_t)batch * ((seqlen + 255) / 256);
+  const int64_t red_blocks = (2 * (int64_t)batch * dstate * seqlen + 255) / 256;
+  if (blocks > INT_MAX || pack_blocks > INT_MAX || red_blocks > INT_MAX) return SSM_ERR_SHAPE;
+  const BwdWsLayout wl = bwd_workspace_layout(batch, dim, dstate, seqlen, dtype, sp);
+  if (workspace == nullptr || workspace_bytes < wl.total) return SSM_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const bool rows16 = ((int64_t)es * seqlen) % 16 == 0;
+
+  // 1. forward checkpoint pass (packs the B, C records too)
+  ssm::ScanLaunch f{};
+  f.u = u;
+  f.delta = delta;
+  f.A = A;
+  f.B = B;
+  f.C = C;
+  f.Dskip = D_skip;
+  f.bias = delta_bias;
+  f.h0 = h0;
+  f.ws_bc = ws + wl.fwd.bc;
+  if (sp.nseg > 1) {
+    f.ws_hend = reinterpret_cast<float*>(ws + wl.fwd.hend);
+    f.ws_sumdt = reinterpret_cast<float*>(ws + wl.fwd.sumdt);
+  }
+  f.batch = batch;
+  f.dim = dim;
+  f.dstate = dstate;
+  f.seqlen = seqlen;
+  f.seglen = sp.seglen;
+  f.nseg = sp.nseg;
+  f.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  f.vec = rows16 && aligned(u, 16) && aligned(delta, 16);
+  f.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
+  f.ncu = device_cu_count();
+  f.prio_epochs = prio_epochs();
+  f.ws_ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
+  if (ssm::launch_scan_fwd(f, st) != hipSuccess) return SSM_ERR_HIP;
+
+  // 2-4. reverse aggregates, the backward sweep, the sums of the partials
+  ssm::BwdLaunch a{};
+  a.u = u;
+  a.delta = delta;
+  a.A = A;
+  a.Dskip = D_skip;
+  a.z = z;
+  a.bias = delta_bias;
+  a.dy = dy;
+  a.dlast = dlast_state;
+  a.du = du;
+  a.ddelta = ddelta;
+  a.dz = dz;
+  a.dh0 = dh0;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = dD;
+  a.dbias = ddelta_bias;
+  a.ws_bc = ws + wl.fwd.bc;
+  a.ws_ckpt = reinterpret_cast<const float*>(ws + wl.ckpt);
+  a.ws_lagg = reinterpret_cast<float*>(ws + wl.lagg);
+  a.ws_lsum = reinterpret_cast<float*>(ws + wl.lsum);
+  a.ws_part_bc = reinterpret_cast<float*>(ws + wl.part_bc);
+  a.ws_part_a = reinterpret_cast<float*>(ws + wl.part_a);
+  a.ws_part_d = reinterpret_cast<float*>(ws + wl.part_d);
+  a.ws_part_bias = reinterpret_cast<float*>(ws + wl.part_bias);
+  a.batch = batch;
+  a.dim = dim;
+  a.dstate = dstate;
+  a.seqlen = seqlen;
+  a.seglen = sp.seglen;
+  a.nseg = sp.nseg;
+  a.softplus = f.softplus;
+  a.vec = rows16 && aligned(u, 16) && aligned(delta, 16) && aligned(z, 16) && aligned(dy, 16) &&
+          aligned(du, 16) && aligned(ddelta, 16) && aligned(dz, 16);
+  a.dtype = f.dtype;
+  return ssm::launch_scan_bwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 const char* ssm_status_string(int status) {

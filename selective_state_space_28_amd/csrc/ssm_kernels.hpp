@@ -13,6 +13,11 @@ constexpr int kScanTile = 16;
 // Storage type of the per-token tensors.
 enum class Dtype { F32 = 0, BF16 = 1 };
 
+// Passes of the forward scan kernel (its PASS template argument).
+constexpr int kPassMain = 0;  // y and last_state
+constexpr int kPassAgg = 1;   // segment aggregates (end state from zero, Delta sum)
+constexpr int kPassCkpt = 2;  // the state entering every tile, for the backward pass
+
 // Kernel variants (bits of the MODE template argument).
 constexpr int kModeZoh = 1;   // zero-order-hold input term (else Euler)
 constexpr int kModeConv = 2;  // causal depthwise conv1d + silu applied to the input first
@@ -47,6 +52,8 @@ struct ScanLaunch {
   const float* conv_state_in;   // (batch, dim, conv_k-1) nullable
   float* conv_state_out;        // (batch, dim, conv_k-1) nullable
   int conv_k;                   // 1..4
+  // checkpoint pass instead of the main pass (backward): (batch, ntiles, N, dim)
+  float* ws_ckpt;
   Dtype dtype;
 };
 
@@ -76,7 +83,45 @@ struct DecodeLaunch {
 // Widest convolution the kernels take.
 constexpr int kMaxConvWidth = 4;
 
+// Backward pass (Euler input term, no convolution prologue).  The caller has
+// already run the forward checkpoint pass (launch_scan_fwd with ws_ckpt),
+// which also packs the B, C records into ws_bc.
+struct BwdLaunch {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const float* Dskip;     // nullable
+  const void* z;          // nullable
+  const float* bias;      // nullable
+  const void* dy;
+  const float* dlast;     // nullable
+  void* du;
+  void* ddelta;
+  void* dz;               // required when z is given
+  float* dh0;             // nullable
+  float* dA;
+  void* dB;
+  void* dC;
+  float* dD;              // nullable
+  float* dbias;           // nullable
+  const void* ws_bc;      // records from the checkpoint pass
+  const float* ws_ckpt;   // (batch, ntiles, dstate, dim)
+  float* ws_lagg;         // (nseg-1, batch, dim, dstate) when nseg > 1
+  float* ws_lsum;         // (nseg-1, batch, dim) when nseg > 1
+  float* ws_part_bc;      // (batch, ncg, 2, dstate, seqlen)
+  float* ws_part_a;       // (batch, nseg, dim, dstate)
+  float* ws_part_d;       // (batch, nseg, dim)
+  float* ws_part_bias;    // (batch, nseg, dim)
+  int batch, dim, dstate;
+  int64_t seqlen, seglen;
+  int nseg;
+  int softplus;
+  int vec;
+  Dtype dtype;
+};
+
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream);
+hipError_t launch_scan_bwd(const BwdLaunch& a, hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
 // last_state = h0 (or zeros when h0 is null) for an empty sequence.
 hipError_t launch_fill_state(float* dst, const float* src, int64_t n, hipStream_t stream);

@@ -189,3 +189,58 @@ def ssm_conv_state_update(conv_state, state, x, conv_w, conv_b, delta, A, B, C, 
     (batch, dim, K-1) and state (batch, dim, N) are updated in place."""
     return _update(state, x, delta, A, B, C, D, z, delta_bias, delta_softplus, bbar, out,
                    (conv_state, conv_w, conv_b))
+
+
+def ssm_scan_bwd_workspace_bytes(batch: int, dim: int, dstate: int, seqlen: int,
+                                 dtype: torch.dtype) -> int:
+    return int(load().ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, _DTYPES[dtype]))
+
+
+def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 h0=None, *, dy, dlast_state=None, workspace=None):
+    """Gradients through ssm_scan_fwd (Euler input term) given dy = dL/dy
+    and optionally dL/dlast_state; the states are recomputed, not stored.
+    Returns a dict: du, ddelta, dz (None without z) and dB, dC in the input
+    dtype; dA, dD, ddelta_bias, dh0 in float32."""
+    lib = load()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("libssm runs on the GPU: tensors must be on a cuda device")
+    dt = u.dtype
+    code = _code(u)
+    batch, dim, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    _check("u", u, (batch, dim, L), dt, dev)
+    _check("delta", delta, (batch, dim, L), dt, dev)
+    _check("A", A, (dim, N), torch.float32, dev)
+    _check("B", B, (batch, N, L), dt, dev)
+    _check("C", C, (batch, N, L), dt, dev)
+    _check("D", D, (dim,), torch.float32, dev, required=False)
+    _check("z", z, (batch, dim, L), dt, dev, required=False)
+    _check("delta_bias", delta_bias, (dim,), torch.float32, dev, required=False)
+    _check("h0", h0, (batch, dim, N), torch.float32, dev, required=False)
+    _check("dy", dy, (batch, dim, L), dt, dev)
+    _check("dlast_state", dlast_state, (batch, dim, N), torch.float32, dev, required=False)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u), dA=torch.empty((dim, N), **f32),
+             dB=torch.empty_like(B), dC=torch.empty_like(C), dD=torch.empty(dim, **f32),
+             dz=torch.empty_like(u) if z is not None else None,
+             ddelta_bias=torch.empty(dim, **f32), dh0=torch.empty((batch, dim, N), **f32))
+    need = int(lib.ssm_scan_bwd_workspace_bytes(batch, dim, N, L, code))
+    ws_bytes = 0
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(delta_bias), _flags(delta_softplus, "euler"), _ptr(h0), _ptr(dy),
+                          _ptr(dlast_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                          _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                          _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, dim, N, L, code,
+                          _ptr(workspace), ws_bytes, stream)
+    if rc != 0:
+        raise SsmError(rc, "ssm_scan_bwd")
+    return g

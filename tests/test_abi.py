@@ -14,7 +14,8 @@ P = 0x10000  # a 256-byte aligned fake device address, never dereferenced
 def test_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) == {"ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
-                          "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_status_string"}
+                          "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_scan_bwd_workspace_bytes",
+                          "ssm_scan_bwd", "ssm_status_string"}
     lib = ctypes.CDLL(load()._name)
     for n in names:
         assert hasattr(lib, n), n
@@ -166,3 +167,40 @@ def test_conv_update_validation(kw, code):
 def test_conv_update_width_one_needs_no_state():
     # K = 1: no carried inputs; an empty problem returns before any launch
     assert _cupd(cs=None, K=1, batch=0) == OK
+
+
+def _bwd(**kw):
+    a = dict(u=P, delta=P + 0x10000, A=P + 0x20000, B=P + 0x30000, C=P + 0x40000, D=None, z=None,
+             bias=None, fl=1, h0=None, dy=P + 0x50000, dlast=None, du=P + 0x60000, dd=P + 0x70000,
+             dA=P + 0x80000, dB=P + 0x90000, dC=P + 0xA0000, dD=None, dz=None, dbias=None, dh0=None,
+             batch=1, dim=64, dstate=16, L=2048, dtype=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return load().ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                               a["fl"], a["h0"], a["dy"], a["dlast"], a["du"], a["dd"], a["dA"],
+                               a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"], a["dh0"], a["batch"],
+                               a["dim"], a["dstate"], a["L"], a["dtype"], a["ws"], a["wsb"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fl=2), FLAGS), (dict(fl=3), FLAGS), (dict(fl=4), FLAGS), (dict(dtype=7), DTYPE),
+    (dict(dstate=12), SHAPE), (dict(L=-3), SHAPE),
+    (dict(dy=None), NULL), (dict(du=None), NULL), (dict(dA=None), NULL), (dict(dB=None), NULL),
+    (dict(z=P + 0xB0000), NULL),
+    (dict(du=P + 1), ALIGN), (dict(dA=P + 2), ALIGN), (dict(dlast=P + 1), ALIGN),
+    (dict(du=P), ALIAS), (dict(dB=P + 0x30000), ALIAS), (dict(ddelta=None, dd=P + 0x50000), ALIAS),
+])
+def test_bwd_validation(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_workspace_query_and_check():
+    lib = load()
+    need = lib.ssm_scan_bwd_workspace_bytes(1, 64, 16, 2048, 1)
+    fwd = lib.ssm_scan_fwd_workspace_bytes(1, 64, 16, 2048, 1)
+    # forward workspace + tile checkpoints + dB/dC partials at least
+    assert need >= fwd + 128 * 16 * 64 * 4 + 2 * 16 * 2048 * 4
+    assert lib.ssm_scan_bwd_workspace_bytes(0, 64, 16, 2048, 1) == 0
+    assert _bwd(ws=None, wsb=0) == WS
+    assert _bwd(ws=P, wsb=need - 1) == WS
+    assert _bwd(batch=0) == OK
