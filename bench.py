@@ -46,6 +46,12 @@ OPS_EXECUTED_PER_ELEMENT_STATE_ZOH = 13
 # reciprocal, multiply), at the width the benchmark uses.
 CONV_WIDTH = 4
 OPS_PER_ELEMENT_CONV = CONV_WIDTH + 4
+# Backward by recomputation, per (element, state): the forward recurrence
+# and readout again (Delta*A, exp2, Delta*u*B, state FMA, C*h FMA), then the
+# reverse step (lambda FMA, lambda*h*Abar: 2, dA FMA, dDelta FMA, lambda*B
+# FMA, dB and dC terms, the carry Abar*lambda) and one add each for the
+# channel sums of dB and dC.
+OPS_PER_ELEMENT_STATE_BWD = 16
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_kernel_c3_traffic.json")
 KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, false, 0>"
 KERNEL_SOURCES = ["selective_state_space_28_amd/csrc/scan_fwd.hip",
@@ -259,6 +265,38 @@ def main():
                                 "frac": round(tops_c / VALU_PEAK_TOPS, 4),
                                 "kernel": KERNEL_NAME.replace("false, 0>", "false, 2>"),
                                 "ops_per_launch": ops_c}}
+
+    # the backward pass of the same workload (dy ~ N(0, 1), bf16)
+    gy = torch.randn(u.shape, generator=torch.Generator(device=dev).manual_seed(5), device=dev,
+                     dtype=torch.float32).to(u.dtype)
+    bws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen,
+                                                       u.dtype), dtype=torch.uint8, device=dev)
+
+    def step_bwd():
+        ssm.ssm_scan_bwd(u, delta, A, B, C, D, z, bias, dy=gy, workspace=bws)
+
+    for _ in range(max(1, args.warmup // 2)):
+        step_bwd()
+    torch.cuda.synchronize(dev)
+    nb = max(1, args.steps // 5)
+    for s, e in ev[:nb]:
+        s.record(stream)
+        step_bwd()
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_b = float(np.mean([s.elapsed_time(e) for s, e in ev[:nb]]))
+    ops_b = elements * cfg.dstate * OPS_PER_ELEMENT_STATE_BWD
+    tops_b = ops_b / (ms_b * 1e-3) / 1e12
+    out["bwd"] = {"workload": "ssm_scan_bwd of the same scan (all gradients, states recomputed)",
+                  "steps": nb, "ms_per_step": ms_b, "value": elements / (ms_b * 1e-3),
+                  "unit": "elements/s",
+                  "roofline": {"bound": "alu", "achieved": round(tops_b, 3),
+                               "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
+                               "frac": round(tops_b / VALU_PEAK_TOPS, 4),
+                               "kernel": "ssm::bwd_kernel<unsigned short, 4, 4, 16> (+ checkpoint "
+                                         "pass and sums)",
+                               "ops_per_launch": ops_b}}
+    del gy, bws
     del u, delta, B, C, z, y, ws
 
     if not args.no_decode:
