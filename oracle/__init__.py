@@ -19,6 +19,9 @@ convolution with the taps reversed, its identity and delay special cases,
 and its own chunking and decode identities; its tap order, width and
 non-linearity are readings of the pages, not printed on them.  The backward
 (scan_bwd) is pinned by central finite differences of the forward, in fp64.
+ssd_scan_fwd is the scan with a scalar A per head ("Mamba" paper review,
+"Mamba 2"; NN LAB "Mamba" page, "Bridging Tensor Cores and Recurrence"),
+pinned against an independent chunked evaluation and linear attention.
 """
 from .oracle import (build, causal_conv1d_silu, conv_scan_fwd, conv_step,  # noqa: F401
-                     lib_path, scan_bwd, scan_fwd, state_update)
+                     lib_path, scan_bwd, scan_fwd, ssd_scan_fwd, state_update)

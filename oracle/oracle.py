@@ -194,3 +194,25 @@ def conv_scan_fwd(x, conv_w, conv_b, conv_state_in, delta, A, B, C, D=None, z=No
     u, cst = causal_conv1d_silu(x, conv_w, conv_b, conv_state_in)
     y, last = scan_fwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, nthreads, bbar)
     return y, last, cst
+
+
+def ssd_scan_fwd(x, dt, A_head, B, C, D=None, z=None, dt_bias=None, delta_softplus=True, h0=None,
+                 nthreads=1):
+    """The SSD (Mamba-2) layer with scalar A per head, as the selective scan
+    it is: channel d belongs to head d // P, and every channel of head h
+    uses A[d, n] = A_head[h] for all n and Delta[b, d, t] = Delta_head[b, h, t].
+
+    x, z: (batch, dim, L) with dim = H * P; dt: (batch, H, L) (raw, before
+    bias and softplus); A_head, dt_bias: (H,); B, C: (batch, N, L) shared by
+    all heads; D: (dim,); h0: (batch, dim, N).  Returns (y, last_state)."""
+    x, dt, A_head = map(_f64, (x, dt, A_head))
+    batch, dim, L = x.shape
+    H = A_head.shape[0]
+    assert dim % H == 0, "dim must be a multiple of the number of heads"
+    P = dim // H
+    assert dt.shape == (batch, H, L)
+    N = np.asarray(B).shape[1]
+    A_full = np.repeat(A_head, P)[:, None] * np.ones((1, N))
+    delta_full = np.repeat(dt, P, axis=1)
+    bias_full = None if dt_bias is None else np.repeat(_f64(dt_bias), P)
+    return scan_fwd(x, delta_full, A_full, B, C, D, z, bias_full, delta_softplus, h0, nthreads)

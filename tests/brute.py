@@ -156,3 +156,40 @@ def chunked_scan(elems, chunk):
 def affine_elements(u_row, dl_row, A_row, B_b, L):
     """Elements (Abar_t, Bbar_t x_t) of one channel, arrays over states."""
     return [(np.exp(dl_row[t] * A_row), dl_row[t] * B_b[:, t] * u_row[t]) for t in range(L)]
+
+
+def ssd_chunked_y(x, dt, A_head, B, C, chunk, D=None, h0=None):
+    """The SSD evaluation the pages describe, in plain numpy: within each
+    chunk the quadratic (masked-attention) form
+        Y_diag = (L o (C^T B)) (Delta x),  L[t, s] = exp(sum_{s<k<=t} Delta_k A)
+    plus the contribution of the state entering the chunk, and across
+    chunks the linear recurrence of the chunk states.  Delta = dt (already
+    positive; no softplus or bias here), Euler input term, no gate.
+    x: (dim, L) for one batch row, dt: (H, L), B, C: (N, L), h0: (dim, N).
+    Independent of the sequential oracle: no per-step recurrence."""
+    x = np.asarray(x, np.float64)
+    dim, L = x.shape
+    H = len(A_head)
+    P = dim // H
+    N = B.shape[0]
+    y = np.zeros((dim, L))
+    for h in range(H):
+        Xh = x[h * P:(h + 1) * P]                     # (P, L)
+        S = np.zeros((N, P)) if h0 is None else np.asarray(h0[h * P:(h + 1) * P], np.float64).T
+        for c0 in range(0, L, chunk):
+            c1 = min(c0 + chunk, L)
+            q = c1 - c0
+            dl = np.asarray(dt[h, c0:c1], np.float64)
+            la = dl * A_head[h]
+            cum = np.cumsum(la)                        # inclusive log-decay from the chunk start
+            Lm = np.tril(np.exp(cum[:, None] - cum[None, :]))
+            G = C[:, c0:c1].T @ B[:, c0:c1]            # (q, q): C_t . B_s
+            Xc = Xh[:, c0:c1] * dl[None, :]            # Delta_s x_s, (P, q)
+            Yd = (G * Lm) @ Xc.T                        # (q, P)
+            Yo = (np.exp(cum)[:, None] * (C[:, c0:c1].T @ S))   # state entering the chunk
+            y[h * P:(h + 1) * P, c0:c1] = (Yd + Yo).T
+            w = np.exp(cum[-1] - cum)                   # decay from each step to the chunk end
+            S = np.exp(cum[-1]) * S + (B[:, c0:c1] * w[None, :]) @ Xc.T
+    if D is not None:
+        y += np.asarray(D, np.float64)[:, None] * x
+    return y

@@ -626,3 +626,58 @@ def test_backward_of_linear_special_case():
     np.testing.assert_allclose(g["dC"][0], S * dy[None, :], rtol=1e-12, atol=1e-13)
     M = np.tril(C.T @ B)          # M[t, s] = C_t . B_s for s <= t
     np.testing.assert_allclose(g["du"][0, 0], dl * (M.T @ dy), rtol=1e-12, atol=1e-13)
+
+
+
+# --------------------------------------------------------------------- SSD
+# "Mamba" paper review, "Mamba 2": with a scalar-identity A the semiseparable
+# matrix is M_ji = A_{j:i} (C_j . B_i), evaluated by chunks (quadratic form
+# inside a chunk, the linear recurrence across chunks).  NN LAB "Mamba" page,
+# "Bridging Tensor Cores and Recurrence": A = alpha I; intra-chunk dense
+# products, inter-chunk state propagation.  Linear attention is the case
+# Abar = I.
+
+def _ssd_case(rng, batch=1, H=3, P=4, N=5, L=40):
+    x = rng.standard_normal((batch, H * P, L))
+    dt = rng.uniform(0.05, 0.6, size=(batch, H, L))
+    A = -rng.uniform(0.3, 2.0, size=H)
+    B = rng.standard_normal((batch, N, L))
+    C = rng.standard_normal((batch, N, L))
+    D = rng.standard_normal(H * P)
+    h0 = rng.standard_normal((batch, H * P, N))
+    return x, dt, A, B, C, D, h0
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 40, 64])
+def test_ssd_equals_chunked_quadratic_form(chunk):
+    rng = np.random.default_rng(400 + chunk)
+    x, dt, A, B, C, D, h0 = _ssd_case(rng)
+    y, _ = oracle.ssd_scan_fwd(x, dt, A, B, C, D, delta_softplus=False, h0=h0)
+    yc = brute.ssd_chunked_y(x[0], dt[0], A, B[0], C[0], chunk, D, h0[0])
+    np.testing.assert_allclose(y[0], yc, rtol=1e-11, atol=1e-11 * np.abs(yc).max())
+
+
+def test_ssd_linear_attention_special_case():
+    """A = 0: y_t = sum_{s<=t} (C_t . B_s) Delta_s x_s, causal linear attention."""
+    rng = np.random.default_rng(410)
+    x, dt, A, B, C, _, _ = _ssd_case(rng, H=2, P=3, L=25)
+    y, _ = oracle.ssd_scan_fwd(x, dt, np.zeros(2), B, C, delta_softplus=False)
+    G = np.tril(C[0].T @ B[0])                       # (L, L) causal C_t . B_s
+    for h in range(2):
+        for p_ in range(3):
+            d = h * 3 + p_
+            ref = G @ (dt[0, h] * x[0, d])
+            np.testing.assert_allclose(y[0, d], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_ssd_heads_share_delta_and_decay():
+    """Within a head every channel sees the same decay: scaling one
+    channel's input scales only its own output (the heads are SISO banks)."""
+    rng = np.random.default_rng(411)
+    x, dt, A, B, C, _, _ = _ssd_case(rng)
+    y, _ = oracle.ssd_scan_fwd(x, dt, A, B, C, delta_softplus=False)
+    x2 = x.copy()
+    x2[0, 5] *= 3.0
+    y2, _ = oracle.ssd_scan_fwd(x2, dt, A, B, C, delta_softplus=False)
+    np.testing.assert_allclose(y2[0, 5], 3.0 * y[0, 5], rtol=1e-13)
+    np.testing.assert_array_equal(np.delete(y2[0], 5, 0), np.delete(y[0], 5, 0))
