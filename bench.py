@@ -53,7 +53,9 @@ OPS_PER_ELEMENT_CONV = CONV_WIDTH + 4
 # channel sums of dB and dC.
 OPS_PER_ELEMENT_STATE_BWD = 16
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_kernel_c3_traffic.json")
-KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, false, 0>"
+KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 0>"
+KERNEL_NAME_ZOH = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 1>"
+KERNEL_NAME_CONV = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 2>"
 KERNEL_SOURCES = ["selective_state_space_28_amd/csrc/scan_fwd.hip",
                   "selective_state_space_28_amd/csrc/ssm_math.hpp"]
 
@@ -233,7 +235,7 @@ def main():
                   "roofline": {"bound": "alu", "achieved": round(tops_z, 3),
                                "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
                                "frac": round(tops_z / VALU_PEAK_TOPS, 4),
-                               "kernel": KERNEL_NAME.replace("false, 0>", "false, 1>"),
+                               "kernel": KERNEL_NAME_ZOH,
                                "ops_per_launch": ops_z,
                                "ops_executed_per_element_state": OPS_EXECUTED_PER_ELEMENT_STATE_ZOH}}
 
@@ -263,7 +265,7 @@ def main():
                    "roofline": {"bound": "alu", "achieved": round(tops_c, 3),
                                 "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
                                 "frac": round(tops_c / VALU_PEAK_TOPS, 4),
-                                "kernel": KERNEL_NAME.replace("false, 0>", "false, 2>"),
+                                "kernel": KERNEL_NAME_CONV,
                                 "ops_per_launch": ops_c}}
 
     # the backward pass of the same workload (dy ~ N(0, 1), bf16)
