@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selective-scan elements/s (batch·D·L) + achieved HBM GB/s vs peak, 1×MI355X"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, public spec
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, public spec
 # One fp32 VALU instruction per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x
 # 2.4 GHz (the non-packed issue rate; packed fp32 doubles it to 157.3 TFLOP/s
 # of FMA, but packed fp32 is not used here).
@@ -71,6 +72,28 @@ def scan_bytes(cfg) -> int:
     return tok + bc + params + el * s                    # + y
 
 
+def ssd_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one SSD call: x, z read and y written once
+    per element, dt once per (batch, head, step), B and C once, parameters."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    el = cfg.batch * cfg.dim * cfg.seqlen
+    tok = el * s * (2 + (1 if cfg.gate else 0))               # x, y (, z)
+    dt = cfg.batch * cfg.nheads * cfg.seqlen * s
+    bc = 2 * cfg.batch * cfg.dstate * cfg.seqlen * s
+    params = cfg.nheads * 4 * 2 + (cfg.dim * 4 if cfg.dskip else 0)
+    return tok + dt + bc + params
+
+
+def ssd_flops(cfg, chunk=64) -> int:
+    """Matrix work of the chunked evaluation, per chunk and head: the causal
+    half of C^T B (Q^2 N) and of M X^T (Q^2 P), C^T H and the state update
+    (2 Q N P each), as multiply-adds times two."""
+    Q, N, P = chunk, cfg.dstate, cfg.headdim
+    per = Q * Q * N + Q * Q * P + 4 * Q * N * P
+    nchunks = (cfg.seqlen + Q - 1) // Q
+    return cfg.batch * cfg.nheads * nchunks * per
+
+
 def decode_bytes(cfg) -> int:
     s = 2 if cfg.dtype == "bf16" else 4
     rows = cfg.batch * cfg.dim
@@ -111,6 +134,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for the "
                          "HBM byte counters) and exit")
@@ -303,6 +327,8 @@ def main():
 
     if not args.no_decode:
         out["decode"] = bench_decode(dev, args.decode_steps)
+    if not args.no_ssd:
+        out["ssd"] = bench_ssd(dev, args.steps, args.warmup)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
@@ -373,6 +399,63 @@ def bench_decode(dev, steps):
                          "note": "reference = torch in-place update of a state-sized buffer "
                                  "over six rotating buffers (the practical HBM rate of an "
                                  "in-place read-modify-write)"}}
+
+
+def bench_ssd(dev, steps, warmup):
+    """The SSD (scalar A per head) workload: the 2.8B token grid (batch 16,
+    L 2048, 5120 channels) as 80 heads of 64 with 128 states, bf16."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    import synth
+    cfg = synth.SSD_CONFIG
+    inp = synth.make_ssd_inputs(cfg)
+
+    def dev_t(a, f32=False):
+        if a is None:
+            return None
+        if not f32 and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    x, dt, B, C, z = (dev_t(inp[k]) for k in ("x", "dt", "B", "C", "z"))
+    A, D, bias = (dev_t(inp[k], True) for k in ("A", "D", "dt_bias"))
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssm.ssm_ssd_scan_fwd(x, dt, A, B, C, D, z, bias, out=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev]))
+    nbytes = ssd_bytes(cfg)
+    flops = ssd_flops(cfg)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof.update({"kernel": f"ssm::ssd_kernel<unsigned short, {cfg.dstate}>",
+                 "bytes_per_launch": nbytes, "flops_per_launch": flops,
+                 "mfma_TFLOPs": round(tflops, 2)})
+    del x, dt, B, C, z, y
+    return {"workload": f"SSD (scalar A per head) scan: batch {cfg.batch}, {cfg.nheads} heads x "
+                        f"{cfg.headdim}, N {cfg.dstate}, L {cfg.seqlen}, bf16, chunks of 64 on the "
+                        "matrix cores", "ms_per_step": ms, "value": cfg.elements / (ms * 1e-3),
+            "unit": "elements/s", "roofline": roof}
 
 
 def cpu_baseline(cfg, inp, min_core_seconds=12.0):

@@ -251,6 +251,37 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                  float* dh0, int batch, int dim, int dstate, int64_t seqlen, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ssm_ssd_scan_fwd -- the SSD (Mamba-2) form: the same recurrence with a
+ * scalar A per head, computed by chunks on the matrix cores.  The dim =
+ * nheads * headdim channels form heads of headdim consecutive channels;
+ * every channel d of head h = d / headdim uses A[d, n] = A_head[h] for all
+ * states n and the head's step Delta[b, h, t] = softplus(dt[b, h, t] +
+ * dt_bias[h]); B and C are shared by all heads.  Source: "Mamba" paper
+ * review, "Mamba 2" (scalar-identity A; M_ji = A_{j:i} (C_j . B_i); small
+ * chunks in the quadratic form, the linear recurrence across chunks); NN LAB
+ * "Mamba" page, "Bridging Tensor Cores and Recurrence" (A = alpha I;
+ * intra-chunk matrix products, inter-chunk state propagation).
+ *
+ *   x, z, y        (batch, nheads*headdim, seqlen), dtype    x, y required; z NULL -> no gate
+ *   dt             (batch, nheads, seqlen), dtype            required (raw: bias and softplus inside)
+ *   A_head         (nheads) float32                          required
+ *   B, C           (batch, dstate, seqlen), dtype            required
+ *   D_skip         (nheads*headdim) float32                  NULL -> 0
+ *   dt_bias        (nheads) float32                          NULL -> 0
+ *   flags          SSM_DELTA_SOFTPLUS, SSM_BBAR_ZOH as for ssm_scan_fwd
+ *   h0, last_state (batch, nheads*headdim, dstate) float32   NULL -> zero start / not written
+ *   headdim must be 64; dstate in {16, 32, 64, 128} (128 for SSM_BF16 only).
+ * bf16 storage feeds the matrix cores bf16 operands: the chunk matrix, the
+ * decayed B and the state are rounded to bf16 for the products, which are
+ * accumulated in float32; the state itself is carried in float32.  No
+ * workspace.  Otherwise as ssm_scan_fwd.
+ */
+int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const void* B,
+                     const void* C, const float* D_skip, const void* z, const float* dt_bias,
+                     int flags, const float* h0, void* y, float* last_state, int batch, int nheads,
+                     int headdim, int dstate, int64_t seqlen, int dtype, void* stream);
+
 /* ssm_status_string -- a static, human-readable name for a status code. */
 const char* ssm_status_string(int status);
 

@@ -197,7 +197,7 @@ def conv_scan_fwd(x, conv_w, conv_b, conv_state_in, delta, A, B, C, D=None, z=No
 
 
 def ssd_scan_fwd(x, dt, A_head, B, C, D=None, z=None, dt_bias=None, delta_softplus=True, h0=None,
-                 nthreads=1):
+                 nthreads=1, bbar="euler"):
     """The SSD (Mamba-2) layer with scalar A per head, as the selective scan
     it is: channel d belongs to head d // P, and every channel of head h
     uses A[d, n] = A_head[h] for all n and Delta[b, d, t] = Delta_head[b, h, t].
@@ -215,4 +215,4 @@ def ssd_scan_fwd(x, dt, A_head, B, C, D=None, z=None, dt_bias=None, delta_softpl
     A_full = np.repeat(A_head, P)[:, None] * np.ones((1, N))
     delta_full = np.repeat(dt, P, axis=1)
     bias_full = None if dt_bias is None else np.repeat(_f64(dt_bias), P)
-    return scan_fwd(x, delta_full, A_full, B, C, D, z, bias_full, delta_softplus, h0, nthreads)
+    return scan_fwd(x, delta_full, A_full, B, C, D, z, bias_full, delta_softplus, h0, nthreads, bbar)

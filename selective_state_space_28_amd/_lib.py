@@ -56,6 +56,9 @@ def load():
     lib.ssm_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, vp, vp, fp, vp,
                                  vp, fp, vp, fp, fp, i32, i32, i32, i64, i32, vp, sz, vp]
     lib.ssm_scan_bwd.restype = i32
+    lib.ssm_ssd_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, i32, i32, i32,
+                                     i32, i64, i32, vp]
+    lib.ssm_ssd_scan_fwd.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     _lib = lib

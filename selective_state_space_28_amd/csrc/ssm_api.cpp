@@ -503,6 +503,61 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   return ssm::launch_scan_bwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const void* B,
+                     const void* C, const float* D_skip, const void* z, const float* dt_bias,
+                     int flags, const float* h0, void* y, float* last_state, int batch, int nheads,
+                     int headdim, int dstate, int64_t seqlen, int dtype, void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (!flags_ok(flags)) return SSM_ERR_FLAGS;
+  if (batch < 0 || nheads < 0 || seqlen < 0) return SSM_ERR_SHAPE;
+  if (headdim != ssm::kSsdHeadDim) return SSM_ERR_SHAPE;
+  const bool n_ok = dstate == 16 || dstate == 32 || dstate == 64 || (dstate == 128 && dtype == SSM_BF16);
+  if (!n_ok) return SSM_ERR_SHAPE;
+  if ((int64_t)nheads * headdim > INT_MAX / 2 || !shapes_fit(batch, nheads * headdim, seqlen))
+    return SSM_ERR_SHAPE;
+  if ((int64_t)batch * nheads > INT_MAX) return SSM_ERR_SHAPE;
+  const bool empty = batch == 0 || nheads == 0;
+  if (!empty && seqlen > 0 && (!x || !dt || !A_head || !B || !C || !y)) return SSM_ERR_NULL;
+  const size_t es = (size_t)elem_bytes(dtype);
+  if (!aligned(x, es) || !aligned(dt, es) || !aligned(B, es) || !aligned(C, es) ||
+      !aligned(z, es) || !aligned(y, es) || !aligned(A_head, 4) || !aligned(D_skip, 4) ||
+      !aligned(dt_bias, 4) || !aligned(h0, 4) || !aligned(last_state, 4))
+    return SSM_ERR_ALIGN;
+  if (y != nullptr && (y == x || y == dt || (z != nullptr && y == z))) return SSM_ERR_ALIAS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (empty) return SSM_OK;
+  if (seqlen == 0) {
+    if (last_state == nullptr) return SSM_OK;
+    const hipError_t e =
+        ssm::launch_fill_state(last_state, h0, (int64_t)batch * nheads * headdim * dstate, st);
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+  ssm::SsdLaunch a{};
+  a.x = x;
+  a.dt = dt;
+  a.A = A_head;
+  a.B = B;
+  a.C = C;
+  a.Dskip = D_skip;
+  a.z = z;
+  a.dt_bias = dt_bias;
+  a.h0 = h0;
+  a.y = y;
+  a.last_state = last_state;
+  a.batch = batch;
+  a.nheads = nheads;
+  a.headdim = headdim;
+  a.dstate = dstate;
+  a.seqlen = seqlen;
+  a.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  a.zoh = (flags & SSM_BBAR_ZOH) ? 1 : 0;
+  const bool rows16 = ((int64_t)es * seqlen) % 16 == 0;
+  a.vec = rows16 && aligned(x, 16) && aligned(B, 16) && aligned(C, 16) && aligned(z, 16) &&
+          aligned(y, 16);
+  a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
+  return ssm::launch_ssd_fwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 const char* ssm_status_string(int status) {
   switch (status) {
     case SSM_OK: return "SSM_OK";

@@ -120,7 +120,28 @@ struct BwdLaunch {
   Dtype dtype;
 };
 
+// SSD (scalar A per head) forward: heads of kSsdHeadDim channels.
+constexpr int kSsdHeadDim = 64;
+struct SsdLaunch {
+  const void* x;          // (batch, nheads * headdim, seqlen)
+  const void* dt;         // (batch, nheads, seqlen), raw (bias, softplus applied inside)
+  const float* A;         // (nheads)
+  const void* B;          // (batch, dstate, seqlen), shared by the heads
+  const void* C;
+  const float* Dskip;     // (nheads * headdim) nullable
+  const void* z;          // nullable
+  const float* dt_bias;   // (nheads) nullable
+  const float* h0;        // (batch, nheads * headdim, dstate) nullable
+  void* y;
+  float* last_state;      // nullable
+  int batch, nheads, headdim, dstate;
+  int64_t seqlen;
+  int softplus, zoh, vec;
+  Dtype dtype;
+};
+
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream);
+hipError_t launch_ssd_fwd(const SsdLaunch& a, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdLaunch& a, hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);
 // last_state = h0 (or zeros when h0 is null) for an empty sequence.

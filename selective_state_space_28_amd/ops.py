@@ -244,3 +244,42 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     if rc != 0:
         raise SsmError(rc, "ssm_scan_bwd")
     return g
+
+
+def ssm_ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, delta_softplus=True, h0=None, *,
+                     bbar="euler", return_last_state=False, out=None):
+    """The SSD (scalar A per head) scan on the matrix cores; see include/ssm.h.
+    x, z: (batch, nheads * 64, L); dt: (batch, nheads, L); A, dt_bias:
+    (nheads,) float32; B, C: (batch, N, L); D: (dim,) float32; h0:
+    (batch, dim, N) float32.  Returns y, and (y, last_state) when asked."""
+    lib = load()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("libssm runs on the GPU: tensors must be on a cuda device")
+    dtp = x.dtype
+    code = _code(x)
+    batch, dim, L = x.shape
+    H = A.shape[0] if A.dim() == 1 else -1
+    if H <= 0 or dim % H != 0:
+        raise ValueError("x's channel count must be a multiple of the number of heads")
+    P = dim // H
+    N = B.shape[1] if B.dim() == 3 else -1
+    _check("x", x, (batch, dim, L), dtp, dev)
+    _check("dt", dt, (batch, H, L), dtp, dev)
+    _check("A", A, (H,), torch.float32, dev)
+    _check("B", B, (batch, N, L), dtp, dev)
+    _check("C", C, (batch, N, L), dtp, dev)
+    _check("D", D, (dim,), torch.float32, dev, required=False)
+    _check("z", z, (batch, dim, L), dtp, dev, required=False)
+    _check("dt_bias", dt_bias, (H,), torch.float32, dev, required=False)
+    _check("h0", h0, (batch, dim, N), torch.float32, dev, required=False)
+    y = out if out is not None else torch.empty_like(x)
+    _check("out", y, (batch, dim, L), dtp, dev)
+    last = torch.empty((batch, dim, N), dtype=torch.float32, device=dev) if return_last_state else None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_ssd_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                              _ptr(dt_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(y),
+                              _ptr(last), batch, H, P, N, L, code, stream)
+    if rc != 0:
+        raise SsmError(rc, "ssm_ssd_scan_fwd")
+    return (y, last) if return_last_state else y

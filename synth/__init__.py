@@ -20,8 +20,8 @@ The convolution prologue's taps, bias and carried state come from
 ``default_rng([seed, 1_000_003])`` (make_conv_params), a key no decode
 step uses; its input x is the workload's u draw.
 """
-from .configs import (ScanConfig, DecodeConfig, SCAN_CONFIGS, DECODE_CONFIG,  # noqa: F401
-                      CONFIGS, get_config)
+from .configs import (ScanConfig, DecodeConfig, SsdConfig, SCAN_CONFIGS, DECODE_CONFIG,  # noqa: F401
+                      SSD_CONFIG, CONFIGS, get_config)
 from .inputs import (bf16_bits, bf16_to_f32, make_scan_inputs, make_decode_params,  # noqa: F401
                      make_decode_step, impulse_inputs, widen, inv_softplus_bias,
-                     make_conv_params)
+                     make_conv_params, make_ssd_inputs)

@@ -52,6 +52,35 @@ SCAN_CONFIGS = {
     "c3": ScanConfig("c3", 16, 5120, 16, 2048, "bf16", seed=3, a_jitter=0.1),
 }
 DECODE_CONFIG = DecodeConfig("c4", 256, 5120, 16, 64, "bf16", seed=4)
+
+
+@dataclass(frozen=True)
+class SsdConfig:
+    """A scalar-A-per-head (SSD) workload: nheads heads of headdim channels."""
+    name: str
+    batch: int
+    nheads: int
+    headdim: int
+    dstate: int
+    seqlen: int
+    dtype: str
+    seed: int
+    delta_std: float = 0.5
+    gate: bool = True
+    dskip: bool = True
+
+    @property
+    def dim(self) -> int:
+        return self.nheads * self.headdim
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+
+# the 2.8B-shaped token grid of c3 (batch 16, D 5120, L 2048) as 80 heads of 64
+# channels with 128 states
+SSD_CONFIG = SsdConfig("c5", 16, 80, 64, 128, 2048, "bf16", seed=5)
 CONFIGS = dict(SCAN_CONFIGS, c4=DECODE_CONFIG)
 
 

@@ -5,7 +5,7 @@ import math
 
 import numpy as np
 
-from .configs import ScanConfig, DecodeConfig
+from .configs import ScanConfig, DecodeConfig, SsdConfig
 
 DT_MIN, DT_MAX = 1e-3, 1e-1
 
@@ -126,3 +126,23 @@ def make_conv_params(dim: int, width: int, seed: int, state_batch: int | None = 
         out["conv_state"] = rng.standard_normal(size=(state_batch, dim, width - 1),
                                                 dtype=np.float32)
     return out
+
+
+def make_ssd_inputs(cfg: SsdConfig, seed: int | None = None) -> dict:
+    """Seeded inputs of an SSD workload, drawn in the order
+    A_head -> dt (-> dt_bias) -> D -> dt_raw -> x -> B -> C -> z:
+    A_head = -U(1, 16) per head; dt_bias = softplus^-1 of a log-uniform step
+    in [1e-3, 1e-1]; D, x, B, C, z ~ N(0, 1); dt_raw ~ N(0, delta_std^2).
+    x, z: (batch, dim, L); dt_raw: (batch, nheads, L); B, C: (batch, N, L)."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    b, H, L = cfg.batch, cfg.nheads, cfg.seqlen
+    A = -rng.uniform(1.0, 16.0, size=H).astype(np.float32)
+    dtv = np.exp(rng.uniform(math.log(DT_MIN), math.log(DT_MAX), size=H))
+    dt_bias = inv_softplus_bias(dtv).astype(np.float32)
+    D = rng.standard_normal(size=cfg.dim).astype(np.float32) if cfg.dskip else None
+    dt = _normal(rng, (b, H, L), cfg.delta_std, cfg.dtype)
+    x = _normal(rng, (b, cfg.dim, L), 1.0, cfg.dtype)
+    B = _normal(rng, (b, cfg.dstate, L), 1.0, cfg.dtype)
+    C = _normal(rng, (b, cfg.dstate, L), 1.0, cfg.dtype)
+    z = _normal(rng, (b, cfg.dim, L), 1.0, cfg.dtype) if cfg.gate else None
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, z=z, dt_bias=dt_bias, dtype=cfg.dtype)

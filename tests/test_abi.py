@@ -15,7 +15,7 @@ def test_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) == {"ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
                           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_scan_bwd_workspace_bytes",
-                          "ssm_scan_bwd", "ssm_status_string"}
+                          "ssm_scan_bwd", "ssm_ssd_scan_fwd", "ssm_status_string"}
     lib = ctypes.CDLL(load()._name)
     for n in names:
         assert hasattr(lib, n), n
@@ -204,3 +204,28 @@ def test_bwd_workspace_query_and_check():
     assert _bwd(ws=None, wsb=0) == WS
     assert _bwd(ws=P, wsb=need - 1) == WS
     assert _bwd(batch=0) == OK
+
+
+def _ssd(**kw):
+    a = dict(x=P, dt=P + 0x10000, A=P + 0x20000, B=P + 0x30000, C=P + 0x40000, D=None, z=None,
+             bias=None, fl=1, h0=None, y=P + 0x50000, last=None, batch=1, H=4, hd=64, N=128, L=2048,
+             dtype=1, stream=None)
+    a.update(kw)
+    return load().ssm_ssd_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                                   a["fl"], a["h0"], a["y"], a["last"], a["batch"], a["H"], a["hd"],
+                                   a["N"], a["L"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hd=32), SHAPE), (dict(N=8), SHAPE), (dict(N=128, dtype=0), SHAPE), (dict(N=256), SHAPE),
+    (dict(H=-1), SHAPE), (dict(L=-1), SHAPE), (dict(dtype=4), DTYPE), (dict(fl=8), FLAGS),
+    (dict(x=None), NULL), (dict(dt=None), NULL), (dict(A=None), NULL), (dict(y=None), NULL),
+    (dict(x=P + 1), ALIGN), (dict(A=P + 0x20002), ALIGN), (dict(y=P), ALIAS),
+])
+def test_ssd_validation(kw, code):
+    assert _ssd(**kw) == code
+
+
+def test_ssd_empty_needs_no_gpu():
+    assert _ssd(batch=0) == OK
+    assert _ssd(H=0, x=None) == OK
