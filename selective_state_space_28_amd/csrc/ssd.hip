@@ -44,6 +44,18 @@ struct Mma<uint16_t> {  // bf16 storage: bf16 operands, v_mfma_f32_16x16x32_bf16
                                                    0);
   }
   __device__ static Op cvt(float v) { return (__bf16)v; }
+  // acc += A (16 x 16, rows of a [.][lda] array at a, k contiguous) times a
+  // 16x16 tile held in accumulator layout (lane l: rows 4*(l/16)..+3, column
+  // l % 16): v_mfma_f32_16x16x16_bf16 takes exactly that layout as its B
+  // operand (4 consecutive k per lane).
+  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, f32x4_t btile, f32x4_t acc, int lane) {
+    typedef short s16x4_t __attribute__((ext_vector_type(4)));
+    const s16x4_t av = *reinterpret_cast<const s16x4_t*>(a + (lane & 15) * lda + 4 * (lane >> 4));
+    s16x4_t bv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = __builtin_bit_cast(short, (__bf16)btile[j]);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+  }
 };
 
 template <>
@@ -55,6 +67,15 @@ struct Mma<float> {  // fp32 storage: fp32 operands, v_mfma_f32_16x16x4_f32
     return __builtin_amdgcn_mfma_f32_16x16x4f32(*a, *b, c, 0, 0, 0);
   }
   __device__ static Op cvt(float v) { return v; }
+  // as for bf16, with four K = 4 products: the r-th takes k = 4 * (l/16) + r
+  // from each lane's own accumulator element r
+  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, f32x4_t btile, f32x4_t acc, int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(lane & 15) * lda + 4 * (lane >> 4) + r], btile[r],
+                                                  acc, 0, 0, 0);
+    return acc;
+  }
 };
 
 struct SsdSizes {
@@ -79,6 +100,59 @@ __device__ __forceinline__ f32x4_t tile_mma(const typename Mma<T>::Op* A, int ld
   return acc;
 }
 
+// Words of a run of 8 consecutive elements of T.
+template <typename T>
+constexpr int kRunWords = 8 * (int)sizeof(T) / 4;
+
+// 8 elements at p into raw words: one or two 16-byte loads when `vec`, else
+// element loads with zeros past `valid`.
+template <typename T>
+__device__ __forceinline__ void load_run8(const T* __restrict__ p, bool vec, int valid,
+                                          uint32_t (&w)[kRunWords<T>]) {
+  if (vec) {
+    load_words<kRunWords<T>>(p, w);
+  } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = 2 * q < valid ? (uint32_t)p[2 * q] : 0u;
+      const uint32_t hi = 2 * q + 1 < valid ? (uint32_t)p[2 * q + 1] : 0u;
+      w[q] = lo | (hi << 16);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = q < valid ? __float_as_uint(p[q]) : 0u;
+  }
+}
+
+// Element j (0..7) of a run, as float.
+template <typename T>
+__device__ __forceinline__ float run_elem(const uint32_t (&w)[kRunWords<T>], int j) {
+  if constexpr (sizeof(T) == 2) return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+  else return __uint_as_float(w[j]);
+}
+
+// Row j of the transpose of an 8 x 8 tile (rows r = 0..7, each a run of 8):
+// out = (tile[0][j], ..., tile[7][j]) as raw words.
+template <typename T>
+__device__ __forceinline__ void tile_column(const uint32_t (&tile)[8][kRunWords<T>], int j,
+                                            uint32_t (&out)[kRunWords<T>]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = tile[2 * q][j >> 1], b = tile[2 * q + 1][j >> 1];
+      out[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) out[r] = tile[r][j];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_store_run(void* dst, const uint32_t (&w)[kRunWords<T>]) {
+  store_words<kRunWords<T>>(dst, w);
+}
+
 template <typename T, int N>
 __global__ __launch_bounds__(256, 1) void ssd_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A_head,
@@ -86,25 +160,33 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
     const T* __restrict__ z, const float* __restrict__ dt_bias, const float* __restrict__ h0,
     T* __restrict__ y, float* __restrict__ last_state, const SsdSizes p) {
   using Op = typename Mma<T>::Op;
+  static_assert(sizeof(Op) == sizeof(T), "operands keep the storage type");
   constexpr int Q = 64;            // chunk length
   constexpr int P = 64;            // channels per head
+  constexpr int RW = kRunWords<T>;
   constexpr int PADK = 16 / (int)sizeof(Op);   // one 16-byte pad per row
   constexpr int LQ = Q + PADK;     // row length of [.][Q] operand arrays
   // the state index as a product dimension, rounded up to the instruction's K
   // (columns N .. KN-1 of the [.][KN] arrays stay zero)
   constexpr int KN = (N + Mma<T>::K - 1) / Mma<T>::K * Mma<T>::K;
   constexpr int LN = KN + PADK;    // row length of [.][KN] operand arrays
-  constexpr int HT = N / 16;       // state tiles per wave (rows of N, 4 column tiles of P)
+  constexpr int HT = N / 16;       // state tiles per wave
+  constexpr int XI = P * (Q / 8) / 256;        // runs of x (and z) per thread
   static_assert(N % 16 == 0 && N >= 16 && N <= 128, "state count");
+  static_assert(P == Q && XI * 256 == P * (Q / 8), "staging layout");
 
   __shared__ __align__(16) Op sX[P][LQ];     // x chunk, [p][t]
+  __shared__ __align__(16) Op sXw[P][LQ];    // x o exp(cum_Q - cum_s) Bbar_s, [p][s]
+  __shared__ __align__(16) Op sB[N][LQ];     // B chunk, [n][s]
   __shared__ __align__(16) Op sCt[Q][LN];    // C^T, [t][n]
-  __shared__ __align__(16) Op sBt[Q][LN];    // B^T, [s][n]
-  __shared__ __align__(16) Op sBw[N][LQ];    // B o exp(cum_Q - cum_s) Bbar_s, [n][s]
+  // B^T, [s][n]; after the mask step, the output staging [p][t] (float)
+  constexpr int BT_BYTES = (int)sizeof(Op) * Q * LN;
+  constexpr int Y_BYTES = (int)sizeof(float) * P * (Q + 4);
+  __shared__ __align__(16) unsigned char sBtY[BT_BYTES > Y_BYTES ? BT_BYTES : Y_BYTES];
   __shared__ __align__(16) Op sM[Q][LQ];     // the masked chunk matrix, [t][s]
-  __shared__ __align__(16) Op sH[P][LN];     // the state entering the chunk, [p][n]
-  __shared__ float sY[P][Q + 4];             // output staging, [p][t]
-  __shared__ float sDt[Q], sCum[Q], sCoef[Q];
+  __shared__ float sCum[Q], sCoef[Q];
+  Op(*sBt)[LN] = reinterpret_cast<Op(*)[LN]>(sBtY);
+  float(*sY)[Q + 4] = reinterpret_cast<float(*)[Q + 4]>(sBtY);
 
   const int b = blockIdx.x / p.nheads;
   const int h = blockIdx.x % p.nheads;
@@ -125,38 +207,79 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
   const T* dth = dt + ((int64_t)b * p.nheads + h) * L;
 
   if constexpr (KN > N) {
-    for (int i = tid; i < Q * (KN - N); i += 256) {
-      const int r = i / (KN - N), c = N + i % (KN - N);
-      sCt[r][c] = Mma<T>::cvt(0.0f);
-      sBt[r][c] = Mma<T>::cvt(0.0f);
-      sH[r][c] = Mma<T>::cvt(0.0f);   // P == Q rows
-    }
+    for (int i = tid; i < Q * (KN - N); i += 256) sCt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
   }
-  static_assert(P == Q, "the padding loop covers sH's rows with Q");
 
-  // state tiles of this wave: the (N/16) x 4 grid of 16x16 tiles of H (N x P)
-  // is split over the waves, HT tiles each
+  // the state: wave w owns channels 16w..16w+15, as HT 16x16 tiles of states
+  // 16k..16k+15 (accumulator layout: lane l holds rows 4*(l/16)..+3, column l % 16)
   f32x4_t H[HT];
 #pragma unroll
-  for (int i = 0; i < HT; ++i) {
-    const int tile = w * HT + i;
-    const int n0 = (tile / 4) * 16, p0 = (tile % 4) * 16;
+  for (int k = 0; k < HT; ++k) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int n = n0 + 4 * (lane >> 4) + r, pp = p0 + (lane & 15);
-      H[i][r] = h0 != nullptr ? h0[((int64_t)b * dim + h * P + pp) * N + n] : 0.0f;
+      const int n = 16 * k + 4 * (lane >> 4) + r, pp = 16 * w + (lane & 15);
+      H[k][r] = h0 != nullptr ? h0[((int64_t)b * dim + h * P + pp) * N + n] : 0.0f;
     }
   }
+
+  // ---- staging roles ---------------------------------------------------------------
+  // x, z: runs (p = item / 8, steps 8 * (item % 8) ..) for item = tid + 256 k
+  // B, C: thread tid < 2N owns the 8 x 8 tile (states n0.., steps t8..) of B
+  //       (tid < N) or C (N <= tid < 2N)
+  const bool has_tile = tid < 2 * N;
+  const int tile_id = has_tile ? (tid < N ? tid : tid - N) : 0;
+  const int tn0 = (tile_id / 8) * 8, tt8 = (tile_id % 8) * 8;
+  const T* tsrc = (tid < N ? Bb : Cb) + (int64_t)tn0 * L + tt8;
+
+  uint32_t rx[XI][RW], rz[XI][RW], rt[8][RW];
+  float rdt = 0.0f;
+  auto prefetch = [&](int64_t c0) {
+    const int tv = (int)(L - c0 < Q ? L - c0 : Q);
+    const bool vec = p.vec && tv == Q;
+#pragma unroll
+    for (int k = 0; k < XI; ++k) {
+      const int item = tid + 256 * k;
+      const int t8 = (item % (Q / 8)) * 8;
+      load_run8<T>(xh + (int64_t)(item / (Q / 8)) * L + c0 + t8, vec, tv - t8, rx[k]);
+    }
+    if (has_tile) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) load_run8<T>(tsrc + (int64_t)r * L + c0, vec, tv - tt8, rt[r]);
+    }
+    if (w == 0) rdt = lane < tv ? Elem<T>::load(dth + c0 + lane) : 0.0f;
+  };
+  prefetch(0);
 
   for (int64_t t0 = 0; t0 < L; t0 += Q) {
     const int tvalid = (int)(L - t0 < Q ? L - t0 : Q);
     const bool full = p.vec && tvalid == Q;
 
-    // ---- Delta, its prefix sum over the chunk, the input coefficient -------------
+    // ---- (1) this chunk's x, B, C into LDS; Delta and its prefix sum; H ---------------
+    if constexpr (KN > N) {  // the output staging of the last chunk overwrote B^T's padding
+      for (int i = tid; i < Q * (KN - N); i += 256) sBt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < XI; ++k) {
+      const int item = tid + 256 * k;
+      lds_store_run<T>(&sX[item / (Q / 8)][(item % (Q / 8)) * 8], rx[k]);
+    }
+    if (has_tile) {
+      Op(*dstT)[LN] = tid < N ? sBt : sCt;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t col[RW];
+        tile_column<T>(rt, j, col);
+        lds_store_run<T>(&dstT[tt8 + j][tn0], col);
+      }
+      if (tid < N) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) lds_store_run<T>(&sB[tn0 + r][tt8], rt[r]);
+      }
+    }
     if (w == 0) {
       float dl = 0.0f, coef = 0.0f;
       if (lane < tvalid) {
-        const float xr = Elem<T>::load(dth + t0 + lane) + bias_h;
+        const float xr = rdt + bias_h;
         dl = p.softplus ? softplus_f32(xr) : xr;
         if (p.zoh) {
           const float x2 = dl * A2h;
@@ -171,69 +294,37 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
         const float o = __shfl_up(cum, off);
         if (lane >= off) cum += o;
       }
-      sDt[lane] = dl;
       sCum[lane] = cum;
       sCoef[lane] = coef;
     }
-    // ---- x chunk: [p][t] -------------------------------------------------------
-    for (int i = tid; i < P * (Q / 8); i += 256) {
-      const int pp = i / (Q / 8), t8 = (i % (Q / 8)) * 8;
-      const T* src = xh + (int64_t)pp * L + t0 + t8;
-      float v[8];
-      if (full) {
-        uint32_t wds[8 * sizeof(T) / 4];
-        load_words<8 * sizeof(T) / 4>(src, wds);
-        words_to_floats<T, 8>(wds, v);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = t8 + j < tvalid ? Elem<T>::load(src + j) : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sX[pp][t8 + j] = Mma<T>::cvt(v[j]);
-    }
     __syncthreads();
 
-    // ---- B, C rows: B^T and C^T for G, B o w for the state update ----------------
+    // ---- (2) x o w, then the next chunk's loads and this chunk's z; the mask --------------
     {
       const float cumQ = sCum[Q - 1];
-      for (int i = tid; i < N * (Q / 8); i += 256) {
-        const int n = i / (Q / 8), t8 = (i % (Q / 8)) * 8;
-        float vb[8], vc[8];
-        const T* sb = Bb + (int64_t)n * L + t0 + t8;
-        const T* sc = Cb + (int64_t)n * L + t0 + t8;
-        if (full) {
-          uint32_t wb[8 * sizeof(T) / 4], wc[8 * sizeof(T) / 4];
-          load_words<8 * sizeof(T) / 4>(sb, wb);
-          load_words<8 * sizeof(T) / 4>(sc, wc);
-          words_to_floats<T, 8>(wb, vb);
-          words_to_floats<T, 8>(wc, vc);
-        } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            vb[j] = t8 + j < tvalid ? Elem<T>::load(sb + j) : 0.0f;
-            vc[j] = t8 + j < tvalid ? Elem<T>::load(sc + j) : 0.0f;
-          }
-        }
+      for (int k = 0; k < XI; ++k) {
+        const int item = tid + 256 * k;
+        const int pp = item / (Q / 8), t8 = (item % (Q / 8)) * 8;
+        float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = t8 + j;
-          sBt[t][n] = Mma<T>::cvt(vb[j]);
-          sCt[t][n] = Mma<T>::cvt(vc[j]);
-          sBw[n][t] = Mma<T>::cvt(vb[j] * (exp2_hw((cumQ - sCum[t]) * kLog2e) * sCoef[t]));
-        }
+        for (int j = 0; j < 8; ++j)
+          v[j] = run_elem<T>(rx[k], j) * (exp2_hw((cumQ - sCum[t8 + j]) * kLog2e) * sCoef[t8 + j]);
+        uint32_t wv[RW];
+        pack_floats<T, 8>(v, wv);
+        lds_store_run<T>(&sXw[pp][t8], wv);
       }
     }
-    // ---- the state entering the chunk, [p][n], as an operand -----------------------
+    if (zh != nullptr) {
 #pragma unroll
-    for (int i = 0; i < HT; ++i) {
-      const int tile = w * HT + i;
-      const int n0 = (tile / 4) * 16, p0 = (tile % 4) * 16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sH[p0 + (lane & 15)][n0 + 4 * (lane >> 4) + r] = Mma<T>::cvt(H[i][r]);
+      for (int k = 0; k < XI; ++k) {
+        const int item = tid + 256 * k;
+        const int t8 = (item % (Q / 8)) * 8;
+        load_run8<T>(zh + (int64_t)(item / (Q / 8)) * L + t0 + t8, full, tvalid - t8, rz[k]);
+      }
     }
-    __syncthreads();
+    if (t0 + Q < L) prefetch(t0 + Q);
 
-    // ---- M = (C^T B) o exp(cum_t - cum_s) Bbar_s (s <= t): rows 16w.. -----------------
 #pragma unroll
     for (int j = 0; j < Q / 16; ++j) {
       f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -249,67 +340,48 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
     }
     __syncthreads();
 
-    // ---- Y = M X^T + diag(exp(cum_t)) C^T H ----------------------------------------------
-    f32x4_t Y[P / 16], Yo[P / 16];
+    // ---- (3) Y = M X^T + diag(exp(cum_t)) C^T H for this wave's channels, staged [p][t]
+    //          (the staging reuses sBt: its last reads were in the mask step) ---------------
 #pragma unroll
-    for (int j = 0; j < P / 16; ++j) {
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      Y[j] = tile_mma<T>(&sM[0][0], LQ, 16 * w, &sX[0][0], LQ, 16 * j, 16 * (w + 1), lane, acc);
-      Yo[j] = tile_mma<T>(&sCt[0][0], LN, 16 * w, &sH[0][0], LN, 16 * j, KN, lane, acc);
+    for (int i = 0; i < Q / 16; ++i) {
+      f32x4_t yd = {0.0f, 0.0f, 0.0f, 0.0f}, yo = {0.0f, 0.0f, 0.0f, 0.0f};
+      yd = tile_mma<T>(&sM[0][0], LQ, 16 * i, &sX[0][0], LQ, 16 * w, 16 * (i + 1), lane, yd);
+#pragma unroll
+      for (int k = 0; k < HT; ++k) yo = Mma<T>::mma_acc_b(&sCt[16 * i][16 * k], LN, H[k], yo, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * i + 4 * (lane >> 4) + r;
+        sY[16 * w + (lane & 15)][t] = __builtin_fmaf(exp2_hw(sCum[t] * kLog2e), yo[r], yd[r]);
+      }
     }
-    // ---- H <- exp(cum_Q) H + (B o w) X^T ------------------------------------------------
+    // ---- H <- exp(cum_Q) H + B (x o w)^T ----------------------------------------------------
     {
       const float decay = exp2_hw(sCum[Q - 1] * kLog2e);
 #pragma unroll
-      for (int i = 0; i < HT; ++i) {
-        const int tile = w * HT + i;
-        const int n0 = (tile / 4) * 16, p0 = (tile % 4) * 16;
+      for (int k = 0; k < HT; ++k) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) H[i][r] *= decay;
-        H[i] = tile_mma<T>(&sBw[0][0], LQ, n0, &sX[0][0], LQ, p0, Q, lane, H[i]);
-      }
-    }
-    // ---- stage Y, [p][t] ---------------------------------------------------------------
-#pragma unroll
-    for (int j = 0; j < P / 16; ++j) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * (lane >> 4) + r;
-        const int pp = 16 * j + (lane & 15);
-        sY[pp][t] = __builtin_fmaf(exp2_hw(sCum[t] * kLog2e), Yo[j][r], Y[j][r]);
+        for (int r = 0; r < 4; ++r) H[k][r] *= decay;
+        H[k] = tile_mma<T>(&sB[0][0], LQ, 16 * k, &sXw[0][0], LQ, 16 * w, Q, lane, H[k]);
       }
     }
     __syncthreads();
 
-    // ---- y = (Y + D x) silu(z): rows of 8 steps per thread ---------------------------------
-    for (int i = tid; i < P * (Q / 8); i += 256) {
-      const int pp = i / (Q / 8), t8 = (i % (Q / 8)) * 8;
-      const int c = h * P + pp;
-      const float Dc = Dskip != nullptr ? Dskip[c] : 0.0f;
-      const int64_t off = (int64_t)pp * L + t0 + t8;
-      float xv[8], zv[8], yv[8];
-      if (full) {
-        uint32_t wx[8 * sizeof(T) / 4];
-        load_words<8 * sizeof(T) / 4>(xh + off, wx);
-        words_to_floats<T, 8>(wx, xv);
-        if (zh != nullptr) {
-          uint32_t wz[8 * sizeof(T) / 4];
-          load_words<8 * sizeof(T) / 4>(zh + off, wz);
-          words_to_floats<T, 8>(wz, zv);
-        }
-      } else {
+    // ---- (4) y = (Y + D x) silu(z) -----------------------------------------------------
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          xv[j] = t8 + j < tvalid ? Elem<T>::load(xh + off + j) : 0.0f;
-          zv[j] = (zh != nullptr && t8 + j < tvalid) ? Elem<T>::load(zh + off + j) : 0.0f;
-        }
-      }
+    for (int k = 0; k < XI; ++k) {
+      const int item = tid + 256 * k;
+      const int pp = item / (Q / 8), t8 = (item % (Q / 8)) * 8;
+      const float Dc = Dskip != nullptr ? Dskip[h * P + pp] : 0.0f;
+      uint32_t xw[RW];
+      load_words<RW>(&sX[pp][t8], xw);
+      float yv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float v = __builtin_fmaf(Dc, xv[j], sY[pp][t8 + j]);
-        if (zh != nullptr) v *= silu_f32(zv[j]);
+        float v = __builtin_fmaf(Dc, run_elem<T>(xw, j), sY[pp][t8 + j]);
+        if (zh != nullptr) v *= silu_f32(run_elem<T>(rz[k], j));
         yv[j] = v;
       }
+      const int64_t off = (int64_t)pp * L + t0 + t8;
       if (full) {
         store_floats<T, 8>(yh + off, yv);
       } else {
@@ -323,13 +395,11 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
 
   if (last_state != nullptr) {
 #pragma unroll
-    for (int i = 0; i < HT; ++i) {
-      const int tile = w * HT + i;
-      const int n0 = (tile / 4) * 16, p0 = (tile % 4) * 16;
+    for (int k = 0; k < HT; ++k) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int n = n0 + 4 * (lane >> 4) + r, pp = p0 + (lane & 15);
-        last_state[((int64_t)b * dim + h * P + pp) * N + n] = H[i][r];
+        const int n = 16 * k + 4 * (lane >> 4) + r, pp = 16 * w + (lane & 15);
+        last_state[((int64_t)b * dim + h * P + pp) * N + n] = H[k][r];
       }
     }
   }
