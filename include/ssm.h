@@ -272,15 +272,23 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
  *   flags          SSM_DELTA_SOFTPLUS, SSM_BBAR_ZOH as for ssm_scan_fwd
  *   h0, last_state (batch, nheads*headdim, dstate) float32   NULL -> zero start / not written
  *   headdim must be 64; dstate in {16, 32, 64, 128} (128 for SSM_BF16 only).
+ *   workspace      at least ssm_ssd_scan_fwd_workspace_bytes(...) bytes, 256-byte
+ *                  aligned, owned by the caller (B and C with the state index
+ *                  contiguous, rewritten by every call)
  * bf16 storage feeds the matrix cores bf16 operands: the chunk matrix, the
- * decayed B and the state are rounded to bf16 for the products, which are
- * accumulated in float32; the state itself is carried in float32.  No
- * workspace.  Otherwise as ssm_scan_fwd.
+ * decayed x and the state are rounded to bf16 for the products, which are
+ * accumulated in float32; the state itself is carried in float32.
+ * Otherwise as ssm_scan_fwd.
  */
 int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const void* B,
                      const void* C, const float* D_skip, const void* z, const float* dt_bias,
                      int flags, const float* h0, void* y, float* last_state, int batch, int nheads,
-                     int headdim, int dstate, int64_t seqlen, int dtype, void* stream);
+                     int headdim, int dstate, int64_t seqlen, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* ssm_ssd_scan_fwd_workspace_bytes -- 2 * batch * seqlen * dstate elements of
+ * dtype, rounded up to 256 bytes; 0 for an empty problem.  Pure host function. */
+size_t ssm_ssd_scan_fwd_workspace_bytes(int batch, int dstate, int64_t seqlen, int dtype);
 
 /* ssm_status_string -- a static, human-readable name for a status code. */
 const char* ssm_status_string(int status);

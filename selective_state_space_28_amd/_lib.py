@@ -57,7 +57,9 @@ def load():
                                  vp, fp, vp, fp, fp, i32, i32, i32, i64, i32, vp, sz, vp]
     lib.ssm_scan_bwd.restype = i32
     lib.ssm_ssd_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, i32, i32, i32,
-                                     i32, i64, i32, vp]
+                                     i32, i64, i32, vp, sz, vp]
+    lib.ssm_ssd_scan_fwd_workspace_bytes.argtypes = [i32, i32, i64, i32]
+    lib.ssm_ssd_scan_fwd_workspace_bytes.restype = sz
     lib.ssm_ssd_scan_fwd.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p

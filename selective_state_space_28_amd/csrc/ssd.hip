@@ -48,12 +48,16 @@ struct Mma<uint16_t> {  // bf16 storage: bf16 operands, v_mfma_f32_16x16x32_bf16
   // 16x16 tile held in accumulator layout (lane l: rows 4*(l/16)..+3, column
   // l % 16): v_mfma_f32_16x16x16_bf16 takes exactly that layout as its B
   // operand (4 consecutive k per lane).
-  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, f32x4_t btile, f32x4_t acc, int lane) {
-    typedef short s16x4_t __attribute__((ext_vector_type(4)));
-    const s16x4_t av = *reinterpret_cast<const s16x4_t*>(a + (lane & 15) * lda + 4 * (lane >> 4));
-    s16x4_t bv;
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  using AccB = s16x4_t;  // an accumulator tile as a B operand
+  __device__ static AccB pack_acc(f32x4_t t) {
+    AccB bv;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = __builtin_bit_cast(short, (__bf16)btile[j]);
+    for (int j = 0; j < 4; ++j) bv[j] = __builtin_bit_cast(short, (__bf16)t[j]);
+    return bv;
+  }
+  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, AccB bv, f32x4_t acc, int lane) {
+    const s16x4_t av = *reinterpret_cast<const s16x4_t*>(a + (lane & 15) * lda + 4 * (lane >> 4));
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
   }
 };
@@ -69,7 +73,9 @@ struct Mma<float> {  // fp32 storage: fp32 operands, v_mfma_f32_16x16x4_f32
   __device__ static Op cvt(float v) { return v; }
   // as for bf16, with four K = 4 products: the r-th takes k = 4 * (l/16) + r
   // from each lane's own accumulator element r
-  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, f32x4_t btile, f32x4_t acc, int lane) {
+  using AccB = f32x4_t;
+  __device__ static AccB pack_acc(f32x4_t t) { return t; }
+  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, AccB btile, f32x4_t acc, int lane) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(lane & 15) * lda + 4 * (lane >> 4) + r], btile[r],
@@ -124,6 +130,10 @@ __device__ __forceinline__ void load_run8(const T* __restrict__ p, bool vec, int
   }
 }
 
+// A raw element as float.
+__device__ __forceinline__ float raw_value(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float raw_value(float v) { return v; }
+
 // Element j (0..7) of a run, as float.
 template <typename T>
 __device__ __forceinline__ float run_elem(const uint32_t (&w)[kRunWords<T>], int j) {
@@ -131,34 +141,68 @@ __device__ __forceinline__ float run_elem(const uint32_t (&w)[kRunWords<T>], int
   else return __uint_as_float(w[j]);
 }
 
-// Row j of the transpose of an 8 x 8 tile (rows r = 0..7, each a run of 8):
-// out = (tile[0][j], ..., tile[7][j]) as raw words.
-template <typename T>
-__device__ __forceinline__ void tile_column(const uint32_t (&tile)[8][kRunWords<T>], int j,
-                                            uint32_t (&out)[kRunWords<T>]) {
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = tile[2 * q][j >> 1], b = tile[2 * q + 1][j >> 1];
-      out[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) out[r] = tile[r][j];
-  }
-}
-
 template <typename T>
 __device__ __forceinline__ void lds_store_run(void* dst, const uint32_t (&w)[kRunWords<T>]) {
   store_words<kRunWords<T>>(dst, w);
 }
 
+// (batch, N, L) -> (batch, L, N) for B and C: the chunk products contract
+// over the state index, so their operands need it contiguous.  64 steps per
+// workgroup, through LDS.
 template <typename T, int N>
-__global__ __launch_bounds__(256, 1) void ssd_kernel(
+__global__ __launch_bounds__(256) void ssd_transpose_kernel(const T* __restrict__ B, const T* __restrict__ C,
+                                                            T* __restrict__ Bt, T* __restrict__ Ct,
+                                                            int64_t L, int tblocks) {
+  __shared__ T tile[N][65];
+  const int which = blockIdx.y;  // 0: B, 1: C
+  const T* src = which == 0 ? B : C;
+  T* dst = which == 0 ? Bt : Ct;
+  const int b = blockIdx.x / tblocks;
+  const int64_t t0 = (int64_t)(blockIdx.x % tblocks) * 64;
+  const T* sb = src + (int64_t)b * N * L;
+  T* db = dst + (int64_t)b * L * N;
+  for (int i = threadIdx.x; i < N * 64; i += 256) {
+    const int n = i / 64, tt = i % 64;
+    if (t0 + tt < L) tile[n][tt] = sb[(int64_t)n * L + t0 + tt];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < N * 64; i += 256) {
+    const int tt = i / N, n = i % N;
+    if (t0 + tt < L) db[(t0 + tt) * N + n] = tile[n][tt];
+  }
+}
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+// v from the lane that the DPP control CTRL names (0 where it names none, or
+// in rows that ROW_MASK leaves out).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_moved(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
+// 16 lanes, then the row totals carried forward by row broadcasts.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_moved<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_moved<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_moved<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_moved<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_moved<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_moved<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+template <typename T, int N, bool GATE>
+__global__ __launch_bounds__(256, 2) void ssd_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A_head,
-    const T* __restrict__ B, const T* __restrict__ C, const float* __restrict__ Dskip,
-    const T* __restrict__ z, const float* __restrict__ dt_bias, const float* __restrict__ h0,
-    T* __restrict__ y, float* __restrict__ last_state, const SsdSizes p) {
+    const T* __restrict__ B, const T* __restrict__ Bt, const T* __restrict__ Ct,
+    const float* __restrict__ Dskip, const T* __restrict__ z, const float* __restrict__ dt_bias,
+    const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ last_state,
+    const SsdSizes p) {
   using Op = typename Mma<T>::Op;
   static_assert(sizeof(Op) == sizeof(T), "operands keep the storage type");
   constexpr int Q = 64;            // chunk length
@@ -171,27 +215,37 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
   constexpr int KN = (N + Mma<T>::K - 1) / Mma<T>::K * Mma<T>::K;
   constexpr int LN = KN + PADK;    // row length of [.][KN] operand arrays
   constexpr int HT = N / 16;       // state tiles per wave
-  constexpr int XI = P * (Q / 8) / 256;        // runs of x (and z) per thread
+  constexpr int XI = P * (Q / 8) / 256;        // 8-step runs of x (and z, y) per thread
+  constexpr int NR = N * (Q / 8);              // 8-element runs of B (and of B^T, C^T) per chunk
+  constexpr int NI = (NR + 255) / 256;         // ... per thread
+  constexpr int YL = Q + 4;        // row length of the output staging [p][t]
   static_assert(N % 16 == 0 && N >= 16 && N <= 128, "state count");
   static_assert(P == Q && XI * 256 == P * (Q / 8), "staging layout");
 
+  // Item layouts: 8 consecutive lanes cover one 128-byte piece of a row in
+  // global memory and in LDS -- x, z, y runs (p = item / 8, steps
+  // 8 * (item % 8)..), B runs (n = item / 8, steps 8 * (item % 8)..) -- and
+  // B^T, C^T runs (step item / (N/8), states 8 * (item % (N/8))..) are whole
+  // contiguous rows.
   __shared__ __align__(16) Op sX[P][LQ];     // x chunk, [p][t]
   __shared__ __align__(16) Op sXw[P][LQ];    // x o exp(cum_Q - cum_s) Bbar_s, [p][s]
   __shared__ __align__(16) Op sB[N][LQ];     // B chunk, [n][s]
   __shared__ __align__(16) Op sCt[Q][LN];    // C^T, [t][n]
   // B^T, [s][n]; after the mask step, the output staging [p][t] (float)
   constexpr int BT_BYTES = (int)sizeof(Op) * Q * LN;
-  constexpr int Y_BYTES = (int)sizeof(float) * P * (Q + 4);
+  constexpr int Y_BYTES = (int)sizeof(float) * P * YL;
   __shared__ __align__(16) unsigned char sBtY[BT_BYTES > Y_BYTES ? BT_BYTES : Y_BYTES];
   __shared__ __align__(16) Op sM[Q][LQ];     // the masked chunk matrix, [t][s]
-  __shared__ float sCum[Q], sCoef[Q];
+  // per step of the chunk: cum2_t = log2 e * sum_{k<=t} Delta_k A and the input
+  // coefficient Bbar_t
+  __shared__ float sCum2[Q], sCoef[Q];
   Op(*sBt)[LN] = reinterpret_cast<Op(*)[LN]>(sBtY);
-  float(*sY)[Q + 4] = reinterpret_cast<float(*)[Q + 4]>(sBtY);
+  float(*sY)[YL] = reinterpret_cast<float(*)[YL]>(sBtY);
 
   const int b = blockIdx.x / p.nheads;
   const int h = blockIdx.x % p.nheads;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;          // wave: rows 16w.. of the chunk matrices
+  const int w = tid >> 6;          // wave: owns channels 16w..
   const int lane = tid & 63;
   const int64_t L = p.seqlen;
   const int dim = p.nheads * P;
@@ -200,18 +254,27 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
   const float rAh = 1.0f / Ah;
   const float bias_h = dt_bias != nullptr ? dt_bias[h] : 0.0f;
   const T* xh = x + ((int64_t)b * dim + (int64_t)h * P) * L;
-  const T* zh = z != nullptr ? z + ((int64_t)b * dim + (int64_t)h * P) * L : nullptr;
+  const T* zh = GATE ? z + ((int64_t)b * dim + (int64_t)h * P) * L : nullptr;
   T* yh = y + ((int64_t)b * dim + (int64_t)h * P) * L;
   const T* Bb = B + (int64_t)b * N * L;
-  const T* Cb = C + (int64_t)b * N * L;
+  const T* Btb = Bt + (int64_t)b * L * N;
+  const T* Ctb = Ct + (int64_t)b * L * N;
   const T* dth = dt + ((int64_t)b * p.nheads + h) * L;
 
   if constexpr (KN > N) {
     for (int i = tid; i < Q * (KN - N); i += 256) sCt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
   }
+  // the two tiles above the diagonal that the diagonal product reads (its K
+  // steps of 32 take rows 0..15 up to s < 32 and rows 32..47 up to s < 64)
+  // stay zero; the mask step writes only the causal tiles
+  for (int i = tid; i < 2 * 16 * 16; i += 256) {
+    const int which = i / 256, r = (i % 256) / 16, c = i % 16;
+    if (which == 0) sM[r][16 + c] = Mma<T>::cvt(0.0f);
+    else sM[32 + r][48 + c] = Mma<T>::cvt(0.0f);
+  }
 
-  // the state: wave w owns channels 16w..16w+15, as HT 16x16 tiles of states
-  // 16k..16k+15 (accumulator layout: lane l holds rows 4*(l/16)..+3, column l % 16)
+  // the state: wave w owns channels 16w..16w+15, as HT accumulator tiles
+  // (states 16k.., channels 16w..)
   f32x4_t H[HT];
 #pragma unroll
   for (int k = 0; k < HT; ++k) {
@@ -221,65 +284,80 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
       H[k][r] = h0 != nullptr ? h0[((int64_t)b * dim + h * P + pp) * N + n] : 0.0f;
     }
   }
+  float Dc[XI];  // the skip weight of each x run's channel
+#pragma unroll
+  for (int k = 0; k < XI; ++k) Dc[k] = Dskip != nullptr ? Dskip[h * P + (tid + 256 * k) / 8] : 0.0f;
 
-  // ---- staging roles ---------------------------------------------------------------
-  // x, z: runs (p = item / 8, steps 8 * (item % 8) ..) for item = tid + 256 k
-  // B, C: thread tid < 2N owns the 8 x 8 tile (states n0.., steps t8..) of B
-  //       (tid < N) or C (N <= tid < 2N)
-  const bool has_tile = tid < 2 * N;
-  const int tile_id = has_tile ? (tid < N ? tid : tid - N) : 0;
-  const int tn0 = (tile_id / 8) * 8, tt8 = (tile_id % 8) * 8;
-  const T* tsrc = (tid < N ? Bb : Cb) + (int64_t)tn0 * L + tt8;
-
-  uint32_t rx[XI][RW], rz[XI][RW], rt[8][RW];
-  float rdt = 0.0f;
-  auto prefetch = [&](int64_t c0) {
-    const int tv = (int)(L - c0 < Q ? L - c0 : Q);
-    const bool vec = p.vec && tv == Q;
+  // A chunk's inputs in registers.  Whole chunks (FULL) take straight vector
+  // loads and stores, so the only memory operations in flight across the
+  // loop are in program order; the ragged last chunk takes element accesses.
+  uint32_t rx[XI][RW], rz[XI][RW], rb[NI][RW], rbt[NI][RW], rct[NI][RW];
+  T rdt = T(0);  // raw: converted where it is used, so the load is not waited for early
+  auto load_chunk = [&](auto full_c, int64_t c0) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int tv = FULL ? Q : (int)(L - c0 < Q ? L - c0 : Q);
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
       const int item = tid + 256 * k;
-      const int t8 = (item % (Q / 8)) * 8;
-      load_run8<T>(xh + (int64_t)(item / (Q / 8)) * L + c0 + t8, vec, tv - t8, rx[k]);
+      const int t8 = 8 * (item % 8);
+      load_run8<T>(xh + (int64_t)(item / 8) * L + c0 + t8, FULL, tv - t8, rx[k]);
     }
-    if (has_tile) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) load_run8<T>(tsrc + (int64_t)r * L + c0, vec, tv - tt8, rt[r]);
+    for (int k = 0; k < NI; ++k) {
+      const int item = tid + 256 * k;
+      if (NR % 256 == 0 || item < NR) {
+        const int t8 = 8 * (item % 8);
+        load_run8<T>(Bb + (int64_t)(item / 8) * L + c0 + t8, FULL, tv - t8, rb[k]);
+        const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
+        const bool ok = FULL || t < tv;
+        load_run8<T>(Btb + (c0 + t) * N + n8, ok, 0, rbt[k]);  // the workspace rows are aligned
+        load_run8<T>(Ctb + (c0 + t) * N + n8, ok, 0, rct[k]);
+      }
     }
-    if (w == 0) rdt = lane < tv ? Elem<T>::load(dth + c0 + lane) : 0.0f;
+    rdt = (FULL || lane < tv) ? dth[c0 + lane] : T(0);
   };
-  prefetch(0);
+  auto load_gate = [&](auto full_c, int64_t c0) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int tv = FULL ? Q : (int)(L - c0 < Q ? L - c0 : Q);
+#pragma unroll
+    for (int k = 0; k < XI; ++k) {
+      const int item = tid + 256 * k;
+      const int t8 = 8 * (item % 8);
+      load_run8<T>(zh + (int64_t)(item / 8) * L + c0 + t8, FULL, tv - t8, rz[k]);
+    }
+  };
 
-  for (int64_t t0 = 0; t0 < L; t0 += Q) {
-    const int tvalid = (int)(L - t0 < Q ? L - t0 : Q);
-    const bool full = p.vec && tvalid == Q;
+  // One chunk at t0, its inputs (and z) already in registers.  A whole chunk
+  // also loads the inputs of the chunk at `next`, and after its output that
+  // chunk's z (the last whole chunk reloads its own: the loads stay
+  // unconditional).
+  auto chunk = [&](auto full_c, int64_t t0, int64_t next) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int tvalid = FULL ? Q : (int)(L - t0 < Q ? L - t0 : Q);
 
-    // ---- (1) this chunk's x, B, C into LDS; Delta and its prefix sum; H ---------------
+    // ---- (1) this chunk's x, B, B^T, C^T into LDS; Delta and its prefix sum -----------
     if constexpr (KN > N) {  // the output staging of the last chunk overwrote B^T's padding
       for (int i = tid; i < Q * (KN - N); i += 256) sBt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
     }
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
       const int item = tid + 256 * k;
-      lds_store_run<T>(&sX[item / (Q / 8)][(item % (Q / 8)) * 8], rx[k]);
+      lds_store_run<T>(&sX[item / 8][8 * (item % 8)], rx[k]);
     }
-    if (has_tile) {
-      Op(*dstT)[LN] = tid < N ? sBt : sCt;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t col[RW];
-        tile_column<T>(rt, j, col);
-        lds_store_run<T>(&dstT[tt8 + j][tn0], col);
-      }
-      if (tid < N) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) lds_store_run<T>(&sB[tn0 + r][tt8], rt[r]);
+    for (int k = 0; k < NI; ++k) {
+      const int item = tid + 256 * k;
+      if (NR % 256 == 0 || item < NR) {
+        lds_store_run<T>(&sB[item / 8][8 * (item % 8)], rb[k]);
+        const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
+        lds_store_run<T>(&sBt[t][n8], rbt[k]);
+        lds_store_run<T>(&sCt[t][n8], rct[k]);
       }
     }
     if (w == 0) {
       float dl = 0.0f, coef = 0.0f;
-      if (lane < tvalid) {
-        const float xr = rdt + bias_h;
+      if (FULL || lane < tvalid) {
+        const float xr = raw_value(rdt) + bias_h;
         dl = p.softplus ? softplus_f32(xr) : xr;
         if (p.zoh) {
           const float x2 = dl * A2h;
@@ -288,53 +366,40 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
           coef = dl;
         }
       }
-      float cum = dl * Ah;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(cum, off);
-        if (lane >= off) cum += o;
-      }
-      sCum[lane] = cum;
+      sCum2[lane] = wave_prefix_sum(dl * A2h);
       sCoef[lane] = coef;
     }
     __syncthreads();
 
-    // ---- (2) x o w, then the next chunk's loads and this chunk's z; the mask --------------
-    {
-      const float cumQ = sCum[Q - 1];
+    // ---- (2) x o w, then the next chunk's loads; the mask -------------------------------------
+    const float cum2Q = sCum2[Q - 1];
 #pragma unroll
-      for (int k = 0; k < XI; ++k) {
-        const int item = tid + 256 * k;
-        const int pp = item / (Q / 8), t8 = (item % (Q / 8)) * 8;
-        float v[8];
+    for (int k = 0; k < XI; ++k) {
+      const int item = tid + 256 * k;
+      const int pp = item / 8, t8 = 8 * (item % 8);
+      float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v[j] = run_elem<T>(rx[k], j) * (exp2_hw((cumQ - sCum[t8 + j]) * kLog2e) * sCoef[t8 + j]);
-        uint32_t wv[RW];
-        pack_floats<T, 8>(v, wv);
-        lds_store_run<T>(&sXw[pp][t8], wv);
-      }
+      for (int j = 0; j < 8; ++j)
+        v[j] = run_elem<T>(rx[k], j) * (exp2_hw(cum2Q - sCum2[t8 + j]) * sCoef[t8 + j]);
+      uint32_t wv[RW];
+      pack_floats<T, 8>(v, wv);
+      lds_store_run<T>(&sXw[pp][t8], wv);
     }
-    if (zh != nullptr) {
-#pragma unroll
-      for (int k = 0; k < XI; ++k) {
-        const int item = tid + 256 * k;
-        const int t8 = (item % (Q / 8)) * 8;
-        load_run8<T>(zh + (int64_t)(item / (Q / 8)) * L + t0 + t8, full, tvalid - t8, rz[k]);
-      }
-    }
-    if (t0 + Q < L) prefetch(t0 + Q);
+    if constexpr (FULL) load_chunk(full_c, next);
 
+    // the 10 causal 16x16 tiles (i, j <= i) dealt round-robin over the 4 waves
 #pragma unroll
-    for (int j = 0; j < Q / 16; ++j) {
+    for (int q = w; q < 10; q += 4) {
+      const int i = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+      const int j = q - i * (i + 1) / 2;
       f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (j <= w) g = tile_mma<T>(&sCt[0][0], LN, 16 * w, &sBt[0][0], LN, 16 * j, KN, lane, g);
+      g = tile_mma<T>(&sCt[0][0], LN, 16 * i, &sBt[0][0], LN, 16 * j, KN, lane, g);
       const int s = 16 * j + (lane & 15);
-      const float cs = sCum[s], bs = sCoef[s];
+      const float cs = sCum2[s], bs = sCoef[s];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * (lane >> 4) + r;
-        const float m = s <= t ? g[r] * exp2_hw((sCum[t] - cs) * kLog2e) * bs : 0.0f;
+        const int t = 16 * i + 4 * (lane >> 4) + r;
+        const float m = s <= t ? (g[r] * bs) * exp2_hw(sCum2[t] - cs) : 0.0f;
         sM[t][s] = Mma<T>::cvt(m);
       }
     }
@@ -342,26 +407,39 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
 
     // ---- (3) Y = M X^T + diag(exp(cum_t)) C^T H for this wave's channels, staged [p][t]
     //          (the staging reuses sBt: its last reads were in the mask step) ---------------
+    {
+      typename Mma<T>::AccB hb[HT];
 #pragma unroll
-    for (int i = 0; i < Q / 16; ++i) {
-      f32x4_t yd = {0.0f, 0.0f, 0.0f, 0.0f}, yo = {0.0f, 0.0f, 0.0f, 0.0f};
-      yd = tile_mma<T>(&sM[0][0], LQ, 16 * i, &sX[0][0], LQ, 16 * w, 16 * (i + 1), lane, yd);
+      for (int k = 0; k < HT; ++k) hb[k] = Mma<T>::pack_acc(H[k]);
 #pragma unroll
-      for (int k = 0; k < HT; ++k) yo = Mma<T>::mma_acc_b(&sCt[16 * i][16 * k], LN, H[k], yo, lane);
+      for (int i = 0; i < Q / 16; ++i) {
+        f32x4_t yd = {0.0f, 0.0f, 0.0f, 0.0f}, yo = {0.0f, 0.0f, 0.0f, 0.0f};
+        // diagonal part: t-block i needs s < 16 (i + 1)
+        yd = tile_mma<T>(&sM[0][0], LQ, 16 * i, &sX[0][0], LQ, 16 * w, 16 * (i + 1), lane, yd);
+        // the state entering the chunk
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * i + 4 * (lane >> 4) + r;
-        sY[16 * w + (lane & 15)][t] = __builtin_fmaf(exp2_hw(sCum[t] * kLog2e), yo[r], yd[r]);
+        for (int k = 0; k < HT; ++k) yo = Mma<T>::mma_acc_b(&sCt[16 * i][16 * k], LN, hb[k], yo, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * i + 4 * (lane >> 4) + r;
+          sY[16 * w + (lane & 15)][t] = __builtin_fmaf(exp2_hw(sCum2[t]), yo[r], yd[r]);
+        }
       }
     }
     // ---- H <- exp(cum_Q) H + B (x o w)^T ----------------------------------------------------
     {
-      const float decay = exp2_hw(sCum[Q - 1] * kLog2e);
+      const float decay = exp2_hw(cum2Q);
 #pragma unroll
       for (int k = 0; k < HT; ++k) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) H[k][r] *= decay;
-        H[k] = tile_mma<T>(&sB[0][0], LQ, 16 * k, &sXw[0][0], LQ, 16 * w, Q, lane, H[k]);
+      }
+      const int rr = lane & 15, kk = Mma<T>::KL * (lane >> 4);
+#pragma unroll
+      for (int k0 = 0; k0 < Q; k0 += Mma<T>::K) {
+        const Op* bx = &sXw[16 * w + rr][k0 + kk];
+#pragma unroll
+        for (int k = 0; k < HT; ++k) H[k] = Mma<T>::mma(&sB[16 * k + rr][k0 + kk], bx, H[k]);
       }
     }
     __syncthreads();
@@ -370,19 +448,18 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
       const int item = tid + 256 * k;
-      const int pp = item / (Q / 8), t8 = (item % (Q / 8)) * 8;
-      const float Dc = Dskip != nullptr ? Dskip[h * P + pp] : 0.0f;
+      const int pp = item / 8, t8 = 8 * (item % 8);
       uint32_t xw[RW];
       load_words<RW>(&sX[pp][t8], xw);
       float yv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float v = __builtin_fmaf(Dc, run_elem<T>(xw, j), sY[pp][t8 + j]);
-        if (zh != nullptr) v *= silu_f32(run_elem<T>(rz[k], j));
+        float v = __builtin_fmaf(Dc[k], run_elem<T>(xw, j), sY[pp][t8 + j]);
+        if constexpr (GATE) v *= silu_f32(run_elem<T>(rz[k], j));
         yv[j] = v;
       }
       const int64_t off = (int64_t)pp * L + t0 + t8;
-      if (full) {
+      if constexpr (FULL) {
         store_floats<T, 8>(yh + off, yv);
       } else {
 #pragma unroll
@@ -390,7 +467,21 @@ __global__ __launch_bounds__(256, 1) void ssd_kernel(
           if (t8 + j < tvalid) Elem<T>::store(yh + off + j, yv[j]);
       }
     }
+    if constexpr (FULL && GATE) load_gate(full_c, next);
     __syncthreads();
+  };
+
+  // whole chunks while the rows allow 16-byte accesses, then the rest
+  const int64_t nfull = p.vec ? L / Q : 0;
+  if (nfull > 0) {
+    load_chunk(BoolC<true>{}, 0);
+    if constexpr (GATE) load_gate(BoolC<true>{}, 0);
+  }
+  for (int64_t c = 0; c < nfull; ++c) chunk(BoolC<true>{}, c * Q, (c + 1 < nfull ? c + 1 : c) * Q);
+  for (int64_t t0 = nfull * Q; t0 < L; t0 += Q) {
+    load_chunk(BoolC<false>{}, t0);
+    if constexpr (GATE) load_gate(BoolC<false>{}, t0);
+    chunk(BoolC<false>{}, t0, t0);
   }
 
   if (last_state != nullptr) {
@@ -414,10 +505,16 @@ static hipError_t launch_ssd_n(const SsdLaunch& a, hipStream_t stream) {
   s.softplus = a.softplus;
   s.zoh = a.zoh;
   s.vec = a.vec;
-  ssd_kernel<T, N><<<(unsigned)(a.batch * a.nheads), 256, 0, stream>>>(
-      static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.A, static_cast<const T*>(a.B),
-      static_cast<const T*>(a.C), a.Dskip, static_cast<const T*>(a.z), a.dt_bias, a.h0,
-      static_cast<T*>(a.y), a.last_state, s);
+  T* Bt = static_cast<T*>(a.ws_bt);
+  T* Ct = Bt + (int64_t)a.batch * a.seqlen * N;
+  const int tblocks = (int)((a.seqlen + 63) / 64);
+  ssd_transpose_kernel<T, N><<<dim3((unsigned)(a.batch * tblocks), 2), 256, 0, stream>>>(
+      static_cast<const T*>(a.B), static_cast<const T*>(a.C), Bt, Ct, a.seqlen, tblocks);
+  auto kernel = a.z != nullptr ? ssd_kernel<T, N, true> : ssd_kernel<T, N, false>;
+  kernel<<<(unsigned)(a.batch * a.nheads), 256, 0, stream>>>(
+      static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.A, static_cast<const T*>(a.B), Bt,
+      Ct, a.Dskip, static_cast<const T*>(a.z), a.dt_bias, a.h0, static_cast<T*>(a.y),
+      a.last_state, s);
   return hipGetLastError();
 }
 

@@ -503,10 +503,17 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   return ssm::launch_scan_bwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+size_t ssm_ssd_scan_fwd_workspace_bytes(int batch, int dstate, int64_t seqlen, int dtype) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
+  if (batch <= 0 || seqlen <= 0 || dstate <= 0 || dstate > 128) return 0;
+  return round256(2 * (size_t)batch * (size_t)seqlen * (size_t)dstate * (size_t)elem_bytes(dtype));
+}
+
 int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const void* B,
                      const void* C, const float* D_skip, const void* z, const float* dt_bias,
                      int flags, const float* h0, void* y, float* last_state, int batch, int nheads,
-                     int headdim, int dstate, int64_t seqlen, int dtype, void* stream) {
+                     int headdim, int dstate, int64_t seqlen, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (batch < 0 || nheads < 0 || seqlen < 0) return SSM_ERR_SHAPE;
@@ -521,7 +528,7 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
   const size_t es = (size_t)elem_bytes(dtype);
   if (!aligned(x, es) || !aligned(dt, es) || !aligned(B, es) || !aligned(C, es) ||
       !aligned(z, es) || !aligned(y, es) || !aligned(A_head, 4) || !aligned(D_skip, 4) ||
-      !aligned(dt_bias, 4) || !aligned(h0, 4) || !aligned(last_state, 4))
+      !aligned(dt_bias, 4) || !aligned(h0, 4) || !aligned(last_state, 4) || !aligned(workspace, 256))
     return SSM_ERR_ALIGN;
   if (y != nullptr && (y == x || y == dt || (z != nullptr && y == z))) return SSM_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -532,6 +539,9 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
         ssm::launch_fill_state(last_state, h0, (int64_t)batch * nheads * headdim * dstate, st);
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
+  if ((int64_t)batch * ((seqlen + 63) / 64) > INT_MAX) return SSM_ERR_SHAPE;
+  if (workspace == nullptr || workspace_bytes < ssm_ssd_scan_fwd_workspace_bytes(batch, dstate, seqlen, dtype))
+    return SSM_ERR_WORKSPACE;
   ssm::SsdLaunch a{};
   a.x = x;
   a.dt = dt;
@@ -544,6 +554,7 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
   a.h0 = h0;
   a.y = y;
   a.last_state = last_state;
+  a.ws_bt = workspace;
   a.batch = batch;
   a.nheads = nheads;
   a.headdim = headdim;

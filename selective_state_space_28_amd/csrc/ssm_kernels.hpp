@@ -134,6 +134,7 @@ struct SsdLaunch {
   const float* h0;        // (batch, nheads * headdim, dstate) nullable
   void* y;
   float* last_state;      // nullable
+  void* ws_bt;            // B^T then C^T, (batch, seqlen, dstate) each, input type
   int batch, nheads, headdim, dstate;
   int64_t seqlen;
   int softplus, zoh, vec;

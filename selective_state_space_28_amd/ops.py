@@ -246,8 +246,12 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     return g
 
 
+def ssm_ssd_scan_fwd_workspace_bytes(batch: int, dstate: int, seqlen: int, dtype: torch.dtype) -> int:
+    return int(load().ssm_ssd_scan_fwd_workspace_bytes(batch, dstate, seqlen, _DTYPES[dtype]))
+
+
 def ssm_ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, delta_softplus=True, h0=None, *,
-                     bbar="euler", return_last_state=False, out=None):
+                     bbar="euler", return_last_state=False, out=None, workspace=None):
     """The SSD (scalar A per head) scan on the matrix cores; see include/ssm.h.
     x, z: (batch, nheads * 64, L); dt: (batch, nheads, L); A, dt_bias:
     (nheads,) float32; B, C: (batch, N, L); D: (dim,) float32; h0:
@@ -276,10 +280,18 @@ def ssm_ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, delta_softplu
     y = out if out is not None else torch.empty_like(x)
     _check("out", y, (batch, dim, L), dtp, dev)
     last = torch.empty((batch, dim, N), dtype=torch.float32, device=dev) if return_last_state else None
+    need = int(lib.ssm_ssd_scan_fwd_workspace_bytes(batch, N, L, code))
+    ws_bytes = 0
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.ssm_ssd_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                               _ptr(dt_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(y),
-                              _ptr(last), batch, H, P, N, L, code, stream)
+                              _ptr(last), batch, H, P, N, L, code, _ptr(workspace), ws_bytes, stream)
     if rc != 0:
         raise SsmError(rc, "ssm_ssd_scan_fwd")
     return (y, last) if return_last_state else y

@@ -15,7 +15,8 @@ def test_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) == {"ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
                           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_scan_bwd_workspace_bytes",
-                          "ssm_scan_bwd", "ssm_ssd_scan_fwd", "ssm_status_string"}
+                          "ssm_scan_bwd", "ssm_ssd_scan_fwd", "ssm_ssd_scan_fwd_workspace_bytes",
+                          "ssm_status_string"}
     lib = ctypes.CDLL(load()._name)
     for n in names:
         assert hasattr(lib, n), n
@@ -209,11 +210,11 @@ def test_bwd_workspace_query_and_check():
 def _ssd(**kw):
     a = dict(x=P, dt=P + 0x10000, A=P + 0x20000, B=P + 0x30000, C=P + 0x40000, D=None, z=None,
              bias=None, fl=1, h0=None, y=P + 0x50000, last=None, batch=1, H=4, hd=64, N=128, L=2048,
-             dtype=1, stream=None)
+             dtype=1, ws=P + 0x1000000, wsb=1 << 24, stream=None)
     a.update(kw)
     return load().ssm_ssd_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
                                    a["fl"], a["h0"], a["y"], a["last"], a["batch"], a["H"], a["hd"],
-                                   a["N"], a["L"], a["dtype"], a["stream"])
+                                   a["N"], a["L"], a["dtype"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -221,9 +222,17 @@ def _ssd(**kw):
     (dict(H=-1), SHAPE), (dict(L=-1), SHAPE), (dict(dtype=4), DTYPE), (dict(fl=8), FLAGS),
     (dict(x=None), NULL), (dict(dt=None), NULL), (dict(A=None), NULL), (dict(y=None), NULL),
     (dict(x=P + 1), ALIGN), (dict(A=P + 0x20002), ALIGN), (dict(y=P), ALIAS),
+    (dict(ws=P + 0x1000010), ALIGN), (dict(ws=None), WS), (dict(wsb=1000), WS),
 ])
 def test_ssd_validation(kw, code):
     assert _ssd(**kw) == code
+
+
+def test_ssd_workspace_query():
+    lib = load()
+    assert lib.ssm_ssd_scan_fwd_workspace_bytes(2, 128, 2048, 1) == 2 * 2 * 2048 * 128 * 2
+    assert lib.ssm_ssd_scan_fwd_workspace_bytes(1, 64, 100, 0) == (2 * 100 * 64 * 4 + 255) // 256 * 256
+    assert lib.ssm_ssd_scan_fwd_workspace_bytes(0, 64, 100, 0) == 0
 
 
 def test_ssd_empty_needs_no_gpu():
