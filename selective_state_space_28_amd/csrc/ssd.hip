@@ -44,21 +44,31 @@ struct Mma<uint16_t> {  // bf16 storage: bf16 operands, v_mfma_f32_16x16x32_bf16
                                                    0);
   }
   __device__ static Op cvt(float v) { return (__bf16)v; }
-  // acc += A (16 x 16, rows of a [.][lda] array at a, k contiguous) times a
-  // 16x16 tile held in accumulator layout (lane l: rows 4*(l/16)..+3, column
-  // l % 16): v_mfma_f32_16x16x16_bf16 takes exactly that layout as its B
-  // operand (4 consecutive k per lane).
-  typedef short s16x4_t __attribute__((ext_vector_type(4)));
-  using AccB = s16x4_t;  // an accumulator tile as a B operand
-  __device__ static AccB pack_acc(f32x4_t t) {
-    AccB bv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = __builtin_bit_cast(short, (__bf16)t[j]);
-    return bv;
+  // Products with the state H (N x 16 channels, held as 16x16 accumulator
+  // tiles: lane l has states 16k + 4*(l/16) + i, channel l % 16) contract over
+  // the state index.  One instruction takes 32 states as K: lane l's 8 B
+  // values are its accumulator rows of two tiles (states 32m + 4*(l/16) + i
+  // and 32m + 16 + 4*(l/16) + i), so the A operand (C^T, B^T) is staged in LDS
+  // with the states of each 32-block in that order: state_pos(n).
+  static constexpr int kPackStates = 32;
+  __device__ static int state_pos(int n) {
+    const int q = n & 31;
+    return (n & ~31) + 8 * ((q & 15) >> 2) + 4 * (q >> 4) + (q & 3);
   }
-  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, AccB bv, f32x4_t acc, int lane) {
-    const s16x4_t av = *reinterpret_cast<const s16x4_t*>(a + (lane & 15) * lda + 4 * (lane >> 4));
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+  using StatePack = bf16x8_t;
+  __device__ static StatePack pack_state(f32x4_t lo, f32x4_t hi) {
+    StatePack v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] = (__bf16)lo[j];
+      v[4 + j] = (__bf16)hi[j];
+    }
+    return v;
+  }
+  // acc += A (16 rows of a [.][lda] array at a, 32 staged states) times the pack
+  __device__ static f32x4_t mma_state(const Op* a, int lda, StatePack b, f32x4_t acc, int lane) {
+    const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(a + (lane & 15) * lda + 8 * (lane >> 4));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b, acc, 0, 0, 0);
   }
 };
 
@@ -71,15 +81,18 @@ struct Mma<float> {  // fp32 storage: fp32 operands, v_mfma_f32_16x16x4_f32
     return __builtin_amdgcn_mfma_f32_16x16x4f32(*a, *b, c, 0, 0, 0);
   }
   __device__ static Op cvt(float v) { return v; }
-  // as for bf16, with four K = 4 products: the r-th takes k = 4 * (l/16) + r
-  // from each lane's own accumulator element r
-  using AccB = f32x4_t;
-  __device__ static AccB pack_acc(f32x4_t t) { return t; }
-  __device__ static f32x4_t mma_acc_b(const Op* a, int lda, AccB btile, f32x4_t acc, int lane) {
+  // products with the state: one 16-state tile per pack, states in natural
+  // order, as four K = 4 products (the r-th takes state 4 * (l/16) + r from
+  // each lane's own accumulator element r)
+  static constexpr int kPackStates = 16;
+  __device__ static int state_pos(int n) { return n; }
+  using StatePack = f32x4_t;
+  __device__ static StatePack pack_state(f32x4_t lo, f32x4_t) { return lo; }
+  __device__ static f32x4_t mma_state(const Op* a, int lda, StatePack b, f32x4_t acc, int lane) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(lane & 15) * lda + 4 * (lane >> 4) + r], btile[r],
-                                                  acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[(lane & 15) * lda + 4 * (lane >> 4) + r], b[r], acc, 0,
+                                                  0, 0);
     return acc;
   }
 };
@@ -146,6 +159,25 @@ __device__ __forceinline__ void lds_store_run(void* dst, const uint32_t (&w)[kRu
   store_words<kRunWords<T>>(dst, w);
 }
 
+// A run of 8 consecutive states (n8..n8+7, n8 a multiple of 8) into a row of
+// state-staged operands: bf16 splits it into two 4-state pieces.
+template <typename T>
+__device__ __forceinline__ void lds_store_states(typename Mma<T>::Op* row, int n8,
+                                                 const uint32_t (&w)[kRunWords<T>]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t lo[2] = {w[0], w[1]}, hi[2] = {w[2], w[3]};
+    store_words<2>(row + Mma<T>::state_pos(n8), lo);
+    store_words<2>(row + Mma<T>::state_pos(n8 + 4), hi);
+  } else {
+    store_words<kRunWords<T>>(row + n8, w);
+  }
+}
+
+// Column of step t in a row of the output staging: the second half of the
+// row is shifted by 4, so 8 lanes reading 8-step runs of one row, and 8 lanes
+// writing 4-step runs of 8 rows, each touch all 32 banks once.
+__device__ __forceinline__ int ystage_col(int t) { return t + ((t >> 5) << 2); }
+
 // (batch, N, L) -> (batch, L, N) for B and C: the chunk products contract
 // over the state index, so their operands need it contiguous.  64 steps per
 // workgroup, through LDS.
@@ -211,8 +243,12 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   constexpr int PADK = 16 / (int)sizeof(Op);   // one 16-byte pad per row
   constexpr int LQ = Q + PADK;     // row length of [.][Q] operand arrays
   // the state index as a product dimension, rounded up to the instruction's K
-  // (columns N .. KN-1 of the [.][KN] arrays stay zero)
+  // (the staged positions of states N .. KN-1 of the [.][KN] arrays stay zero)
   constexpr int KN = (N + Mma<T>::K - 1) / Mma<T>::K * Mma<T>::K;
+  constexpr int PS = Mma<T>::kPackStates;
+  constexpr int NPK = (N + PS - 1) / PS;       // state packs (products with H)
+  constexpr int TPP = PS / 16;                 // state tiles per pack
+  static_assert(KN % PS == 0, "packs cover the staged states");
   constexpr int LN = KN + PADK;    // row length of [.][KN] operand arrays
   constexpr int HT = N / 16;       // state tiles per wave
   constexpr int XI = P * (Q / 8) / 256;        // 8-step runs of x (and z, y) per thread
@@ -238,7 +274,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   __shared__ __align__(16) Op sM[Q][LQ];     // the masked chunk matrix, [t][s]
   // per step of the chunk: cum2_t = log2 e * sum_{k<=t} Delta_k A and the input
   // coefficient Bbar_t
-  __shared__ float sCum2[Q], sCoef[Q];
+  __shared__ __align__(16) float sCum2[Q];
+  __shared__ __align__(16) float sCoef[Q];
   Op(*sBt)[LN] = reinterpret_cast<Op(*)[LN]>(sBtY);
   float(*sY)[YL] = reinterpret_cast<float(*)[YL]>(sBtY);
 
@@ -262,7 +299,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   const T* dth = dt + ((int64_t)b * p.nheads + h) * L;
 
   if constexpr (KN > N) {
-    for (int i = tid; i < Q * (KN - N); i += 256) sCt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
+    for (int i = tid; i < Q * (KN - N); i += 256)
+      sCt[i / (KN - N)][Mma<T>::state_pos(N + i % (KN - N))] = Mma<T>::cvt(0.0f);
   }
   // the two tiles above the diagonal that the diagonal product reads (its K
   // steps of 32 take rows 0..15 up to s < 32 and rows 32..47 up to s < 64)
@@ -337,7 +375,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
 
     // ---- (1) this chunk's x, B, B^T, C^T into LDS; Delta and its prefix sum -----------
     if constexpr (KN > N) {  // the output staging of the last chunk overwrote B^T's padding
-      for (int i = tid; i < Q * (KN - N); i += 256) sBt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
+      for (int i = tid; i < Q * (KN - N); i += 256)
+        sBt[i / (KN - N)][Mma<T>::state_pos(N + i % (KN - N))] = Mma<T>::cvt(0.0f);
     }
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
@@ -350,8 +389,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       if (NR % 256 == 0 || item < NR) {
         lds_store_run<T>(&sB[item / 8][8 * (item % 8)], rb[k]);
         const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
-        lds_store_run<T>(&sBt[t][n8], rbt[k]);
-        lds_store_run<T>(&sCt[t][n8], rct[k]);
+        lds_store_states<T>(&sBt[t][0], n8, rbt[k]);
+        lds_store_states<T>(&sCt[t][0], n8, rct[k]);
       }
     }
     if (w == 0) {
@@ -387,43 +426,52 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     }
     if constexpr (FULL) load_chunk(full_c, next);
 
-    // the 10 causal 16x16 tiles (i, j <= i) dealt round-robin over the 4 waves
+    // the 10 causal 16x16 tiles (t-block i, s-block j <= i) dealt round-robin
+    // over the 4 waves, each formed transposed (B^T C) so that a lane holds 4
+    // consecutive s of one t and writes them at once
 #pragma unroll
     for (int q = w; q < 10; q += 4) {
       const int i = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
       const int j = q - i * (i + 1) / 2;
       f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
-      g = tile_mma<T>(&sCt[0][0], LN, 16 * i, &sBt[0][0], LN, 16 * j, KN, lane, g);
-      const int s = 16 * j + (lane & 15);
-      const float cs = sCum2[s], bs = sCoef[s];
+      g = tile_mma<T>(&sBt[0][0], LN, 16 * j, &sCt[0][0], LN, 16 * i, KN, lane, g);
+      const int t = 16 * i + (lane & 15), s0 = 16 * j + 4 * (lane >> 4);
+      const float ct = sCum2[t];
+      const float4 cs = *reinterpret_cast<const float4*>(&sCum2[s0]);
+      const float4 bs = *reinterpret_cast<const float4*>(&sCoef[s0]);
+      const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
+      float mv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * i + 4 * (lane >> 4) + r;
-        const float m = s <= t ? (g[r] * bs) * exp2_hw(sCum2[t] - cs) : 0.0f;
-        sM[t][s] = Mma<T>::cvt(m);
-      }
+      for (int r = 0; r < 4; ++r) mv[r] = s0 + r <= t ? (g[r] * bsv[r]) * exp2_hw(ct - csv[r]) : 0.0f;
+      uint32_t wv[4 * sizeof(T) / 4];
+      pack_floats<T, 4>(mv, wv);
+      store_words<4 * sizeof(T) / 4>(&sM[t][s0], wv);
     }
     __syncthreads();
 
     // ---- (3) Y = M X^T + diag(exp(cum_t)) C^T H for this wave's channels, staged [p][t]
     //          (the staging reuses sBt: its last reads were in the mask step) ---------------
     {
-      typename Mma<T>::AccB hb[HT];
+      typename Mma<T>::StatePack hp[NPK];
+      const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k = 0; k < HT; ++k) hb[k] = Mma<T>::pack_acc(H[k]);
+      for (int m = 0; m < NPK; ++m) {
+        const int k1 = TPP * m + 1 < HT ? TPP * m + 1 : HT - 1;
+        hp[m] = Mma<T>::pack_state(H[TPP * m], TPP * m + 1 < HT ? H[k1] : zero);
+      }
 #pragma unroll
       for (int i = 0; i < Q / 16; ++i) {
-        f32x4_t yd = {0.0f, 0.0f, 0.0f, 0.0f}, yo = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4_t yd = zero, yo = zero;
         // diagonal part: t-block i needs s < 16 (i + 1)
         yd = tile_mma<T>(&sM[0][0], LQ, 16 * i, &sX[0][0], LQ, 16 * w, 16 * (i + 1), lane, yd);
         // the state entering the chunk
 #pragma unroll
-        for (int k = 0; k < HT; ++k) yo = Mma<T>::mma_acc_b(&sCt[16 * i][16 * k], LN, hb[k], yo, lane);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * i + 4 * (lane >> 4) + r;
-          sY[16 * w + (lane & 15)][t] = __builtin_fmaf(exp2_hw(sCum2[t]), yo[r], yd[r]);
-        }
+        for (int m = 0; m < NPK; ++m) yo = Mma<T>::mma_state(&sCt[16 * i][PS * m], LN, hp[m], yo, lane);
+        const int t0 = 16 * i + 4 * (lane >> 4);
+        const float4 e = *reinterpret_cast<const float4*>(&sCum2[t0]);
+        *reinterpret_cast<float4*>(&sY[16 * w + (lane & 15)][ystage_col(t0)]) =
+            make_float4(__builtin_fmaf(exp2_hw(e.x), yo[0], yd[0]), __builtin_fmaf(exp2_hw(e.y), yo[1], yd[1]),
+                        __builtin_fmaf(exp2_hw(e.z), yo[2], yd[2]), __builtin_fmaf(exp2_hw(e.w), yo[3], yd[3]));
       }
     }
     // ---- H <- exp(cum_Q) H + B (x o w)^T ----------------------------------------------------
@@ -454,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       float yv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float v = __builtin_fmaf(Dc[k], run_elem<T>(xw, j), sY[pp][t8 + j]);
+        float v = __builtin_fmaf(Dc[k], run_elem<T>(xw, j), sY[pp][ystage_col(t8) + j]);
         if constexpr (GATE) v *= silu_f32(run_elem<T>(rz[k], j));
         yv[j] = v;
       }
