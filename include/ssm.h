@@ -273,8 +273,9 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
  *   h0, last_state (batch, nheads*headdim, dstate) float32   NULL -> zero start / not written
  *   headdim must be 64; dstate in {16, 32, 64, 128} (128 for SSM_BF16 only).
  *   workspace      at least ssm_ssd_scan_fwd_workspace_bytes(...) bytes, 256-byte
- *                  aligned, owned by the caller (B and C with the state index
- *                  contiguous, rewritten by every call)
+ *                  aligned, owned by the caller (C with the state index
+ *                  contiguous and, per 64-step chunk, the causal tiles of
+ *                  C^T B, which all heads share; rewritten by every call)
  * bf16 storage feeds the matrix cores bf16 operands: the chunk matrix, the
  * decayed x and the state are rounded to bf16 for the products, which are
  * accumulated in float32; the state itself is carried in float32.
@@ -286,8 +287,10 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
                      int headdim, int dstate, int64_t seqlen, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
 
-/* ssm_ssd_scan_fwd_workspace_bytes -- 2 * batch * seqlen * dstate elements of
- * dtype, rounded up to 256 bytes; 0 for an empty problem.  Pure host function. */
+/* ssm_ssd_scan_fwd_workspace_bytes -- batch * seqlen * dstate elements of
+ * dtype rounded up to 256 bytes, plus 40 KiB (10 tiles of 16 x 16 float32)
+ * per batch row and 64-step chunk; 0 for an empty problem.  Pure host
+ * function. */
 size_t ssm_ssd_scan_fwd_workspace_bytes(int batch, int dstate, int64_t seqlen, int dtype);
 
 /* ssm_status_string -- a static, human-readable name for a status code. */

@@ -178,29 +178,57 @@ __device__ __forceinline__ void lds_store_states(typename Mma<T>::Op* row, int n
 // writing 4-step runs of 8 rows, each touch all 32 banks once.
 __device__ __forceinline__ int ystage_col(int t) { return t + ((t >> 5) << 2); }
 
-// (batch, N, L) -> (batch, L, N) for B and C: the chunk products contract
-// over the state index, so their operands need it contiguous.  64 steps per
-// workgroup, through LDS.
+// A raw element of T as a matrix-core operand.
+__device__ __forceinline__ __bf16 as_operand(uint16_t v) { return __builtin_bit_cast(__bf16, v); }
+__device__ __forceinline__ float as_operand(float v) { return v; }
+
+// The 10 causal 16x16 tiles (t-block i, s-block j <= i) of a 64-step chunk
+// matrix, numbered row by row: tile q has i = the largest with i(i+1)/2 <= q.
+__device__ __forceinline__ int causal_tile_row(int q) { return q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3; }
+
+// Per (batch row, chunk of 64 steps): C^T with the state index contiguous,
+// (batch, L, N), for the products with the state, and the chunk's causal
+// tiles of G = C^T B (G[t][s] = C_t . B_s), which do not depend on the head:
+// formed once here for every head of the row.  Tile q is stored as 64 lanes x
+// 4 floats, lane l holding G[16i + l % 16][16j + 4 (l / 16) + r], r < 4 -- the
+// order in which the scan's lanes use it.
 template <typename T, int N>
-__global__ __launch_bounds__(256) void ssd_transpose_kernel(const T* __restrict__ B, const T* __restrict__ C,
-                                                            T* __restrict__ Bt, T* __restrict__ Ct,
-                                                            int64_t L, int tblocks) {
-  __shared__ T tile[N][65];
-  const int which = blockIdx.y;  // 0: B, 1: C
-  const T* src = which == 0 ? B : C;
-  T* dst = which == 0 ? Bt : Ct;
-  const int b = blockIdx.x / tblocks;
-  const int64_t t0 = (int64_t)(blockIdx.x % tblocks) * 64;
-  const T* sb = src + (int64_t)b * N * L;
-  T* db = dst + (int64_t)b * L * N;
-  for (int i = threadIdx.x; i < N * 64; i += 256) {
+__global__ __launch_bounds__(256) void ssd_prep_kernel(const T* __restrict__ B, const T* __restrict__ C,
+                                                       T* __restrict__ Ct, float4* __restrict__ G,
+                                                       int64_t L, int nchunks) {
+  using Op = typename Mma<T>::Op;
+  constexpr int KN = (N + Mma<T>::K - 1) / Mma<T>::K * Mma<T>::K;
+  constexpr int LN = KN + 16 / (int)sizeof(Op);
+  __shared__ __align__(16) Op sBt[64][LN];   // [s][n]
+  __shared__ __align__(16) Op sCt[64][LN];   // [t][n]
+  const int b = blockIdx.x / nchunks;
+  const int c = blockIdx.x % nchunks;
+  const int64_t t0 = (int64_t)c * 64;
+  const T* Bb = B + (int64_t)b * N * L;
+  const T* Cb = C + (int64_t)b * N * L;
+  for (int i = threadIdx.x; i < KN * 64; i += 256) {
     const int n = i / 64, tt = i % 64;
-    if (t0 + tt < L) tile[n][tt] = sb[(int64_t)n * L + t0 + tt];
+    const bool ok = n < N && t0 + tt < L;  // zeros past the sequence and past N
+    sBt[tt][n] = ok ? as_operand(Bb[(int64_t)n * L + t0 + tt]) : Mma<T>::cvt(0.0f);
+    sCt[tt][n] = ok ? as_operand(Cb[(int64_t)n * L + t0 + tt]) : Mma<T>::cvt(0.0f);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < N * 64; i += 256) {
-    const int tt = i / N, n = i % N;
-    if (t0 + tt < L) db[(t0 + tt) * N + n] = tile[n][tt];
+  constexpr int RW = kRunWords<T>;
+  T* Ctb = Ct + ((int64_t)b * L + t0) * N;
+  for (int i = threadIdx.x; i < 64 * (N / 8); i += 256) {
+    const int tt = i / (N / 8), n8 = 8 * (i % (N / 8));
+    if (t0 + tt < L) {
+      uint32_t w[RW];
+      load_words<RW>(&sCt[tt][n8], w);
+      store_words<RW>(Ctb + (int64_t)tt * N + n8, w);
+    }
+  }
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int q = w; q < 10; q += 4) {
+    const int i = causal_tile_row(q), j = q - i * (i + 1) / 2;
+    f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
+    g = tile_mma<T>(&sBt[0][0], LN, 16 * j, &sCt[0][0], LN, 16 * i, KN, lane, g);
+    G[(((int64_t)b * nchunks + c) * 10 + q) * 64 + lane] = make_float4(g[0], g[1], g[2], g[3]);
   }
 }
 
@@ -231,7 +259,7 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
 template <typename T, int N, bool GATE>
 __global__ __launch_bounds__(256, 2) void ssd_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A_head,
-    const T* __restrict__ B, const T* __restrict__ Bt, const T* __restrict__ Ct,
+    const T* __restrict__ B, const float4* __restrict__ G, const T* __restrict__ Ct,
     const float* __restrict__ Dskip, const T* __restrict__ z, const float* __restrict__ dt_bias,
     const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ last_state,
     const SsdSizes p) {
@@ -267,22 +295,17 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   __shared__ __align__(16) Op sXw[P][LQ];    // x o exp(cum_Q - cum_s) Bbar_s, [p][s]
   __shared__ __align__(16) Op sB[N][LQ];     // B chunk, [n][s]
   __shared__ __align__(16) Op sCt[Q][LN];    // C^T, [t][n]
-  // B^T, [s][n]; after the mask step, the output staging [p][t] (float)
-  constexpr int BT_BYTES = (int)sizeof(Op) * Q * LN;
-  constexpr int Y_BYTES = (int)sizeof(float) * P * YL;
-  __shared__ __align__(16) unsigned char sBtY[BT_BYTES > Y_BYTES ? BT_BYTES : Y_BYTES];
+  __shared__ __align__(16) float sY[P][YL]; // the output staging, [p][t] (columns ystage_col(t))
   __shared__ __align__(16) Op sM[Q][LQ];     // the masked chunk matrix, [t][s]
   // per step of the chunk: cum2_t = log2 e * sum_{k<=t} Delta_k A and the input
   // coefficient Bbar_t
   __shared__ __align__(16) float sCum2[Q];
   __shared__ __align__(16) float sCoef[Q];
-  Op(*sBt)[LN] = reinterpret_cast<Op(*)[LN]>(sBtY);
-  float(*sY)[YL] = reinterpret_cast<float(*)[YL]>(sBtY);
 
   const int b = blockIdx.x / p.nheads;
   const int h = blockIdx.x % p.nheads;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;          // wave: owns channels 16w..
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave: owns channels 16w..
   const int lane = tid & 63;
   const int64_t L = p.seqlen;
   const int dim = p.nheads * P;
@@ -294,7 +317,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   const T* zh = GATE ? z + ((int64_t)b * dim + (int64_t)h * P) * L : nullptr;
   T* yh = y + ((int64_t)b * dim + (int64_t)h * P) * L;
   const T* Bb = B + (int64_t)b * N * L;
-  const T* Btb = Bt + (int64_t)b * L * N;
+  const int nchunks = (int)((L + Q - 1) / Q);
+  const float4* Gb = G + (int64_t)b * nchunks * 10 * 64;
   const T* Ctb = Ct + (int64_t)b * L * N;
   const T* dth = dt + ((int64_t)b * p.nheads + h) * L;
 
@@ -329,7 +353,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   // A chunk's inputs in registers.  Whole chunks (FULL) take straight vector
   // loads and stores, so the only memory operations in flight across the
   // loop are in program order; the ragged last chunk takes element accesses.
-  uint32_t rx[XI][RW], rz[XI][RW], rb[NI][RW], rbt[NI][RW], rct[NI][RW];
+  uint32_t rx[XI][RW], rz[XI][RW], rb[NI][RW], rct[NI][RW];
+  float4 rg[3];  // this wave's causal tiles of G (tiles w, w + 4, w + 8 < 10)
   T rdt = T(0);  // raw: converted where it is used, so the load is not waited for early
   auto load_chunk = [&](auto full_c, int64_t c0) {
     constexpr bool FULL = decltype(full_c)::value;
@@ -348,10 +373,12 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         load_run8<T>(Bb + (int64_t)(item / 8) * L + c0 + t8, FULL, tv - t8, rb[k]);
         const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
         const bool ok = FULL || t < tv;
-        load_run8<T>(Btb + (c0 + t) * N + n8, ok, 0, rbt[k]);  // the workspace rows are aligned
-        load_run8<T>(Ctb + (c0 + t) * N + n8, ok, 0, rct[k]);
+        load_run8<T>(Ctb + (c0 + t) * N + n8, ok, 0, rct[k]);  // the workspace rows are aligned
       }
     }
+    const float4* Gc = Gb + (c0 / Q) * 10 * 64;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) rg[k] = Gc[(w + 4 * k < 10 ? w + 4 * k : 9) * 64 + lane];
     rdt = (FULL || lane < tv) ? dth[c0 + lane] : T(0);
   };
   auto load_gate = [&](auto full_c, int64_t c0) {
@@ -373,11 +400,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     constexpr bool FULL = decltype(full_c)::value;
     const int tvalid = FULL ? Q : (int)(L - t0 < Q ? L - t0 : Q);
 
-    // ---- (1) this chunk's x, B, B^T, C^T into LDS; Delta and its prefix sum -----------
-    if constexpr (KN > N) {  // the output staging of the last chunk overwrote B^T's padding
-      for (int i = tid; i < Q * (KN - N); i += 256)
-        sBt[i / (KN - N)][Mma<T>::state_pos(N + i % (KN - N))] = Mma<T>::cvt(0.0f);
-    }
+    // ---- (1) this chunk's x, B, C^T into LDS; Delta and its prefix sum ------------------
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
       const int item = tid + 256 * k;
@@ -389,7 +412,6 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       if (NR % 256 == 0 || item < NR) {
         lds_store_run<T>(&sB[item / 8][8 * (item % 8)], rb[k]);
         const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
-        lds_store_states<T>(&sBt[t][0], n8, rbt[k]);
         lds_store_states<T>(&sCt[t][0], n8, rct[k]);
       }
     }
@@ -410,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     }
     __syncthreads();
 
-    // ---- (2) x o w, then the next chunk's loads; the mask -------------------------------------
+    // ---- (2) x o w; the mask; then the next chunk's loads ------------------------------------
     const float cum2Q = sCum2[Q - 1];
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
@@ -424,17 +446,16 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       pack_floats<T, 8>(v, wv);
       lds_store_run<T>(&sXw[pp][t8], wv);
     }
-    if constexpr (FULL) load_chunk(full_c, next);
 
     // the 10 causal 16x16 tiles (t-block i, s-block j <= i) dealt round-robin
-    // over the 4 waves, each formed transposed (B^T C) so that a lane holds 4
-    // consecutive s of one t and writes them at once
+    // over the 4 waves; a lane holds 4 consecutive s of one t and writes them
+    // at once
 #pragma unroll
-    for (int q = w; q < 10; q += 4) {
-      const int i = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
-      const int j = q - i * (i + 1) / 2;
-      f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
-      g = tile_mma<T>(&sBt[0][0], LN, 16 * j, &sCt[0][0], LN, 16 * i, KN, lane, g);
+    for (int k = 0; k < 3; ++k) {
+      const int q = w + 4 * k;
+      if (q >= 10) break;
+      const int i = causal_tile_row(q), j = q - i * (i + 1) / 2;
+      const float gv[4] = {rg[k].x, rg[k].y, rg[k].z, rg[k].w};
       const int t = 16 * i + (lane & 15), s0 = 16 * j + 4 * (lane >> 4);
       const float ct = sCum2[t];
       const float4 cs = *reinterpret_cast<const float4*>(&sCum2[s0]);
@@ -442,15 +463,17 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
       float mv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mv[r] = s0 + r <= t ? (g[r] * bsv[r]) * exp2_hw(ct - csv[r]) : 0.0f;
+      for (int r = 0; r < 4; ++r) mv[r] = s0 + r <= t ? (gv[r] * bsv[r]) * exp2_hw(ct - csv[r]) : 0.0f;
       uint32_t wv[4 * sizeof(T) / 4];
       pack_floats<T, 4>(mv, wv);
       store_words<4 * sizeof(T) / 4>(&sM[t][s0], wv);
     }
+    // the next chunk's loads (after the last use of this chunk's G tiles)
+    if constexpr (FULL) load_chunk(full_c, next);
     __syncthreads();
 
     // ---- (3) Y = M X^T + diag(exp(cum_t)) C^T H for this wave's channels, staged [p][t]
-    //          (the staging reuses sBt: its last reads were in the mask step) ---------------
+    // ----------------------------------------------------------------------------------
     {
       typename Mma<T>::StatePack hp[NPK];
       const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -553,14 +576,15 @@ static hipError_t launch_ssd_n(const SsdLaunch& a, hipStream_t stream) {
   s.softplus = a.softplus;
   s.zoh = a.zoh;
   s.vec = a.vec;
-  T* Bt = static_cast<T*>(a.ws_bt);
-  T* Ct = Bt + (int64_t)a.batch * a.seqlen * N;
-  const int tblocks = (int)((a.seqlen + 63) / 64);
-  ssd_transpose_kernel<T, N><<<dim3((unsigned)(a.batch * tblocks), 2), 256, 0, stream>>>(
-      static_cast<const T*>(a.B), static_cast<const T*>(a.C), Bt, Ct, a.seqlen, tblocks);
+  const int nchunks = (int)((a.seqlen + 63) / 64);
+  T* Ct = static_cast<T*>(a.ws);
+  float4* G = reinterpret_cast<float4*>(static_cast<char*>(a.ws) +
+                                        ssd_ws_ct_bytes(a.batch, N, a.seqlen, (int)sizeof(T)));
+  ssd_prep_kernel<T, N><<<(unsigned)(a.batch * nchunks), 256, 0, stream>>>(
+      static_cast<const T*>(a.B), static_cast<const T*>(a.C), Ct, G, a.seqlen, nchunks);
   auto kernel = a.z != nullptr ? ssd_kernel<T, N, true> : ssd_kernel<T, N, false>;
   kernel<<<(unsigned)(a.batch * a.nheads), 256, 0, stream>>>(
-      static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.A, static_cast<const T*>(a.B), Bt,
+      static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.A, static_cast<const T*>(a.B), G,
       Ct, a.Dskip, static_cast<const T*>(a.z), a.dt_bias, a.h0, static_cast<T*>(a.y),
       a.last_state, s);
   return hipGetLastError();

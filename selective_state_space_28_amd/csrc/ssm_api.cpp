@@ -506,7 +506,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
 size_t ssm_ssd_scan_fwd_workspace_bytes(int batch, int dstate, int64_t seqlen, int dtype) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
   if (batch <= 0 || seqlen <= 0 || dstate <= 0 || dstate > 128) return 0;
-  return round256(2 * (size_t)batch * (size_t)seqlen * (size_t)dstate * (size_t)elem_bytes(dtype));
+  return ssm::ssd_ws_bytes(batch, dstate, seqlen, elem_bytes(dtype));
 }
 
 int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const void* B,
@@ -554,7 +554,7 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
   a.h0 = h0;
   a.y = y;
   a.last_state = last_state;
-  a.ws_bt = workspace;
+  a.ws = workspace;
   a.batch = batch;
   a.nheads = nheads;
   a.headdim = headdim;

@@ -122,6 +122,18 @@ struct BwdLaunch {
 
 // SSD (scalar A per head) forward: heads of kSsdHeadDim channels.
 constexpr int kSsdHeadDim = 64;
+// The SSD workspace: C^T, (batch, seqlen, dstate) in the input type, padded
+// to 256 bytes, then per (batch row, 64-step chunk) the 10 causal 16x16 tiles
+// of C^T B in float32.
+inline size_t ssd_ws_ct_bytes(int batch, int dstate, int64_t seqlen, int elem_bytes) {
+  const size_t ct = (size_t)batch * (size_t)seqlen * (size_t)dstate * (size_t)elem_bytes;
+  return (ct + 255) / 256 * 256;
+}
+inline size_t ssd_ws_bytes(int batch, int dstate, int64_t seqlen, int elem_bytes) {
+  const size_t nchunks = (size_t)((seqlen + 63) / 64);
+  return ssd_ws_ct_bytes(batch, dstate, seqlen, elem_bytes) + (size_t)batch * nchunks * 10 * 256 * 4;
+}
+
 struct SsdLaunch {
   const void* x;          // (batch, nheads * headdim, seqlen)
   const void* dt;         // (batch, nheads, seqlen), raw (bias, softplus applied inside)
@@ -134,7 +146,7 @@ struct SsdLaunch {
   const float* h0;        // (batch, nheads * headdim, dstate) nullable
   void* y;
   float* last_state;      // nullable
-  void* ws_bt;            // B^T then C^T, (batch, seqlen, dstate) each, input type
+  void* ws;               // C^T (batch, seqlen, dstate), input type; then the G tiles
   int batch, nheads, headdim, dstate;
   int64_t seqlen;
   int softplus, zoh, vec;

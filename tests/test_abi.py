@@ -230,8 +230,9 @@ def test_ssd_validation(kw, code):
 
 def test_ssd_workspace_query():
     lib = load()
-    assert lib.ssm_ssd_scan_fwd_workspace_bytes(2, 128, 2048, 1) == 2 * 2 * 2048 * 128 * 2
-    assert lib.ssm_ssd_scan_fwd_workspace_bytes(1, 64, 100, 0) == (2 * 100 * 64 * 4 + 255) // 256 * 256
+    # C^T in the input type (rounded to 256 bytes), then 10 float32 16x16 tiles per row and chunk
+    assert lib.ssm_ssd_scan_fwd_workspace_bytes(2, 128, 2048, 1) == 2 * 2048 * 128 * 2 + 2 * 32 * 10 * 1024
+    assert lib.ssm_ssd_scan_fwd_workspace_bytes(1, 64, 100, 0) == (100 * 64 * 4 + 255) // 256 * 256 + 2 * 10 * 1024
     assert lib.ssm_ssd_scan_fwd_workspace_bytes(0, 64, 100, 0) == 0
 
 
