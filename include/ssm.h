@@ -271,7 +271,8 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
  *   dt_bias        (nheads) float32                          NULL -> 0
  *   flags          SSM_DELTA_SOFTPLUS, SSM_BBAR_ZOH as for ssm_scan_fwd
  *   h0, last_state (batch, nheads*headdim, dstate) float32   NULL -> zero start / not written
- *   headdim must be 64; dstate in {16, 32, 64, 128} (128 for SSM_BF16 only).
+ *   headdim must be 64; dstate in {16, 32, 64, 128} (128 for SSM_BF16 only);
+ *   seqlen * max(64, dstate) * element bytes below 2^31 (SSM_ERR_SHAPE).
  *   workspace      at least ssm_ssd_scan_fwd_workspace_bytes(...) bytes, 256-byte
  *                  aligned, owned by the caller (C with the state index
  *                  contiguous and, per 64-step chunk, the causal tiles of

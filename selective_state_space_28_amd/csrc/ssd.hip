@@ -143,6 +143,54 @@ __device__ __forceinline__ void load_run8(const T* __restrict__ p, bool vec, int
   }
 }
 
+// Buffer accesses: a descriptor (base and byte extent of a per-block region,
+// in scalar registers), a 32-bit per-lane offset that stays fixed from chunk
+// to chunk and a scalar offset that moves with the chunk -- no per-lane
+// 64-bit address arithmetic.  Extents are below 2^31 bytes (checked on the
+// host).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ Buf make_buf(const void* base, int64_t bytes) {
+  return Buf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000)};
+}
+
+// A run of 8 elements of T (16 or 32 bytes) at voff + soff.
+template <typename T>
+__device__ __forceinline__ void buf_load_run8(const Buf& b, uint32_t voff, uint32_t soff,
+                                              uint32_t (&w)[kRunWords<T>]) {
+#pragma unroll
+  for (int i = 0; i < kRunWords<T> / 4; ++i) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(b.r, voff + 16 * i, soff, 0);
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store_run8(const Buf& b, uint32_t voff, uint32_t soff,
+                                               const float (&f)[8]) {
+  uint32_t w[kRunWords<T>];
+  pack_floats<T, 8>(f, w);
+#pragma unroll
+  for (int i = 0; i < kRunWords<T> / 4; ++i) {
+    const u32x4_t v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.r, voff + 16 * i, soff, 0);
+  }
+}
+
+__device__ __forceinline__ float4 buf_load_f4(const Buf& b, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(b.r, voff, soff, 0);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
+__device__ __forceinline__ void buf_load_elem(const Buf& b, uint32_t voff, uint32_t soff, uint16_t& v) {
+  v = __builtin_amdgcn_raw_buffer_load_b16(b.r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_load_elem(const Buf& b, uint32_t voff, uint32_t soff, float& v) {
+  v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(b.r, voff, soff, 0));
+}
+
 // A raw element as float.
 __device__ __forceinline__ float raw_value(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ __forceinline__ float raw_value(float v) { return v; }
@@ -356,39 +404,75 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   uint32_t rx[XI][RW], rz[XI][RW], rb[NI][RW], rct[NI][RW];
   float4 rg[3];  // this wave's causal tiles of G (tiles w, w + 4, w + 8 < 10)
   T rdt = T(0);  // raw: converted where it is used, so the load is not waited for early
+  // whole chunks: buffer accesses with fixed per-lane offsets.  Run item k of
+  // x, z, y and B is row tid / 8 + 32k, steps 8 (tid % 8)..; C^T run item k is
+  // elements 8 (tid + 256k).. of the chunk's rows.
+  constexpr uint32_t ES = sizeof(T);
+  const uint32_t vo_run = ((uint32_t)(tid / 8) * (uint32_t)L + 8u * (uint32_t)(tid % 8)) * ES;
+  const uint32_t vo_ct = (uint32_t)tid * 8u * ES;
+  const Buf bufx = make_buf(xh, (int64_t)P * L * ES);
+  const Buf bufz = make_buf(GATE ? zh : xh, (int64_t)P * L * ES);
+  const Buf bufy = make_buf(yh, (int64_t)P * L * ES);
+  const Buf bufB = make_buf(Bb, (int64_t)N * L * ES);
+  const Buf bufct = make_buf(Ctb, (int64_t)N * L * ES);
+  const Buf bufdt = make_buf(dth, L * ES);
+  const Buf bufg = make_buf(Gb, (int64_t)nchunks * 10 * 64 * 16);
+  auto row_soff = [&](int k, int64_t c0) { return (uint32_t)((32 * (int64_t)k * L + c0) * ES); };
+
   auto load_chunk = [&](auto full_c, int64_t c0) {
     constexpr bool FULL = decltype(full_c)::value;
-    const int tv = FULL ? Q : (int)(L - c0 < Q ? L - c0 : Q);
+    if constexpr (FULL) {
 #pragma unroll
-    for (int k = 0; k < XI; ++k) {
-      const int item = tid + 256 * k;
-      const int t8 = 8 * (item % 8);
-      load_run8<T>(xh + (int64_t)(item / 8) * L + c0 + t8, FULL, tv - t8, rx[k]);
-    }
+      for (int k = 0; k < XI; ++k) buf_load_run8<T>(bufx, vo_run, row_soff(k, c0), rx[k]);
 #pragma unroll
-    for (int k = 0; k < NI; ++k) {
-      const int item = tid + 256 * k;
-      if (NR % 256 == 0 || item < NR) {
-        const int t8 = 8 * (item % 8);
-        load_run8<T>(Bb + (int64_t)(item / 8) * L + c0 + t8, FULL, tv - t8, rb[k]);
-        const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
-        const bool ok = FULL || t < tv;
-        load_run8<T>(Ctb + (c0 + t) * N + n8, ok, 0, rct[k]);  // the workspace rows are aligned
+      for (int k = 0; k < NI; ++k) {
+        if (NR % 256 == 0 || tid + 256 * k < NR) {
+          buf_load_run8<T>(bufB, vo_run, row_soff(k, c0), rb[k]);
+          buf_load_run8<T>(bufct, vo_ct, (uint32_t)((c0 * N + 2048 * k) * ES), rct[k]);
+        }
       }
-    }
-    const float4* Gc = Gb + (c0 / Q) * 10 * 64;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) rg[k] = Gc[(w + 4 * k < 10 ? w + 4 * k : 9) * 64 + lane];
-    rdt = (FULL || lane < tv) ? dth[c0 + lane] : T(0);
+      for (int k = 0; k < 3; ++k)
+        rg[k] = buf_load_f4(bufg, (uint32_t)lane * 16u,
+                            (uint32_t)(((c0 / Q) * 10 + (w + 4 * k < 10 ? w + 4 * k : 9)) * 64 * 16));
+      buf_load_elem(bufdt, (uint32_t)lane * ES, (uint32_t)(c0 * ES), rdt);
+    } else {
+      const int tv = (int)(L - c0 < Q ? L - c0 : Q);
+#pragma unroll
+      for (int k = 0; k < XI; ++k) {
+        const int item = tid + 256 * k;
+        const int t8 = 8 * (item % 8);
+        load_run8<T>(xh + (int64_t)(item / 8) * L + c0 + t8, false, tv - t8, rx[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int item = tid + 256 * k;
+        if (NR % 256 == 0 || item < NR) {
+          const int t8 = 8 * (item % 8);
+          load_run8<T>(Bb + (int64_t)(item / 8) * L + c0 + t8, false, tv - t8, rb[k]);
+          const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
+          load_run8<T>(Ctb + (c0 + t) * N + n8, t < tv, 0, rct[k]);  // the workspace rows are aligned
+        }
+      }
+      const float4* Gc = Gb + (c0 / Q) * 10 * 64;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) rg[k] = Gc[(w + 4 * k < 10 ? w + 4 * k : 9) * 64 + lane];
+      rdt = lane < tv ? dth[c0 + lane] : T(0);
+    }
   };
   auto load_gate = [&](auto full_c, int64_t c0) {
     constexpr bool FULL = decltype(full_c)::value;
-    const int tv = FULL ? Q : (int)(L - c0 < Q ? L - c0 : Q);
+    if constexpr (FULL) {
 #pragma unroll
-    for (int k = 0; k < XI; ++k) {
-      const int item = tid + 256 * k;
-      const int t8 = 8 * (item % 8);
-      load_run8<T>(zh + (int64_t)(item / 8) * L + c0 + t8, FULL, tv - t8, rz[k]);
+      for (int k = 0; k < XI; ++k) buf_load_run8<T>(bufz, vo_run, row_soff(k, c0), rz[k]);
+    } else {
+      const int tv = (int)(L - c0 < Q ? L - c0 : Q);
+#pragma unroll
+      for (int k = 0; k < XI; ++k) {
+        const int item = tid + 256 * k;
+        const int t8 = 8 * (item % 8);
+        load_run8<T>(zh + (int64_t)(item / 8) * L + c0 + t8, false, tv - t8, rz[k]);
+      }
     }
   };
 
@@ -529,10 +613,10 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         if constexpr (GATE) v *= silu_f32(run_elem<T>(rz[k], j));
         yv[j] = v;
       }
-      const int64_t off = (int64_t)pp * L + t0 + t8;
       if constexpr (FULL) {
-        store_floats<T, 8>(yh + off, yv);
+        buf_store_run8<T>(bufy, vo_run, row_soff(k, t0), yv);
       } else {
+        const int64_t off = (int64_t)pp * L + t0 + t8;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (t8 + j < tvalid) Elem<T>::store(yh + off + j, yv[j]);
@@ -547,8 +631,12 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   if (nfull > 0) {
     load_chunk(BoolC<true>{}, 0);
     if constexpr (GATE) load_gate(BoolC<true>{}, 0);
+    // the first chunk is peeled so that the loop is entered with the memory
+    // operations of a chunk in flight, as from its own back edge (the
+    // compiler's waits at the loop head then count only the loads they need)
+    chunk(BoolC<true>{}, 0, (nfull > 1 ? 1 : 0) * Q);
   }
-  for (int64_t c = 0; c < nfull; ++c) chunk(BoolC<true>{}, c * Q, (c + 1 < nfull ? c + 1 : c) * Q);
+  for (int64_t c = 1; c < nfull; ++c) chunk(BoolC<true>{}, c * Q, (c + 1 < nfull ? c + 1 : c) * Q);
   for (int64_t t0 = nfull * Q; t0 < L; t0 += Q) {
     load_chunk(BoolC<false>{}, t0);
     if constexpr (GATE) load_gate(BoolC<false>{}, t0);

@@ -540,6 +540,10 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
   if ((int64_t)batch * ((seqlen + 63) / 64) > INT_MAX) return SSM_ERR_SHAPE;
+  // the kernel addresses a head's x, z, y rows, a batch row's B, C^T and its
+  // chunk tiles with 32-bit byte offsets
+  const int64_t widest = dstate > ssm::kSsdHeadDim ? dstate : ssm::kSsdHeadDim;
+  if (seqlen * widest * (int64_t)es > INT_MAX || (seqlen + 63) / 64 * 10240 > INT_MAX) return SSM_ERR_SHAPE;
   if (workspace == nullptr || workspace_bytes < ssm_ssd_scan_fwd_workspace_bytes(batch, dstate, seqlen, dtype))
     return SSM_ERR_WORKSPACE;
   ssm::SsdLaunch a{};

@@ -223,6 +223,8 @@ def _ssd(**kw):
     (dict(x=None), NULL), (dict(dt=None), NULL), (dict(A=None), NULL), (dict(y=None), NULL),
     (dict(x=P + 1), ALIGN), (dict(A=P + 0x20002), ALIGN), (dict(y=P), ALIAS),
     (dict(ws=P + 0x1000010), ALIGN), (dict(ws=None), WS), (dict(wsb=1000), WS),
+    # 32-bit byte offsets within a head's rows and a batch row's B, C^T
+    (dict(L=1 << 23), SHAPE), (dict(L=1 << 23, N=64, dtype=0), SHAPE),
 ])
 def test_ssd_validation(kw, code):
     assert _ssd(**kw) == code
