@@ -420,10 +420,12 @@ def bench_ssd(dev, steps, warmup):
     x, dt, B, C, z = (dev_t(inp[k]) for k in ("x", "dt", "B", "C", "z"))
     A, D, bias = (dev_t(inp[k], True) for k in ("A", "D", "dt_bias"))
     y = torch.empty_like(x)
+    ws = torch.empty(ssm.ssm_ssd_scan_fwd_workspace_bytes(cfg.batch, cfg.dstate, cfg.seqlen, torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        ssm.ssm_ssd_scan_fwd(x, dt, A, B, C, D, z, bias, out=y)
+        ssm.ssm_ssd_scan_fwd(x, dt, A, B, C, D, z, bias, out=y, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -448,10 +450,10 @@ def bench_ssd(dev, steps, warmup):
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof.update({"kernel": f"ssm::ssd_kernel<unsigned short, {cfg.dstate}>",
+    roof.update({"kernel": f"ssm::ssd_kernel<unsigned short, {cfg.dstate}, true>",
                  "bytes_per_launch": nbytes, "flops_per_launch": flops,
                  "mfma_TFLOPs": round(tflops, 2)})
-    del x, dt, B, C, z, y
+    del x, dt, B, C, z, y, ws
     return {"workload": f"SSD (scalar A per head) scan: batch {cfg.batch}, {cfg.nheads} heads x "
                         f"{cfg.headdim}, N {cfg.dstate}, L {cfg.seqlen}, bf16, chunks of 64 on the "
                         "matrix cores", "ms_per_step": ms, "value": cfg.elements / (ms * 1e-3),

@@ -249,8 +249,13 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const T* __restrict__ B, 
   constexpr int LN = KN + 16 / (int)sizeof(Op);
   __shared__ __align__(16) Op sBt[64][LN];   // [s][n]
   __shared__ __align__(16) Op sCt[64][LN];   // [t][n]
-  const int b = blockIdx.x / nchunks;
-  const int c = blockIdx.x % nchunks;
+  // the same regrouping over XCDs as the scan, so a batch row's C^T and tiles
+  // are written from the XCD whose L2 will read them
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int b = bid / nchunks;
+  const int c = bid % nchunks;
   const int64_t t0 = (int64_t)c * 64;
   const T* Bb = B + (int64_t)b * N * L;
   const T* Cb = C + (int64_t)b * N * L;
@@ -350,8 +355,13 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   __shared__ __align__(16) float sCum2[Q];
   __shared__ __align__(16) float sCoef[Q];
 
-  const int b = blockIdx.x / p.nheads;
-  const int h = blockIdx.x % p.nheads;
+  // Consecutive block ids go to different XCDs; regroup so that the heads an
+  // XCD runs share batch rows (and hence B, C^T and the G tiles in its L2).
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int b = bid / p.nheads;
+  const int h = bid % p.nheads;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave: owns channels 16w..
   const int lane = tid & 63;
