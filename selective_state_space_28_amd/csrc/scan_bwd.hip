@@ -258,20 +258,50 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
   const T* bcw = bc + ((int64_t)b * G + g) * L * R;
   float hist[TL][NS];
 
-  for (int64_t t0 = ((seg_end - 1) / TL) * TL; t0 >= seg_begin; t0 -= TL) {
-    const int tvalid = (int)((seg_end - t0) < TL ? (seg_end - t0) : TL);
-    const int valid = ccvalid ? (tvalid - r0 < 0 ? 0 : (tvalid - r0 > E ? E : tvalid - r0)) : 0;
-    const bool vec_ok = p.vec && valid == E;
+  // A whole tile (FULL: all TL steps in the segment, rows 16-byte aligned) takes
+  // its element runs and its checkpoint from registers loaded while the
+  // previous tile ran, and has no per-step guards; a ragged tile loads its own.
+  constexpr int W = E * (int)sizeof(T) / 4;
+  // one tile ahead when a thread's runs are at most 16 bytes (few states give
+  // long runs; those tiles load their own inputs, still without guards)
+  constexpr bool PF = W <= 4;
+  uint32_t pu[W], pd[W], pg[W], pz[W];  // the next whole tile's runs, raw
+  float pck[NS];                          // and the state entering it
+  auto prefetch = [&](int64_t t0) {
+    const int64_t off = rowcc * L + t0 + r0;
+    load_words<W>(u + off, pu);
+    load_words<W>(delta + off, pd);
+    load_words<W>(dy + off, pg);
+    if (has_z) load_words<W>(z + off, pz);
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+      pck[k] = dvalid ? ckpt[(((int64_t)b * ntiles + t0 / TL) * N + g * NS + k) * p.dim + d] : 0.0f;
+  };
+
+  auto tile = [&](auto full_c, int64_t t0, int64_t next) {
+    constexpr bool FULL = decltype(full_c)::value;
+    const int tvalid = FULL ? TL : (int)((seg_end - t0) < TL ? (seg_end - t0) : TL);
+    const int valid = FULL ? (ccvalid ? E : 0)
+                           : (ccvalid ? (tvalid - r0 < 0 ? 0 : (tvalid - r0 > E ? E : tvalid - r0)) : 0);
+    const bool vec_ok = FULL || (p.vec && valid == E);
     const int64_t eoff = rowcc * L + t0 + r0;
+    if constexpr (FULL && !PF) prefetch(t0);
 
     // ---- stage: Delta, Delta*u, ds, u -------------------------------------------
     float e_u[E], e_ds[E], e_sg[E], e_gz[E], e_dt[E];
     {
       float uu[E], dd[E], gg[E], zz[E];
-      load_run<T, E>(u, eoff, vec_ok, valid, uu);
-      load_run<T, E>(delta, eoff, vec_ok, valid, dd);
-      load_run<T, E>(dy, eoff, vec_ok, valid, gg);
-      if (has_z) load_run<T, E>(z, eoff, vec_ok, valid, zz);
+      if constexpr (FULL) {
+        words_to_floats<T, E>(pu, uu);
+        words_to_floats<T, E>(pd, dd);
+        words_to_floats<T, E>(pg, gg);
+        if (has_z) words_to_floats<T, E>(pz, zz);
+      } else {
+        load_run<T, E>(u, eoff, vec_ok, valid, uu);
+        load_run<T, E>(delta, eoff, vec_ok, valid, dd);
+        load_run<T, E>(dy, eoff, vec_ok, valid, gg);
+        if (has_z) load_run<T, E>(z, eoff, vec_ok, valid, zz);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float x = dd[e] + bias_cc;
@@ -296,16 +326,22 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
     // ---- recompute the tile's states from its checkpoint ------------------------
     const T* bct = bcw + t0 * R;
     float hp0[NS];
+    if constexpr (FULL) {
 #pragma unroll
-    for (int k = 0; k < NS; ++k)
-      hp0[k] = dvalid ? ckpt[(((int64_t)b * ntiles + t0 / TL) * N + g * NS + k) * p.dim + d] : 0.0f;
+      for (int k = 0; k < NS; ++k) hp0[k] = pck[k];
+      if constexpr (PF) prefetch(next);  // the registers of this tile are consumed
+    } else {
+#pragma unroll
+      for (int k = 0; k < NS; ++k)
+        hp0[k] = dvalid ? ckpt[(((int64_t)b * ntiles + t0 / TL) * N + g * NS + k) * p.dim + d] : 0.0f;
+    }
     {
       float h[NS];
 #pragma unroll
       for (int k = 0; k < NS; ++k) h[k] = hp0[k];
 #pragma unroll
       for (int t = 0; t < TL; ++t) {
-        if (t < tvalid) {
+        if (FULL || t < tvalid) {
           const float4 v = s_in[t][lane];
           float acc = 0.0f;
 #pragma unroll
@@ -343,12 +379,12 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
     for (int e = 0; e < E; ++e) e_du[e] = e_dd[e] = 0.0f;
 #pragma unroll
     for (int grp = TL / TR - 1; grp >= 0; --grp) {
-      if (grp * TR >= tvalid) continue;  // uniform: a ragged last tile
+      if (!FULL && grp * TR >= tvalid) continue;  // uniform: a ragged last tile
 #pragma unroll
       for (int i = TR - 1; i >= 0; --i) {
         const int t = grp * TR + i;
         float lb = 0.0f, dd = 0.0f;
-        if (t < tvalid) {
+        if (FULL || t < tvalid) {
           const float4 v = s_in[t][lane];
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
@@ -380,7 +416,7 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
 #pragma unroll
         for (int off = 1; off < TPO; off <<= 1) sacc += __shfl_xor(sacc, off);
         const int t = grp * TR + ri;
-        if (rpart == 0 && t < tvalid)
+        if (rpart == 0 && (FULL || t < tvalid))
           part_bc[((((int64_t)b * p.ncg + cg) * 2 + rw) * N + rn) * L + t0 + t] = sacc;
       }
       // du and d(delta) of this group's steps, for this thread's elements
@@ -407,6 +443,25 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
     if (valid > 0) {
       store_run<T, E>(du, eoff, vec_ok, valid, e_du);
       store_run<T, E>(ddelta, eoff, vec_ok, valid, e_dd);
+    }
+  };
+
+  // tiles from last to first: a ragged top tile (or every tile of unaligned
+  // rows) on its own path, then the whole tiles, the first of them peeled so
+  // that the loop is entered with the same loads in flight as from its back edge
+  const int64_t t_top = ((seg_end - 1) / TL) * TL;
+  if (!p.vec) {
+    for (int64_t t0 = t_top; t0 >= seg_begin; t0 -= TL) tile(BoolC<false>{}, t0, t0);
+  } else {
+    int64_t t0 = t_top;
+    if (seg_end - t_top < TL) {
+      tile(BoolC<false>{}, t0, t0);
+      t0 -= TL;
+    }
+    if (t0 >= seg_begin) {
+      if constexpr (PF) prefetch(t0);
+      tile(BoolC<true>{}, t0, t0 - TL >= seg_begin ? t0 - TL : t0);
+      for (int64_t t = t0 - TL; t >= seg_begin; t -= TL) tile(BoolC<true>{}, t, t - TL >= seg_begin ? t - TL : t);
     }
   }
 

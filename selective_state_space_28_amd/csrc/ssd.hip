@@ -285,11 +285,6 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const T* __restrict__ B, 
   }
 }
 
-template <bool B>
-struct BoolC {
-  static constexpr bool value = B;
-};
-
 // v from the lane that the DPP control CTRL names (0 where it names none, or
 // in rows that ROW_MASK leaves out).
 template <int CTRL, int ROW_MASK>

@@ -65,6 +65,12 @@ __device__ __forceinline__ float silu_f32(float z) {
 
 // ---- element access for the two storage types ------------------------------
 // float32 storage: float.  bfloat16 storage: uint16_t bit patterns.
+// A compile-time bool as a value (selects an instantiation of a generic lambda).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 template <typename T> struct Elem;
 
 template <> struct Elem<float> {
