@@ -297,8 +297,8 @@ int update_impl(float* state, const void* u, const void* delta, const float* A, 
       (cv->state == state || (void*)cv->state == y || (const void*)cv->state == u))
     return SSM_ERR_ALIAS;
   if (empty) return SSM_OK;
-  const int64_t threads = (int64_t)batch * dim * (dstate >= 4 ? dstate / 4 : 1);
-  if ((threads + 255) / 256 > INT_MAX) return SSM_ERR_SHAPE;
+  // one grid row per batch row: its lanes (P per channel) are indexed in 32 bits
+  if ((int64_t)dim * (dstate >= 4 ? dstate / 4 : 1) + 255 > INT_MAX) return SSM_ERR_SHAPE;
 
   ssm::DecodeLaunch a{};
   a.state = state;

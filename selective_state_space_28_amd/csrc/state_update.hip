@@ -22,78 +22,50 @@
 
 namespace ssm {
 
-template <typename T, int N, int MODE>
+// A raw element of T as float.
+__device__ __forceinline__ float raw_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float raw_f32(float v) { return v; }
+
+template <typename T, int N, int MODE, bool VEC, bool GATE>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float* __restrict__ state, const T* __restrict__ u, const T* __restrict__ delta,
     const float* __restrict__ A, const T* __restrict__ B, const T* __restrict__ C,
     const float* __restrict__ Dskip, const T* __restrict__ z, const float* __restrict__ bias,
-    T* __restrict__ y, int batch, int dim, int softplus, int vec,
+    T* __restrict__ y, int b0, int dim, int softplus,
     float* __restrict__ conv_state, const float* __restrict__ conv_w,
     const float* __restrict__ conv_b, int conv_k) {
-  // vec: state, A, B and C are aligned for the vector loads below
+  // grid: (lanes of one batch row / 256, batch rows from b0); VEC: state, A,
+  // B and C are aligned for the vector loads below
   constexpr bool ZOH = (MODE & kModeZoh) != 0;
   constexpr bool CONV = (MODE & kModeConv) != 0;
   constexpr int NS = N < 4 ? N : 4;
   constexpr int P = N / NS;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rows = (int64_t)batch * dim;
+  const int idx = (int)blockIdx.x * 256 + (int)threadIdx.x;  // lane within the batch row
   // Whole channel groups of P lanes are either all in range or all out of
-  // range (P divides 64 and gid ranges start at multiples of 64), so the
+  // range (P divides 64 and idx ranges start at multiples of 64), so the
   // shuffles below only ever read lanes that are active.
-  if (gid >= rows * P) return;
-  const int64_t row = gid / P;
-  const int part = (int)(gid % P);
-  const int b = (int)(row / dim);
-  const int d = (int)(row % dim);
+  if (idx >= dim * P) return;
+  const int b = b0 + (int)blockIdx.y;
+  const int d = idx / P;
+  const int part = idx % P;
+  const int64_t row = (int64_t)b * dim + d;
 
-  float h[NS];
+  // ---- every load of the step, issued before any of them is used (one memory
+  // round trip per thread); token values stay raw until then -------------------
+  float h[NS], av[NS], bv[NS], cv[NS];
   float* sp = state + row * N + part * NS;
-  if (NS == 4 && vec) {
+  const int64_t nb = (int64_t)b * N + part * NS;
+  const float* ap = A + (int64_t)d * N + part * NS;
+  uint32_t bw[2], cw[2];  // bf16 B, C of this lane's 4 states (VEC)
+  if constexpr (NS == 4 && VEC) {
     const float4 v = *reinterpret_cast<const float4*>(sp);
     h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
-  } else {
-#pragma unroll
-    for (int k = 0; k < NS; ++k) h[k] = sp[k];
-  }
-
-  float uv = Elem<T>::load(u + row);
-  if constexpr (CONV) {
-    // every lane of the channel forms u (a few FMAs); lane 0 shifts the
-    // carried inputs.  The lanes of a channel are in one wave and lane 0
-    // stores values its own loads returned, so the stores follow every
-    // lane's loads of conv_state.
-    const int K = conv_k;
-    float* cs = conv_state + row * (K - 1);
-    float prev[kMaxConvWidth - 1];
-#pragma unroll
-    for (int j = 0; j < kMaxConvWidth - 1; ++j) prev[j] = j < K - 1 ? cs[j] : 0.0f;
-    float sacc = conv_b != nullptr ? conv_b[d] : 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxConvWidth - 1; ++j)
-      if (j < K - 1) sacc = __builtin_fmaf(conv_w[(int64_t)d * K + j], prev[j], sacc);
-    sacc = __builtin_fmaf(conv_w[(int64_t)d * K + K - 1], uv, sacc);
-    if (part == 0 && K > 1) {
-#pragma unroll
-      for (int j = 0; j < kMaxConvWidth - 2; ++j)
-        if (j < K - 2) cs[j] = prev[j + 1];
-      cs[K - 2] = uv;
-    }
-    uv = silu_f32(sacc);
-  }
-  const float x = Elem<T>::load(delta + row) + (bias != nullptr ? bias[d] : 0.0f);
-  const float dt = softplus ? softplus_f32(x) : x;
-  const float du = dt * uv;
-  // this lane's NS values of A, B and C, each one vector load when aligned
-  float av[NS], bv[NS], cv[NS];
-  const int64_t nb = (int64_t)b * N + part * NS;
-  if (NS == 4 && vec) {
-    const float4 a4 = *reinterpret_cast<const float4*>(A + (int64_t)d * N + part * NS);
+    const float4 a4 = *reinterpret_cast<const float4*>(ap);
     av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
     if constexpr (sizeof(T) == 2) {
       const uint2 b2 = *reinterpret_cast<const uint2*>(B + nb);
       const uint2 c2 = *reinterpret_cast<const uint2*>(C + nb);
-      bv[0] = bf16_lo(b2.x); bv[1] = bf16_hi(b2.x); bv[2] = bf16_lo(b2.y); bv[3] = bf16_hi(b2.y);
-      cv[0] = bf16_lo(c2.x); cv[1] = bf16_hi(c2.x); cv[2] = bf16_lo(c2.y); cv[3] = bf16_hi(c2.y);
+      bw[0] = b2.x; bw[1] = b2.y; cw[0] = c2.x; cw[1] = c2.y;
     } else {
       const float4 b4 = *reinterpret_cast<const float4*>(B + nb);
       const float4 c4 = *reinterpret_cast<const float4*>(C + nb);
@@ -103,11 +75,57 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   } else {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      av[k] = A[(int64_t)d * N + part * NS + k];
-      bv[k] = Elem<T>::load(B + nb + k);
-      cv[k] = Elem<T>::load(C + nb + k);
+      h[k] = sp[k];
+      av[k] = ap[k];
+      bv[k] = raw_f32(B[nb + k]);
+      cv[k] = raw_f32(C[nb + k]);
     }
   }
+  const T u_raw = u[row];
+  const T d_raw = delta[row];
+  T z_raw = T(0);
+  if constexpr (GATE) z_raw = z[row];
+  const float bias_d = bias != nullptr ? bias[d] : 0.0f;
+  const float D_d = Dskip != nullptr ? Dskip[d] : 0.0f;
+  float prev[kMaxConvWidth - 1], taps[kMaxConvWidth], cbias = 0.0f;
+  float* cs = nullptr;
+  if constexpr (CONV) {
+    cs = conv_state + row * (conv_k - 1);
+#pragma unroll
+    for (int j = 0; j < kMaxConvWidth - 1; ++j) prev[j] = j < conv_k - 1 ? cs[j] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxConvWidth; ++j) taps[j] = j < conv_k ? conv_w[(int64_t)d * conv_k + j] : 0.0f;
+    cbias = conv_b != nullptr ? conv_b[d] : 0.0f;
+  }
+  if constexpr (NS == 4 && VEC && sizeof(T) == 2) {
+    bv[0] = bf16_lo(bw[0]); bv[1] = bf16_hi(bw[0]); bv[2] = bf16_lo(bw[1]); bv[3] = bf16_hi(bw[1]);
+    cv[0] = bf16_lo(cw[0]); cv[1] = bf16_hi(cw[0]); cv[2] = bf16_lo(cw[1]); cv[3] = bf16_hi(cw[1]);
+  }
+
+  // ---- the step --------------------------------------------------------------
+  float uv = raw_f32(u_raw);
+  if constexpr (CONV) {
+    // every lane of the channel forms u (a few FMAs); lane 0 shifts the
+    // carried inputs.  The lanes of a channel are in one wave and lane 0
+    // stores values its own loads returned, so the stores follow every
+    // lane's loads of conv_state.
+    const int K = conv_k;
+    float sacc = cbias;
+#pragma unroll
+    for (int j = 0; j < kMaxConvWidth - 1; ++j)
+      if (j < K - 1) sacc = __builtin_fmaf(taps[j], prev[j], sacc);
+    sacc = __builtin_fmaf(taps[K - 1], uv, sacc);
+    if (part == 0 && K > 1) {
+#pragma unroll
+      for (int j = 0; j < kMaxConvWidth - 2; ++j)
+        if (j < K - 2) cs[j] = prev[j + 1];
+      cs[K - 2] = uv;
+    }
+    uv = silu_f32(sacc);
+  }
+  const float x = raw_f32(d_raw) + bias_d;
+  const float dt = softplus ? softplus_f32(x) : x;
+  const float du = dt * uv;
   float acc = 0.0f;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     acc = __builtin_fmaf(cv[k], h[k], acc);
   }
 
-  if (NS == 4 && vec) {
+  if constexpr (NS == 4 && VEC) {
     *reinterpret_cast<float4*>(sp) = make_float4(h[0], h[1], h[2], h[3]);
   } else {
 #pragma unroll
@@ -133,8 +151,8 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   for (int off = 1; off < P; off <<= 1) acc += __shfl_xor(acc, off);
 
   if (part == 0) {
-    float yv = __builtin_fmaf(Dskip != nullptr ? Dskip[d] : 0.0f, uv, acc);
-    if (z != nullptr) yv *= silu_f32(Elem<T>::load(z + row));
+    float yv = __builtin_fmaf(D_d, uv, acc);
+    if constexpr (GATE) yv *= silu_f32(raw_f32(z_raw));
     Elem<T>::store(y + row, yv);
   }
 }
@@ -143,14 +161,23 @@ template <typename T, int N, int MODE>
 static hipError_t launch_n(const DecodeLaunch& a, hipStream_t stream) {
   constexpr int NS = N < 4 ? N : 4;
   constexpr int P = N / NS;
-  const int64_t threads = (int64_t)a.batch * a.dim * P;
-  const unsigned grid = (unsigned)((threads + 255) / 256);
-  state_update_kernel<T, N, MODE><<<grid, 256, 0, stream>>>(
-      a.state, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A,
-      static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.Dskip,
-      static_cast<const T*>(a.z), a.bias, static_cast<T*>(a.y), a.batch, a.dim, a.softplus,
-      a.vec, a.conv_state, a.conv_w, a.conv_b, a.conv_k);
-  return hipGetLastError();
+  const unsigned gx = (unsigned)(((int64_t)a.dim * P + 255) / 256);
+  auto kernel = a.vec ? (a.z != nullptr ? state_update_kernel<T, N, MODE, true, true>
+                                        : state_update_kernel<T, N, MODE, true, false>)
+                      : (a.z != nullptr ? state_update_kernel<T, N, MODE, false, true>
+                                        : state_update_kernel<T, N, MODE, false, false>);
+  constexpr int kMaxRows = 65535;  // grid y per launch
+  for (int b0 = 0; b0 < a.batch; b0 += kMaxRows) {
+    const int nb = a.batch - b0 < kMaxRows ? a.batch - b0 : kMaxRows;
+    kernel<<<dim3(gx, (unsigned)nb), 256, 0, stream>>>(
+        a.state, static_cast<const T*>(a.u), static_cast<const T*>(a.delta), a.A,
+        static_cast<const T*>(a.B), static_cast<const T*>(a.C), a.Dskip,
+        static_cast<const T*>(a.z), a.bias, static_cast<T*>(a.y), b0, a.dim, a.softplus,
+        a.conv_state, a.conv_w, a.conv_b, a.conv_k);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename T, int MODE>
