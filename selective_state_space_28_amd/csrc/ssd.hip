@@ -195,6 +195,23 @@ __device__ __forceinline__ void buf_load_elem(const Buf& b, uint32_t voff, uint3
 __device__ __forceinline__ float raw_value(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ __forceinline__ float raw_value(float v) { return v; }
 
+// Run j of the transpose of an 8 x 8 tile (rows i = 0..7, each a run of 8):
+// (tile[0][j], ..., tile[7][j]) as raw words.
+template <typename T>
+__device__ __forceinline__ void tile_column(const uint32_t (&tile)[8][kRunWords<T>], int j,
+                                            uint32_t (&out)[kRunWords<T>]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = tile[2 * q][j >> 1], b = tile[2 * q + 1][j >> 1];
+      out[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = tile[i][j];
+  }
+}
+
 // Element j (0..7) of a run, as float.
 template <typename T>
 __device__ __forceinline__ float run_elem(const uint32_t (&w)[kRunWords<T>], int j) {
@@ -243,7 +260,7 @@ __device__ __forceinline__ int causal_tile_row(int q) { return q < 1 ? 0 : q < 3
 template <typename T, int N>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(const T* __restrict__ B, const T* __restrict__ C,
                                                        T* __restrict__ Ct, float4* __restrict__ G,
-                                                       int64_t L, int nchunks) {
+                                                       int64_t L, int nchunks, int vec) {
   using Op = typename Mma<T>::Op;
   constexpr int KN = (N + Mma<T>::K - 1) / Mma<T>::K * Mma<T>::K;
   constexpr int LN = KN + 16 / (int)sizeof(Op);
@@ -259,14 +276,37 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const T* __restrict__ B, 
   const int64_t t0 = (int64_t)c * 64;
   const T* Bb = B + (int64_t)b * N * L;
   const T* Cb = C + (int64_t)b * N * L;
-  for (int i = threadIdx.x; i < KN * 64; i += 256) {
-    const int n = i / 64, tt = i % 64;
-    const bool ok = n < N && t0 + tt < L;  // zeros past the sequence and past N
-    sBt[tt][n] = ok ? as_operand(Bb[(int64_t)n * L + t0 + tt]) : Mma<T>::cvt(0.0f);
-    sCt[tt][n] = ok ? as_operand(Cb[(int64_t)n * L + t0 + tt]) : Mma<T>::cvt(0.0f);
+  // Staging: item q takes an 8 x 8 tile (states n0..n0+7, steps t8..t8+7) of
+  // B (q < N) or C: 8 runs of 8 steps read from the (N, L) rows, turned in
+  // registers into 8 runs of 8 states, one per step, each written whole.
+  // Consecutive items take consecutive state tiles of one step tile, so the
+  // lanes of an LDS write phase fill one contiguous row segment.  Steps past
+  // the sequence are zeros.
+  constexpr int RW = kRunWords<T>;
+  const bool whole = vec && t0 + 64 <= L;  // every run 16-byte aligned and inside the sequence
+  for (int q = threadIdx.x; q < 2 * N; q += 256) {
+    const int which = q / N, r = q % N;
+    const int n0 = 8 * (r % (N / 8)), t8 = 8 * (r / (N / 8));
+    const T* src = (which == 0 ? Bb : Cb) + (int64_t)n0 * L + t0 + t8;
+    const int valid = (int)(L - t0) - t8;  // steps of these runs inside the sequence (any sign)
+    uint32_t tile[8][RW];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_run8<T>(src + (int64_t)i * L, whole, valid, tile[i]);
+    Op(*dst)[LN] = which == 0 ? sBt : sCt;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t col[RW];
+      tile_column<T>(tile, j, col);
+      store_words<RW>(&dst[t8 + j][n0], col);
+    }
+  }
+  if constexpr (KN > N) {  // the padded states stay zero
+    for (int i = threadIdx.x; i < 64 * (KN - N); i += 256) {
+      sBt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
+      sCt[i / (KN - N)][N + i % (KN - N)] = Mma<T>::cvt(0.0f);
+    }
   }
   __syncthreads();
-  constexpr int RW = kRunWords<T>;
   T* Ctb = Ct + ((int64_t)b * L + t0) * N;
   for (int i = threadIdx.x; i < 64 * (N / 8); i += 256) {
     const int tt = i / (N / 8), n8 = 8 * (i % (N / 8));
@@ -674,7 +714,7 @@ static hipError_t launch_ssd_n(const SsdLaunch& a, hipStream_t stream) {
   float4* G = reinterpret_cast<float4*>(static_cast<char*>(a.ws) +
                                         ssd_ws_ct_bytes(a.batch, N, a.seqlen, (int)sizeof(T)));
   ssd_prep_kernel<T, N><<<(unsigned)(a.batch * nchunks), 256, 0, stream>>>(
-      static_cast<const T*>(a.B), static_cast<const T*>(a.C), Ct, G, a.seqlen, nchunks);
+      static_cast<const T*>(a.B), static_cast<const T*>(a.C), Ct, G, a.seqlen, nchunks, a.vec);
   auto kernel = a.z != nullptr ? ssd_kernel<T, N, true> : ssd_kernel<T, N, false>;
   kernel<<<(unsigned)(a.batch * a.nheads), 256, 0, stream>>>(
       static_cast<const T*>(a.x), static_cast<const T*>(a.dt), a.A, static_cast<const T*>(a.B), G,
