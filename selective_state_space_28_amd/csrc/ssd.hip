@@ -389,6 +389,21 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   // coefficient Bbar_t
   __shared__ __align__(16) float sCum2[Q];
   __shared__ __align__(16) float sCoef[Q];
+  // Per-step factors, written by wave 0 after the prefix sum and read in the
+  // mask step, in the output staging while it is free (cum_t as above, c_i =
+  // cum_{16i}):
+  //   sE0[t]    = exp2(cum_t)                      scales row t of C^T
+  //   sW[s]     = exp2(cum_Q - cum_s) Bbar_s       scales x for the state update
+  //   sE1[t]    = exp2(cum_t - c_{t/16})
+  //   sW2[i][s] = exp2(c_i - cum_s) Bbar_s, s < 16i
+  // so that an off-diagonal mask entry exp2(cum_t - cum_s) Bbar_s (s < 16i <= t)
+  // is sE1[t] sW2[i][s]: both factors are partial decays over [s, t], never
+  // beyond the entry itself.
+  float* const sE0 = &sY[0][0];
+  float* const sW = sE0 + Q;
+  float* const sE1 = sW + Q;
+  float(*const sW2)[Q] = reinterpret_cast<float(*)[Q]>(sE1 + Q);  // rows 1..3 used
+  static_assert(P * YL >= 7 * Q, "the factors fit in the output staging");
 
   // Consecutive block ids go to different XCDs; regroup so that the heads an
   // XCD runs share batch rows (and hence B, C^T and the G tiles in its L2).
@@ -529,7 +544,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     constexpr bool FULL = decltype(full_c)::value;
     const int tvalid = FULL ? Q : (int)(L - t0 < Q ? L - t0 : Q);
 
-    // ---- (1) this chunk's x, B, C^T into LDS; Delta and its prefix sum ------------------
+    // ---- (1) this chunk's x, B into LDS; Delta, its prefix sum and the per-step factors --
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
       const int item = tid + 256 * k;
@@ -540,8 +555,6 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       const int item = tid + 256 * k;
       if (NR % 256 == 0 || item < NR) {
         lds_store_run<T>(&sB[item / 8][8 * (item % 8)], rb[k]);
-        const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
-        lds_store_states<T>(&sCt[t][0], n8, rct[k]);
       }
     }
     if (w == 0) {
@@ -556,21 +569,49 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
           coef = dl;
         }
       }
-      sCum2[lane] = wave_prefix_sum(dl * A2h);
+      const float cum2 = wave_prefix_sum(dl * A2h);
+      sCum2[lane] = cum2;
       sCoef[lane] = coef;
+      const float cQ = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum2), Q - 1));
+      float cref[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cref[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum2), 16 * i));
+      sE0[lane] = exp2_hw(cum2);
+      sW[lane] = exp2_hw(cQ - cum2) * coef;
+      sE1[lane] = exp2_hw(cum2 - cref[lane >> 4]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) sW2[i][lane] = lane < 16 * i ? exp2_hw(cref[i] - cum2) * coef : 0.0f;
     }
     __syncthreads();
 
     // ---- (2) x o w; the mask; then the next chunk's loads ------------------------------------
     const float cum2Q = sCum2[Q - 1];
+    // C^T rows scaled by exp2(cum_t), so the state part of Y leaves the
+    // product already decayed
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int item = tid + 256 * k;
+      if (NR % 256 == 0 || item < NR) {
+        const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
+        const float e = sE0[t];
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = run_elem<T>(rct[k], j) * e;
+        uint32_t wv[RW];
+        pack_floats<T, 8>(v, wv);
+        lds_store_states<T>(&sCt[t][0], n8, wv);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
       const int item = tid + 256 * k;
       const int pp = item / 8, t8 = 8 * (item % 8);
+      const float4 w0 = *reinterpret_cast<const float4*>(&sW[t8]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&sW[t8 + 4]);
+      const float wvv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       float v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = run_elem<T>(rx[k], j) * (exp2_hw(cum2Q - sCum2[t8 + j]) * sCoef[t8 + j]);
+      for (int j = 0; j < 8; ++j) v[j] = run_elem<T>(rx[k], j) * wvv[j];
       uint32_t wv[RW];
       pack_floats<T, 8>(v, wv);
       lds_store_run<T>(&sXw[pp][t8], wv);
@@ -586,13 +627,22 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       const int i = causal_tile_row(q), j = q - i * (i + 1) / 2;
       const float gv[4] = {rg[k].x, rg[k].y, rg[k].z, rg[k].w};
       const int t = 16 * i + (lane & 15), s0 = 16 * j + 4 * (lane >> 4);
-      const float ct = sCum2[t];
-      const float4 cs = *reinterpret_cast<const float4*>(&sCum2[s0]);
-      const float4 bs = *reinterpret_cast<const float4*>(&sCoef[s0]);
-      const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
       float mv[4];
+      if (i == j) {  // diagonal tile: the decay between s and t directly
+        const float ct = sCum2[t];
+        const float4 cs = *reinterpret_cast<const float4*>(&sCum2[s0]);
+        const float4 bs = *reinterpret_cast<const float4*>(&sCoef[s0]);
+        const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mv[r] = s0 + r <= t ? (gv[r] * bsv[r]) * exp2_hw(ct - csv[r]) : 0.0f;
+        for (int r = 0; r < 4; ++r) mv[r] = s0 + r <= t ? (gv[r] * bsv[r]) * exp2_hw(ct - csv[r]) : 0.0f;
+      } else {  // s < 16i <= t: split at step 16i
+        const float e1 = sE1[t];
+        const float4 w2 = *reinterpret_cast<const float4*>(&sW2[i][s0]);
+        mv[0] = (gv[0] * w2.x) * e1;
+        mv[1] = (gv[1] * w2.y) * e1;
+        mv[2] = (gv[2] * w2.z) * e1;
+        mv[3] = (gv[3] * w2.w) * e1;
+      }
       uint32_t wv[4 * sizeof(T) / 4];
       pack_floats<T, 4>(mv, wv);
       store_words<4 * sizeof(T) / 4>(&sM[t][s0], wv);
@@ -601,7 +651,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     if constexpr (FULL) load_chunk(full_c, next);
     __syncthreads();
 
-    // ---- (3) Y = M X^T + diag(exp(cum_t)) C^T H for this wave's channels, staged [p][t]
+    // ---- (3) Y = M X^T + (diag(exp(cum_t)) C^T) H for this wave's channels, staged [p][t]
     // ----------------------------------------------------------------------------------
     {
       typename Mma<T>::StatePack hp[NPK];
@@ -620,10 +670,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
 #pragma unroll
         for (int m = 0; m < NPK; ++m) yo = Mma<T>::mma_state(&sCt[16 * i][PS * m], LN, hp[m], yo, lane);
         const int t0 = 16 * i + 4 * (lane >> 4);
-        const float4 e = *reinterpret_cast<const float4*>(&sCum2[t0]);
         *reinterpret_cast<float4*>(&sY[16 * w + (lane & 15)][ystage_col(t0)]) =
-            make_float4(__builtin_fmaf(exp2_hw(e.x), yo[0], yd[0]), __builtin_fmaf(exp2_hw(e.y), yo[1], yd[1]),
-                        __builtin_fmaf(exp2_hw(e.z), yo[2], yd[2]), __builtin_fmaf(exp2_hw(e.w), yo[3], yd[3]));
+            make_float4(yd[0] + yo[0], yd[1] + yo[1], yd[2] + yo[2], yd[3] + yo[3]);
       }
     }
     // ---- H <- exp(cum_Q) H + B (x o w)^T ----------------------------------------------------
