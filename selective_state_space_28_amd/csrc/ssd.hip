@@ -251,6 +251,16 @@ __device__ __forceinline__ float as_operand(float v) { return v; }
 // matrix, numbered row by row: tile q has i = the largest with i(i+1)/2 <= q.
 __device__ __forceinline__ int causal_tile_row(int q) { return q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3; }
 
+// The k-th (k < 3) causal tile that wave w (w < 4) forms in the scan, or -1:
+// one diagonal tile per wave (0, 5, 2, 9; the costly ones, with a decay per
+// entry), then the off-diagonal ones.
+__device__ __forceinline__ int wave_mask_tile(int w, int k) {
+  const int t0 = w == 0 ? 0 : w == 1 ? 5 : w == 2 ? 2 : 9;
+  const int t1 = w == 0 ? 4 : w == 1 ? 1 : w == 2 ? 6 : 3;
+  const int t2 = w == 0 ? 8 : w == 1 ? 7 : -1;
+  return k == 0 ? t0 : k == 1 ? t1 : t2;
+}
+
 // Per (batch row, chunk of 64 steps): C^T with the state index contiguous,
 // (batch, L, N), for the products with the state, and the chunk's causal
 // tiles of G = C^T B (G[t][s] = C_t . B_s), which do not depend on the head:
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   // loads and stores, so the only memory operations in flight across the
   // loop are in program order; the ragged last chunk takes element accesses.
   uint32_t rx[XI][RW], rz[XI][RW], rb[NI][RW], rct[NI][RW];
-  float4 rg[3];  // this wave's causal tiles of G (tiles w, w + 4, w + 8 < 10)
+  float4 rg[3];  // this wave's causal tiles of G (wave_mask_tile(w, k))
   T rdt = T(0);  // raw: converted where it is used, so the load is not waited for early
   // whole chunks: buffer accesses with fixed per-lane offsets.  Run item k of
   // x, z, y and B is row tid / 8 + 32k, steps 8 (tid % 8)..; C^T run item k is
@@ -479,23 +489,37 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   const Buf bufg = make_buf(Gb, (int64_t)nchunks * 10 * 64 * 16);
   auto row_soff = [&](int k, int64_t c0) { return (uint32_t)((32 * (int64_t)k * L + c0) * ES); };
 
+  // Whole chunks load the next chunk in three parts, each right after this
+  // chunk's last use of the registers it fills (spreading the loads over the
+  // chunk): B and Delta after step 1, x and C^T after the scaling, the G
+  // tiles after the mask.
+  auto load_part_b = [&](int64_t c0) {
+#pragma unroll
+    for (int k = 0; k < NI; ++k)
+      if (NR % 256 == 0 || tid + 256 * k < NR) buf_load_run8<T>(bufB, vo_run, row_soff(k, c0), rb[k]);
+    buf_load_elem(bufdt, (uint32_t)lane * ES, (uint32_t)(c0 * ES), rdt);
+  };
+  auto load_part_xc = [&](int64_t c0) {
+#pragma unroll
+    for (int k = 0; k < XI; ++k) buf_load_run8<T>(bufx, vo_run, row_soff(k, c0), rx[k]);
+#pragma unroll
+    for (int k = 0; k < NI; ++k)
+      if (NR % 256 == 0 || tid + 256 * k < NR)
+        buf_load_run8<T>(bufct, vo_ct, (uint32_t)((c0 * N + 2048 * k) * ES), rct[k]);
+  };
+  auto load_part_g = [&](int64_t c0) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int q = wave_mask_tile(w, k);
+      rg[k] = buf_load_f4(bufg, (uint32_t)lane * 16u, (uint32_t)(((c0 / Q) * 10 + (q >= 0 ? q : 9)) * 64 * 16));
+    }
+  };
   auto load_chunk = [&](auto full_c, int64_t c0) {
     constexpr bool FULL = decltype(full_c)::value;
     if constexpr (FULL) {
-#pragma unroll
-      for (int k = 0; k < XI; ++k) buf_load_run8<T>(bufx, vo_run, row_soff(k, c0), rx[k]);
-#pragma unroll
-      for (int k = 0; k < NI; ++k) {
-        if (NR % 256 == 0 || tid + 256 * k < NR) {
-          buf_load_run8<T>(bufB, vo_run, row_soff(k, c0), rb[k]);
-          buf_load_run8<T>(bufct, vo_ct, (uint32_t)((c0 * N + 2048 * k) * ES), rct[k]);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < 3; ++k)
-        rg[k] = buf_load_f4(bufg, (uint32_t)lane * 16u,
-                            (uint32_t)(((c0 / Q) * 10 + (w + 4 * k < 10 ? w + 4 * k : 9)) * 64 * 16));
-      buf_load_elem(bufdt, (uint32_t)lane * ES, (uint32_t)(c0 * ES), rdt);
+      load_part_b(c0);
+      load_part_xc(c0);
+      load_part_g(c0);
     } else {
       const int tv = (int)(L - c0 < Q ? L - c0 : Q);
 #pragma unroll
@@ -516,7 +540,10 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       }
       const float4* Gc = Gb + (c0 / Q) * 10 * 64;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) rg[k] = Gc[(w + 4 * k < 10 ? w + 4 * k : 9) * 64 + lane];
+      for (int k = 0; k < 3; ++k) {
+        const int q = wave_mask_tile(w, k);
+        rg[k] = Gc[(q >= 0 ? q : 9) * 64 + lane];
+      }
       rdt = lane < tv ? dth[c0 + lane] : T(0);
     }
   };
@@ -582,9 +609,10 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
 #pragma unroll
       for (int i = 1; i < 4; ++i) sW2[i][lane] = lane < 16 * i ? exp2_hw(cref[i] - cum2) * coef : 0.0f;
     }
+    if constexpr (FULL) load_part_b(next);  // B and Delta are in LDS / used
     __syncthreads();
 
-    // ---- (2) x o w; the mask; then the next chunk's loads ------------------------------------
+    // ---- (2) C^T scaled, x o w, the mask (the next chunk's loads in between) --------------
     const float cum2Q = sCum2[Q - 1];
     // C^T rows scaled by exp2(cum_t), so the state part of Y leaves the
     // product already decayed
@@ -616,14 +644,15 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       pack_floats<T, 8>(v, wv);
       lds_store_run<T>(&sXw[pp][t8], wv);
     }
+    if constexpr (FULL) load_part_xc(next);  // x and C^T are in LDS
 
-    // the 10 causal 16x16 tiles (t-block i, s-block j <= i) dealt round-robin
-    // over the 4 waves; a lane holds 4 consecutive s of one t and writes them
-    // at once
+    // the 10 causal 16x16 tiles (t-block i, s-block j <= i) dealt over the 4
+    // waves one diagonal tile each (wave_mask_tile); a lane holds 4
+    // consecutive s of one t and writes them at once
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      const int q = w + 4 * k;
-      if (q >= 10) break;
+      const int q = wave_mask_tile(w, k);
+      if (q < 0) break;
       const int i = causal_tile_row(q), j = q - i * (i + 1) / 2;
       const float gv[4] = {rg[k].x, rg[k].y, rg[k].z, rg[k].w};
       const int t = 16 * i + (lane & 15), s0 = 16 * j + 4 * (lane >> 4);
@@ -647,8 +676,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       pack_floats<T, 4>(mv, wv);
       store_words<4 * sizeof(T) / 4>(&sM[t][s0], wv);
     }
-    // the next chunk's loads (after the last use of this chunk's G tiles)
-    if constexpr (FULL) load_chunk(full_c, next);
+    if constexpr (FULL) load_part_g(next);  // this chunk's G tiles are used
     __syncthreads();
 
     // ---- (3) Y = M X^T + (diag(exp(cum_t)) C^T) H for this wave's channels, staged [p][t]
