@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         lds_store_run<T>(&sB[item / 8][8 * (item % 8)], rb[k]);
       }
     }
-    if (w == 0) {
+    {  // every wave forms the prefix sum (a few DPP steps) and writes its share of the factors
       float dl = 0.0f, coef = 0.0f;
       if (FULL || lane < tvalid) {
         const float xr = raw_value(rdt) + bias_h;
@@ -597,17 +597,23 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         }
       }
       const float cum2 = wave_prefix_sum(dl * A2h);
-      sCum2[lane] = cum2;
-      sCoef[lane] = coef;
       const float cQ = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum2), Q - 1));
       float cref[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) cref[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum2), 16 * i));
-      sE0[lane] = exp2_hw(cum2);
-      sW[lane] = exp2_hw(cQ - cum2) * coef;
-      sE1[lane] = exp2_hw(cum2 - cref[lane >> 4]);
-#pragma unroll
-      for (int i = 1; i < 4; ++i) sW2[i][lane] = lane < 16 * i ? exp2_hw(cref[i] - cum2) * coef : 0.0f;
+      if (w == 0) {
+        sCum2[lane] = cum2;
+        sCoef[lane] = coef;
+        sE0[lane] = exp2_hw(cum2);
+      } else if (w == 1) {
+        sW[lane] = exp2_hw(cQ - cum2) * coef;
+        sE1[lane] = exp2_hw(cum2 - cref[lane >> 4]);
+      } else if (w == 2) {
+        sW2[1][lane] = lane < 16 ? exp2_hw(cref[1] - cum2) * coef : 0.0f;
+        sW2[2][lane] = lane < 32 ? exp2_hw(cref[2] - cum2) * coef : 0.0f;
+      } else {
+        sW2[3][lane] = lane < 48 ? exp2_hw(cref[3] - cum2) * coef : 0.0f;
+      }
     }
     if constexpr (FULL) load_part_b(next);  // B and Delta are in LDS / used
     __syncthreads();
