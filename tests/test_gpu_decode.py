@@ -140,3 +140,19 @@ def test_decode_unaligned_pointers(dev, dtype):
         torch.cuda.synchronize()
         assert torch.equal(ya.float(), yu.float())
     assert torch.equal(st_a, st_u)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_no_gate_no_skip(dev, dtype):
+    """z and D absent: y = C.h (the ungated instantiation)."""
+    cfg = DecodeConfig("t", 3, 70, 16, 4, dtype, seed=11, gate=False, dskip=False)
+    _run_steps(cfg, dev, 4)
+
+
+def test_decode_more_batch_rows_than_one_launch(dev):
+    """65540 batch rows: the grid holds at most 65535 batch rows per launch, so
+    the step runs as two launches; rows on both sides of the split are checked."""
+    cfg = DecodeConfig("t", 65540, 2, 16, 2, "bf16", seed=12)
+    rows = np.array([0, 1, 2 * 65533, 2 * 65534 + 1, 2 * 65535, 2 * 65535 + 1, 2 * 65539 + 1])
+    print("decode 65540 batch rows", flush=True)
+    _run_steps(cfg, dev, 2, rows=rows)
