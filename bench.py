@@ -319,9 +319,25 @@ def main():
                   "roofline": {"bound": "alu", "achieved": round(tops_b, 3),
                                "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
                                "frac": round(tops_b / VALU_PEAK_TOPS, 4),
-                               "kernel": "ssm::bwd_kernel<unsigned short, 4, 4, 16> (+ checkpoint "
-                                         "pass and sums)",
+                               "kernel": "ssm::bwd_kernel<unsigned short, 4, 4, 16, false> (+ "
+                                         "checkpoint pass and sums)",
                                "ops_per_launch": ops_b}}
+
+    # the same backward with the zero-order-hold input term
+    def step_bwd_zoh():
+        ssm.ssm_scan_bwd(u, delta, A, B, C, D, z, bias, dy=gy, bbar="zoh", workspace=bws)
+
+    step_bwd_zoh()
+    torch.cuda.synchronize(dev)
+    for s, e in ev[:nb]:
+        s.record(stream)
+        step_bwd_zoh()
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_bz = float(np.mean([s.elapsed_time(e) for s, e in ev[:nb]]))
+    out["bwd_zoh"] = {"workload": "ssm_scan_bwd of the same scan with the zero-order-hold input term",
+                      "steps": nb, "ms_per_step": ms_bz, "value": elements / (ms_bz * 1e-3),
+                      "unit": "elements/s"}
     del gy, bws
     del u, delta, B, C, z, y, ws
 

@@ -225,8 +225,10 @@ size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
  * and every gradient is the chain rule through the formula at the top.
  *
  *   u .. h0          in   as for ssm_scan_fwd (same layouts and dtype)
- *   flags            SSM_DELTA_SOFTPLUS only: the backward covers the Euler
- *                    input term (SSM_BBAR_ZOH returns SSM_ERR_FLAGS)
+ *   flags            as for ssm_scan_fwd: SSM_DELTA_SOFTPLUS, SSM_BBAR_ZOH (the
+ *                    zero-order-hold input term, dBbar/dDelta = Abar and
+ *                    dBbar/dA = (x e^x - e^x + 1)/A^2, x = Delta A, with its
+ *                    series Delta^2 (1/2 + x/3 + ...) where abs(x) < 1/4)
  *   dy               in   (batch, dim, seqlen), dtype          required
  *   dlast_state      in   (batch, dim, dstate) float32         NULL -> 0
  *   du, ddelta       out  (batch, dim, seqlen), dtype          required

@@ -30,6 +30,11 @@
 //   dA    += lambda h_{t-1} Abar Delta
 //   dDelta += lambda (h_{t-1} Abar A + B u)
 //   du    += lambda Delta B;   dB += lambda Delta u;   dC += ds h_t
+// With the zero-order-hold term Bbar = (Abar - 1)/A in place of Delta
+// (dBbar/dDelta = Abar, dBbar/dA from zoh_coef_dA):
+//   dA    += lambda (h_{t-1} Abar Delta + dBbar/dA B u)
+//   dDelta += lambda (h_{t-1} Abar A + Abar B u)
+//   du    += lambda Bbar B;    dB += lambda Bbar u
 // and per element du += ds D, dD += ds u, d(delta) = dDelta softplus'(x),
 // dz = dy (C.h + D u) silu'(z), ds = dy silu(z).
 #include "ssm_kernels.hpp"
@@ -168,8 +173,10 @@ __global__ __launch_bounds__(64 * G) void bwd_agg_kernel(
 }
 
 // ---- 3. the main backward sweep --------------------------------------------------
-template <typename T, int NS, int G, int TL>
-__global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
+// The zero-order-hold instantiation carries more live values per (element,
+// state) and takes the whole register file (one workgroup per CU).
+template <typename T, int NS, int G, int TL, bool ZOH>
+__global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
     const float* __restrict__ bias, const T* __restrict__ dy, const float* __restrict__ dlast,
@@ -189,7 +196,11 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
 
   __shared__ float4 s_in[TL][LDW];            // (Delta, Delta*u, ds, u) per (step, channel)
   __shared__ __align__(16) float s_buf[NRED > NY ? NRED : NY];  // readout partials, then dB/dC terms
-  __shared__ float2 s_p[G][TR][LDW];          // per wave and step: (sum lambda B, sum dDelta part)
+  // per wave and step, the sums over this wave's states: Euler (sum lambda B,
+  // sum of the Abar part of dDelta); ZOH (sum lambda Bbar B, sum lambda Abar B,
+  // the Abar part, -)
+  using SP = typename std::conditional<ZOH, float4, float2>::type;
+  __shared__ SP s_p[G][TR][LDW];
   float(*s_y)[TL][LDW] = reinterpret_cast<float(*)[TL][LDW]>(s_buf);
   float(*s_red)[2][N][RW] = reinterpret_cast<float(*)[2][N][RW]>(s_buf);
 
@@ -214,11 +225,13 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
   const int64_t plane = (int64_t)p.batch * p.dim;
 
   // ---- recurrence role: parameters and the carry entering the segment's end --
-  float A2[NS], carry[NS], dA[NS];
+  float A2[NS], rA[NS], carry[NS], dA[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     const int n = g * NS + k;
-    A2[k] = dvalid ? A[(int64_t)d * N + n] * kLog2e : 0.0f;
+    const float av = dvalid ? A[(int64_t)d * N + n] : 0.0f;
+    A2[k] = av * kLog2e;
+    rA[k] = 1.0f / av;  // used by the zero-order-hold forms only, where A = 0 takes the series
     carry[k] = (dvalid && dlast != nullptr) ? dlast[row * N + n] : 0.0f;
     dA[k] = 0.0f;
   }
@@ -346,8 +359,12 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
           float acc = 0.0f;
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
-            const float a = exp2_hw(v.x * A2[k]);
-            h[k] = __builtin_fmaf(a, h[k], v.y * bwd_rec<T>(bct + t * R, k));
+            const float x2 = v.x * A2[k];
+            const float a = exp2_hw(x2);
+            if constexpr (ZOH)
+              h[k] = __builtin_fmaf(a, h[k], zoh_coef(a, x2, v.x, rA[k]) * (v.w * bwd_rec<T>(bct + t * R, k)));
+            else
+              h[k] = __builtin_fmaf(a, h[k], v.y * bwd_rec<T>(bct + t * R, k));
             hist[t][k] = h[k];
             acc = __builtin_fmaf(bwd_rec<T>(bct + t * R, NS + k), h[k], acc);
           }
@@ -383,24 +400,36 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
 #pragma unroll
       for (int i = TR - 1; i >= 0; --i) {
         const int t = grp * TR + i;
-        float lb = 0.0f, dd = 0.0f;
+        float lb = 0.0f, la = 0.0f, dd = 0.0f;
         if (FULL || t < tvalid) {
           const float4 v = s_in[t][lane];
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
-            const float a = exp2_hw(v.x * A2[k]);
+            const float x2 = v.x * A2[k];
+            const float a = exp2_hw(x2);
             const float lam = __builtin_fmaf(v.z, bwd_rec<T>(bct + t * R, NS + k), carry[k]);
             const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hp0[k];
             const float gh = lam * hp * a;
-            dA[k] = __builtin_fmaf(gh, v.x, dA[k]);
             dd = __builtin_fmaf(gh, A2[k], dd);
-            lb = __builtin_fmaf(lam, bwd_rec<T>(bct + t * R, k), lb);
-            s_red[i][0][g * NS + k][lane] = lam * v.y;        // dB term
+            if constexpr (ZOH) {
+              // input term Bbar B u with Bbar = (Abar - 1)/A: dBbar/dDelta = Abar
+              const float coef = zoh_coef(a, x2, v.x, rA[k]);
+              const float lB = lam * bwd_rec<T>(bct + t * R, k);
+              dA[k] = __builtin_fmaf(gh, v.x, __builtin_fmaf(lB * v.w, zoh_coef_dA(a, x2, v.x, rA[k]), dA[k]));
+              lb = __builtin_fmaf(lB, coef, lb);
+              la = __builtin_fmaf(lB, a, la);
+              s_red[i][0][g * NS + k][lane] = (lam * coef) * v.w;  // dB term
+            } else {
+              dA[k] = __builtin_fmaf(gh, v.x, dA[k]);
+              lb = __builtin_fmaf(lam, bwd_rec<T>(bct + t * R, k), lb);
+              s_red[i][0][g * NS + k][lane] = lam * v.y;  // dB term
+            }
             s_red[i][1][g * NS + k][lane] = v.z * hist[t][k];  // dC term
             carry[k] = a * lam;
           }
         }
-        s_p[g][i][lane] = make_float2(lb, dd * kLn2);
+        if constexpr (ZOH) s_p[g][i][lane] = make_float4(lb, la, dd * kLn2, 0.0f);
+        else s_p[g][i][lane] = make_float2(lb, dd * kLn2);
       }
       __syncthreads();
 
@@ -424,15 +453,26 @@ __global__ __launch_bounds__(64 * G, 2) void bwd_kernel(
       for (int e = 0; e < E; ++e) {
         const int t = r0 + e;
         if (t / TR == grp && e < valid) {
-          float slb = 0.0f, sdd = 0.0f;
+          float slb = 0.0f, sla = 0.0f, sdd = 0.0f;
 #pragma unroll
           for (int gg = 0; gg < G; ++gg) {
-            const float2 q = s_p[gg][t - grp * TR][cc];
+            const SP q = s_p[gg][t - grp * TR][cc];
             slb += q.x;
-            sdd += q.y;
+            if constexpr (ZOH) {
+              sla += q.y;
+              sdd += q.z;
+            } else {
+              sdd += q.y;
+            }
           }
-          e_du[e] = __builtin_fmaf(e_ds[e], D_cc, e_dt[e] * slb);
-          const float ddx = __builtin_fmaf(e_u[e], slb, sdd) * e_sg[e];
+          float ddx;
+          if constexpr (ZOH) {  // du = ds D + sum lambda Bbar B; dDelta = u sum lambda Abar B + ...
+            e_du[e] = __builtin_fmaf(e_ds[e], D_cc, slb);
+            ddx = __builtin_fmaf(e_u[e], sla, sdd) * e_sg[e];
+          } else {              // du = ds D + Delta sum lambda B; dDelta = u sum lambda B + ...
+            e_du[e] = __builtin_fmaf(e_ds[e], D_cc, e_dt[e] * slb);
+            ddx = __builtin_fmaf(e_u[e], slb, sdd) * e_sg[e];
+          }
           e_dd[e] = ddx;
           accD = __builtin_fmaf(e_ds[e], e_u[e], accD);
           accBias += ddx;
@@ -534,7 +574,8 @@ static hipError_t launch_bwd_typed(const BwdLaunch& a, hipStream_t stream) {
     bwd_agg_kernel<T, NS, G, TL><<<(unsigned)(base * (a.nseg - 1)), 64 * G, 0, stream>>>(
         dl, a.A, bc, z, a.bias, gy, a.ws_lagg, a.ws_lsum, s);
   }
-  bwd_kernel<T, NS, G, TL><<<(unsigned)(base * a.nseg), 64 * G, 0, stream>>>(
+  auto kernel = a.zoh ? bwd_kernel<T, NS, G, TL, true> : bwd_kernel<T, NS, G, TL, false>;
+  kernel<<<(unsigned)(base * a.nseg), 64 * G, 0, stream>>>(
       u, dl, a.A, bc, a.Dskip, z, a.bias, gy, a.dlast, a.ws_ckpt, a.ws_lagg, a.ws_lsum,
       static_cast<T*>(a.du), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), a.dh0, a.ws_part_bc,
       a.ws_part_a, a.ws_part_d, a.ws_part_bias, s);

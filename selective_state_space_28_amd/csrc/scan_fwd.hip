@@ -528,7 +528,7 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   }
   s.nseg_launch = a.nseg;
   const unsigned grid = (unsigned)(base * s.nseg_launch);
-  if constexpr (MODE == 0) {  // the backward pass exists for the plain variant only
+  if constexpr ((MODE & kModeConv) == 0) {  // the backward pass covers both input terms, no prologue
     if (a.ws_ckpt != nullptr) {
       scan_kernel<T, NS, G, TL, kPassCkpt, MODE><<<grid, 64 * G, 0, stream>>>(
           u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt,
@@ -568,7 +568,7 @@ static hipError_t launch_by_mode(const ScanLaunch& a, hipStream_t stream) {
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream) {
   if (a.batch == 0 || a.dim == 0 || a.seqlen == 0) return hipSuccess;
   if (a.conv_w != nullptr && (a.conv_k < 1 || a.conv_k > kMaxConvWidth)) return hipErrorInvalidValue;
-  if (a.ws_ckpt != nullptr && (a.zoh || a.conv_w != nullptr)) return hipErrorInvalidValue;
+  if (a.ws_ckpt != nullptr && a.conv_w != nullptr) return hipErrorInvalidValue;
   return a.dtype == Dtype::BF16 ? launch_by_mode<uint16_t>(a, stream) : launch_by_mode<float>(a, stream);
 }
 

@@ -387,7 +387,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                  float* dh0, int batch, int dim, int dstate, int64_t seqlen, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  if ((flags & ~SSM_DELTA_SOFTPLUS) != 0) return SSM_ERR_FLAGS;  // Euler input term only
+  if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return SSM_ERR_SHAPE;
   const bool empty = batch == 0 || dim == 0;
   if (!empty && (!A || !dA)) return SSM_ERR_NULL;
@@ -456,6 +456,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   f.seglen = sp.seglen;
   f.nseg = sp.nseg;
   f.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
+  f.zoh = (flags & SSM_BBAR_ZOH) ? 1 : 0;
   f.vec = rows16 && aligned(u, 16) && aligned(delta, 16);
   f.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
   f.ncu = device_cu_count();
@@ -497,6 +498,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.seglen = sp.seglen;
   a.nseg = sp.nseg;
   a.softplus = f.softplus;
+  a.zoh = f.zoh;
   a.vec = rows16 && aligned(u, 16) && aligned(delta, 16) && aligned(z, 16) && aligned(dy, 16) &&
           aligned(du, 16) && aligned(ddelta, 16) && aligned(dz, 16);
   a.dtype = f.dtype;

@@ -87,6 +87,7 @@ constexpr int kMaxConvWidth = 4;
 // already run the forward checkpoint pass (launch_scan_fwd with ws_ckpt),
 // which also packs the B, C records into ws_bc.
 struct BwdLaunch {
+  int zoh;                // zero-order-hold input term (else Euler)
   const void* u;
   const void* delta;
   const float* A;

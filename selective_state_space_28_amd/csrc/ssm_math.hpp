@@ -59,6 +59,26 @@ __device__ __forceinline__ float zoh_coef(float a, float x2, float dt, float rA)
   return __builtin_fabsf(x2) < kZohSeriesX2 ? series : direct;
 }
 
+// d/dA of the zero-order-hold coefficient (exp(Delta A) - 1)/A, for the
+// backward pass: (x e^x - e^x + 1)/A^2 with x = Delta A, i.e. Delta^2 f(x)
+// with f(x) = 1/2 + x/3 + x^2/8 + x^3/30 + x^4/144 + x^5/840 + ... (the
+// series of (x e^x - e^x + 1)/x^2, term m-2 being (m-1)/m!).  The series is
+// taken where abs(x) < 1/4 (truncation below 1e-7 relative; it is also the
+// A = 0 limit Delta^2/2), the closed form elsewhere (its cancellation costs
+// under 1e-6 relative there); both are computed and one is selected.
+__device__ __forceinline__ float zoh_coef_dA(float a, float x2, float dt, float rA) {
+  const float x = x2 * kLn2;
+  const float f = __builtin_fmaf(
+      x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 840.0f, 1.0f / 144.0f),
+                                                                 1.0f / 30.0f),
+                                          1.0f / 8.0f),
+                        1.0f / 3.0f),
+      0.5f);
+  const float series = dt * dt * f;
+  const float direct = __builtin_fmaf(x, a, 1.0f - a) * (rA * rA);
+  return __builtin_fabsf(x) < 0.25f ? series : direct;
+}
+
 __device__ __forceinline__ float silu_f32(float z) {
   return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
 }

@@ -197,9 +197,10 @@ def ssm_scan_bwd_workspace_bytes(batch: int, dim: int, dstate: int, seqlen: int,
 
 
 def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                 h0=None, *, dy, dlast_state=None, workspace=None):
-    """Gradients through ssm_scan_fwd (Euler input term) given dy = dL/dy
-    and optionally dL/dlast_state; the states are recomputed, not stored.
+                 h0=None, *, dy, dlast_state=None, bbar="euler", workspace=None):
+    """Gradients through ssm_scan_fwd (input term `bbar`: "euler" or "zoh")
+    given dy = dL/dy and optionally dL/dlast_state; the states are
+    recomputed, not stored.
     Returns a dict: du, ddelta, dz (None without z) and dB, dC in the input
     dtype; dA, dD, ddelta_bias, dh0 in float32."""
     lib = load()
@@ -236,7 +237,7 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
         workspace = None
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), _flags(delta_softplus, "euler"), _ptr(h0), _ptr(dy),
+                          _ptr(delta_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(dy),
                           _ptr(dlast_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
                           _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
                           _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, dim, N, L, code,

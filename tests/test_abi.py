@@ -184,7 +184,7 @@ def _bwd(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(fl=2), FLAGS), (dict(fl=3), FLAGS), (dict(fl=4), FLAGS), (dict(dtype=7), DTYPE),
+    (dict(fl=4), FLAGS), (dict(fl=5), FLAGS), (dict(fl=-1), FLAGS), (dict(dtype=7), DTYPE),
     (dict(dstate=12), SHAPE), (dict(L=-3), SHAPE),
     (dict(dy=None), NULL), (dict(du=None), NULL), (dict(dA=None), NULL), (dict(dB=None), NULL),
     (dict(z=P + 0xB0000), NULL),

@@ -35,7 +35,7 @@ def _case(dtype, b=2, d=70, n=16, L=77, seed=11, gate=True, dskip=True, jitter=0
     return inp
 
 
-def gpu_bwd(inp, dev, h0=None, dlast=None, softplus=True):
+def gpu_bwd(inp, dev, h0=None, dlast=None, softplus=True, bbar="euler"):
     import torch
     import selective_state_space_28_amd as ssm
     dt = inp["dtype"]
@@ -43,16 +43,17 @@ def gpu_bwd(inp, dev, h0=None, dlast=None, softplus=True):
     A, D, bias = (to_torch(inp.get(k), "f32", dev) for k in ("A", "D", "delta_bias"))
     g = ssm.ssm_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias,
                          delta_softplus=softplus, h0=to_torch(h0, "f32", dev), dy=t["dy"],
-                         dlast_state=to_torch(dlast, "f32", dev))
+                         dlast_state=to_torch(dlast, "f32", dev), bbar=bbar)
     torch.cuda.synchronize(dev)
     return {k: (None if v is None else v.float().cpu().numpy().astype(np.float64)) for k, v in g.items()}
 
 
-def oracle_bwd(inp, h0=None, dlast=None, softplus=True, nthreads=8):
+def oracle_bwd(inp, h0=None, dlast=None, softplus=True, nthreads=8, bbar="euler"):
     w = widened(inp)
     dy = synth.widen(inp["dy"], inp["dtype"])
     return oracle.scan_bwd(w["u"], w["delta"], w["A"], w["B"], w["C"], w["D"], w["z"],
-                           w["delta_bias"], softplus, h0, dy=dy, dlast=dlast, nthreads=nthreads)
+                           w["delta_bias"], softplus, h0, dy=dy, dlast=dlast, nthreads=nthreads,
+                           bbar=bbar)
 
 
 def _compare(g, r, dtype, skip=()):
@@ -139,3 +140,49 @@ def test_bwd_full_size_c1(dev):
     print("c1 backward: oracle", flush=True)
     r = oracle_bwd(inp, nthreads=16)
     _compare(g, r, "f32")
+
+
+# ---- the zero-order-hold input term (Bbar = (Abar - 1)/A) ---------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 4, 16])
+def test_bwd_zoh_dstate_variants(dev, dtype, n):
+    inp = _case(dtype, n=n, L=93, seed=400 + n)
+    _compare(gpu_bwd(inp, dev, bbar="zoh"), oracle_bwd(inp, bbar="zoh"), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 129, 100), (1, 200, 1031)])
+def test_bwd_zoh_shapes(dev, dtype, shape):
+    b, d, L = shape
+    inp = _case(dtype, b=b, d=d, L=L, seed=4000 + b * 1000 + d + L)
+    _compare(gpu_bwd(inp, dev, bbar="zoh"), oracle_bwd(inp, bbar="zoh"), dtype)
+
+
+def test_bwd_zoh_zero_and_tiny_A_h0_dlast(dev):
+    """A = 0 and |Delta A| below the series threshold take the series forms of
+    Bbar and dBbar/dA (Delta and Delta^2/2 at A = 0); h0, dlast, no softplus."""
+    inp = _case("f32", b=2, d=70, L=130, seed=410)
+    inp["delta_bias"] = None
+    inp["delta"] = np.abs(inp["delta"]) * np.float32(0.2)
+    inp["A"] = inp["A"].copy()
+    inp["A"][0, :] = 0.0
+    inp["A"][1, :] = -1e-4
+    inp["A"][2, :] = -0.5          # |Delta A| around the series threshold
+    rng = np.random.default_rng(11)
+    h0 = rng.standard_normal((2, 70, 16)).astype(np.float32)
+    dlast = rng.standard_normal((2, 70, 16)).astype(np.float32)
+    g = gpu_bwd(inp, dev, h0=h0, dlast=dlast, softplus=False, bbar="zoh")
+    r = oracle_bwd(inp, h0=h0, dlast=dlast, softplus=False, bbar="zoh")
+    _compare(g, r, "f32")
+
+
+@pytest.mark.parametrize("segs", [3])
+def test_bwd_zoh_segment_carries(dev, segs, monkeypatch):
+    monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+    inp = _case("bf16", b=2, d=100, L=1037, seed=420)
+    rng = np.random.default_rng(12)
+    h0 = (rng.standard_normal((2, 100, 16)) * 0.3).astype(np.float32)
+    dlast = rng.standard_normal((2, 100, 16)).astype(np.float32)
+    _compare(gpu_bwd(inp, dev, h0=h0, dlast=dlast, bbar="zoh"),
+             oracle_bwd(inp, h0=h0, dlast=dlast, bbar="zoh"), "bf16")
