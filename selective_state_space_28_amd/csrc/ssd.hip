@@ -167,15 +167,17 @@ __device__ __forceinline__ void buf_load_run8(const Buf& b, uint32_t voff, uint3
   }
 }
 
+// A run of 4 elements of T (8 or 16 bytes) at voff + soff.
 template <typename T>
-__device__ __forceinline__ void buf_store_run8(const Buf& b, uint32_t voff, uint32_t soff,
-                                               const float (&f)[8]) {
-  uint32_t w[kRunWords<T>];
-  pack_floats<T, 8>(f, w);
-#pragma unroll
-  for (int i = 0; i < kRunWords<T> / 4; ++i) {
-    const u32x4_t v = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-    __builtin_amdgcn_raw_buffer_store_b128(v, b.r, voff + 16 * i, soff, 0);
+__device__ __forceinline__ void buf_load_run4(const Buf& b, uint32_t voff, uint32_t soff,
+                                              uint32_t (&w)[kRunWords<T> / 2]) {
+  if constexpr (sizeof(T) == 2) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(b.r, voff, soff, 0);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(b.r, voff, soff, 0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   }
 }
 
@@ -212,6 +214,13 @@ __device__ __forceinline__ void tile_column(const uint32_t (&tile)[8][kRunWords<
   }
 }
 
+// Element j (0..3) of a 4-element run, as float.
+template <typename T>
+__device__ __forceinline__ float run_elem4(const uint32_t (&w)[kRunWords<T> / 2], int j) {
+  if constexpr (sizeof(T) == 2) return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+  else return __uint_as_float(w[j]);
+}
+
 // Element j (0..7) of a run, as float.
 template <typename T>
 __device__ __forceinline__ float run_elem(const uint32_t (&w)[kRunWords<T>], int j) {
@@ -238,10 +247,6 @@ __device__ __forceinline__ void lds_store_states(typename Mma<T>::Op* row, int n
   }
 }
 
-// Column of step t in a row of the output staging: the second half of the
-// row is shifted by 4, so 8 lanes reading 8-step runs of one row, and 8 lanes
-// writing 4-step runs of 8 rows, each touch all 32 banks once.
-__device__ __forceinline__ int ystage_col(int t) { return t + ((t >> 5) << 2); }
 
 // A raw element of T as a matrix-core operand.
 __device__ __forceinline__ __bf16 as_operand(uint16_t v) { return __builtin_bit_cast(__bf16, v); }
@@ -380,7 +385,6 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   constexpr int XI = P * (Q / 8) / 256;        // 8-step runs of x (and z, y) per thread
   constexpr int NR = N * (Q / 8);              // 8-element runs of B (and of B^T, C^T) per chunk
   constexpr int NI = (NR + 255) / 256;         // ... per thread
-  constexpr int YL = Q + 4;        // row length of the output staging [p][t]
   static_assert(N % 16 == 0 && N >= 16 && N <= 128, "state count");
   static_assert(P == Q && XI * 256 == P * (Q / 8), "staging layout");
 
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   __shared__ __align__(16) Op sXw[P][LQ];    // x o exp(cum_Q - cum_s) Bbar_s, [p][s]
   __shared__ __align__(16) Op sB[N][LQ];     // B chunk, [n][s]
   __shared__ __align__(16) Op sCt[Q][LN];    // C^T, [t][n]
-  __shared__ __align__(16) float sY[P][YL]; // the output staging, [p][t] (columns ystage_col(t))
+  __shared__ __align__(16) Op sY[P][LQ];     // y in the storage type, [p][t], before its 16-byte stores
   __shared__ __align__(16) Op sM[Q][LQ];     // the masked chunk matrix, [t][s]
   // per step of the chunk: cum2_t = log2 e * sum_{k<=t} Delta_k A and the input
   // coefficient Bbar_t
@@ -409,11 +413,11 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   // so that an off-diagonal mask entry exp2(cum_t - cum_s) Bbar_s (s < 16i <= t)
   // is sE1[t] sW2[i][s]: both factors are partial decays over [s, t], never
   // beyond the entry itself.
-  float* const sE0 = &sY[0][0];
+  float* const sE0 = reinterpret_cast<float*>(&sY[0][0]);
   float* const sW = sE0 + Q;
   float* const sE1 = sW + Q;
   float(*const sW2)[Q] = reinterpret_cast<float(*)[Q]>(sE1 + Q);  // rows 1..3 used
-  static_assert(P * YL >= 7 * Q, "the factors fit in the output staging");
+  static_assert((int)sizeof(Op) * P * LQ >= 7 * Q * (int)sizeof(float), "the factors fit in the output staging");
 
   // Consecutive block ids go to different XCDs; regroup so that the heads an
   // XCD runs share batch rows (and hence B, C^T and the G tiles in its L2).
@@ -464,14 +468,18 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
       H[k][r] = h0 != nullptr ? h0[((int64_t)b * dim + h * P + pp) * N + n] : 0.0f;
     }
   }
-  float Dc[XI];  // the skip weight of each x run's channel
-#pragma unroll
-  for (int k = 0; k < XI; ++k) Dc[k] = Dskip != nullptr ? Dskip[h * P + (tid + 256 * k) / 8] : 0.0f;
+  // Output role: the Y tiles leave the products in accumulator layout, so
+  // lane l of wave w holds channel py = 16w + l % 16 and, in t-block i, steps
+  // 16i + ty .. +3 (ty = 4 (l / 16)); it forms those y and stages them.
+  const int py = 16 * w + (lane & 15);
+  const int ty = 4 * (lane >> 4);
+  const float Dp = Dskip != nullptr ? Dskip[h * P + py] : 0.0f;
 
   // A chunk's inputs in registers.  Whole chunks (FULL) take straight vector
   // loads and stores, so the only memory operations in flight across the
   // loop are in program order; the ragged last chunk takes element accesses.
-  uint32_t rx[XI][RW], rz[XI][RW], rb[NI][RW], rct[NI][RW];
+  uint32_t rx[XI][RW], rb[NI][RW], rct[NI][RW];
+  uint32_t rz[Q / 16][RW / 2];  // z of the output role's 4 runs of 4 steps
   float4 rg[3];  // this wave's causal tiles of G (wave_mask_tile(w, k))
   T rdt = T(0);  // raw: converted where it is used, so the load is not waited for early
   // whole chunks: buffer accesses with fixed per-lane offsets.  Run item k of
@@ -480,6 +488,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   constexpr uint32_t ES = sizeof(T);
   const uint32_t vo_run = ((uint32_t)(tid / 8) * (uint32_t)L + 8u * (uint32_t)(tid % 8)) * ES;
   const uint32_t vo_ct = (uint32_t)tid * 8u * ES;
+  const uint32_t vo_z = ((uint32_t)py * (uint32_t)L + (uint32_t)ty) * ES;  // z of the output role
   const Buf bufx = make_buf(xh, (int64_t)P * L * ES);
   const Buf bufz = make_buf(GATE ? zh : xh, (int64_t)P * L * ES);
   const Buf bufy = make_buf(yh, (int64_t)P * L * ES);
@@ -549,16 +558,18 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   };
   auto load_gate = [&](auto full_c, int64_t c0) {
     constexpr bool FULL = decltype(full_c)::value;
-    if constexpr (FULL) {
 #pragma unroll
-      for (int k = 0; k < XI; ++k) buf_load_run8<T>(bufz, vo_run, row_soff(k, c0), rz[k]);
-    } else {
-      const int tv = (int)(L - c0 < Q ? L - c0 : Q);
+    for (int i = 0; i < Q / 16; ++i) {
+      if constexpr (FULL) {
+        buf_load_run4<T>(bufz, vo_z, (uint32_t)((c0 + 16 * i) * ES), rz[i]);
+      } else {
+        float f[4];
 #pragma unroll
-      for (int k = 0; k < XI; ++k) {
-        const int item = tid + 256 * k;
-        const int t8 = 8 * (item % 8);
-        load_run8<T>(zh + (int64_t)(item / 8) * L + c0 + t8, false, tv - t8, rz[k]);
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = c0 + 16 * i + ty + r;
+          f[r] = t < L ? Elem<T>::load(zh + (int64_t)py * L + t) : 0.0f;
+        }
+        pack_floats<T, 4>(f, rz[i]);
       }
     }
   };
@@ -703,11 +714,23 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         // the state entering the chunk
 #pragma unroll
         for (int m = 0; m < NPK; ++m) yo = Mma<T>::mma_state(&sCt[16 * i][PS * m], LN, hp[m], yo, lane);
-        const int t0 = 16 * i + 4 * (lane >> 4);
-        *reinterpret_cast<float4*>(&sY[16 * w + (lane & 15)][ystage_col(t0)]) =
-            make_float4(yd[0] + yo[0], yd[1] + yo[1], yd[2] + yo[2], yd[3] + yo[3]);
+        // y = (Y + D x) silu(z) for this lane's 4 steps, staged in the storage type
+        const int tc = 16 * i + ty;
+        uint32_t xr[RW / 2];
+        load_words<RW / 2>(&sX[py][tc], xr);
+        float yv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = __builtin_fmaf(Dp, run_elem4<T>(xr, r), yd[r] + yo[r]);
+          if constexpr (GATE) v *= silu_f32(run_elem4<T>(rz[i], r));
+          yv[r] = v;
+        }
+        uint32_t yw[RW / 2];
+        pack_floats<T, 4>(yv, yw);
+        store_words<RW / 2>(&sY[py][tc], yw);
       }
     }
+    if constexpr (FULL && GATE) load_gate(full_c, next);  // this chunk's z are used
     // ---- H <- exp(cum_Q) H + B (x o w)^T ----------------------------------------------------
     {
       const float decay = exp2_hw(cum2Q);
@@ -726,30 +749,26 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     }
     __syncthreads();
 
-    // ---- (4) y = (Y + D x) silu(z) -----------------------------------------------------
+    // ---- (4) the staged y out, 16-byte runs along the rows ------------------------------
 #pragma unroll
     for (int k = 0; k < XI; ++k) {
       const int item = tid + 256 * k;
       const int pp = item / 8, t8 = 8 * (item % 8);
-      uint32_t xw[RW];
-      load_words<RW>(&sX[pp][t8], xw);
-      float yv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = __builtin_fmaf(Dc[k], run_elem<T>(xw, j), sY[pp][ystage_col(t8) + j]);
-        if constexpr (GATE) v *= silu_f32(run_elem<T>(rz[k], j));
-        yv[j] = v;
-      }
+      uint32_t yw[RW];
+      load_words<RW>(&sY[pp][t8], yw);
       if constexpr (FULL) {
-        buf_store_run8<T>(bufy, vo_run, row_soff(k, t0), yv);
+#pragma unroll
+        for (int q = 0; q < RW / 4; ++q) {
+          const u32x4_t v = {yw[4 * q], yw[4 * q + 1], yw[4 * q + 2], yw[4 * q + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(v, bufy.r, vo_run + 16 * q, row_soff(k, t0), 0);
+        }
       } else {
         const int64_t off = (int64_t)pp * L + t0 + t8;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (t8 + j < tvalid) Elem<T>::store(yh + off + j, yv[j]);
+          if (t8 + j < tvalid) Elem<T>::store(yh + off + j, run_elem<T>(yw, j));
       }
     }
-    if constexpr (FULL && GATE) load_gate(full_c, next);
     __syncthreads();
   };
 
