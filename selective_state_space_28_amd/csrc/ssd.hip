@@ -403,9 +403,8 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   // coefficient Bbar_t
   __shared__ __align__(16) float sCum2[Q];
   __shared__ __align__(16) float sCoef[Q];
-  // Per-step factors, written by wave 0 after the prefix sum and read in the
-  // mask step, in the output staging while it is free (cum_t as above, c_i =
-  // cum_{16i}):
+  // Per-step factors, written after the prefix sum and read in step 2 (cum_t
+  // as above, c_i = cum_{16i}):
   //   sE0[t]    = exp2(cum_t)                      scales row t of C^T
   //   sW[s]     = exp2(cum_Q - cum_s) Bbar_s       scales x for the state update
   //   sE1[t]    = exp2(cum_t - c_{t/16})
@@ -413,11 +412,11 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   // so that an off-diagonal mask entry exp2(cum_t - cum_s) Bbar_s (s < 16i <= t)
   // is sE1[t] sW2[i][s]: both factors are partial decays over [s, t], never
   // beyond the entry itself.
-  float* const sE0 = reinterpret_cast<float*>(&sY[0][0]);
+  __shared__ __align__(16) float sFac[7 * Q];
+  float* const sE0 = sFac;
   float* const sW = sE0 + Q;
   float* const sE1 = sW + Q;
   float(*const sW2)[Q] = reinterpret_cast<float(*)[Q]>(sE1 + Q);  // rows 1..3 used
-  static_assert((int)sizeof(Op) * P * LQ >= 7 * Q * (int)sizeof(float), "the factors fit in the output staging");
 
   // Consecutive block ids go to different XCDs; regroup so that the heads an
   // XCD runs share batch rows (and hence B, C^T and the G tiles in its L2).
@@ -769,7 +768,9 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
           if (t8 + j < tvalid) Elem<T>::store(yh + off + j, run_elem<T>(yw, j));
       }
     }
-    __syncthreads();
+    // no barrier: the next chunk's step 1 writes neither the staging nor
+    // anything read here, and its step 3 (which rewrites the staging) comes
+    // after two barriers that every wave reaches only past this step
   };
 
   // whole chunks while the rows allow 16-byte accesses, then the rest
