@@ -90,3 +90,72 @@ def test_decode_graph_replays(dev):
         for s in range(cfg.steps):
             assert torch.equal(ys[s].view(torch.int16), ys_ref[s].view(torch.int16)), (i, s)
         assert torch.equal(state, st_ref), f"replay {i}"
+
+
+def test_ssd_graph_replays(dev):
+    """The SSD scan (prep kernel + chunked scan) captured and replayed."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    from synth.configs import SsdConfig
+    inp = synth.make_ssd_inputs(SsdConfig("g", 2, 3, 64, 64, 300, "bf16", seed=34))
+    t = {k: to_torch(inp[k], "bf16", dev) for k in ("x", "dt", "B", "C", "z")}
+    A, D, bias = (to_torch(inp[k], "f32", dev) for k in ("A", "D", "dt_bias"))
+    ref = ssm.ssm_ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], D, t["z"], bias)
+    torch.cuda.synchronize()
+    y = torch.empty_like(t["x"])
+    ws = torch.empty(ssm.ssm_ssd_scan_fwd_workspace_bytes(2, 64, 300, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: ssm.ssm_ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], D, t["z"], bias, out=y, workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(4):
+        y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        ssm.ssm_ssd_scan_fwd(t["x"][:1].contiguous(), t["dt"][:1].contiguous(), A, t["B"][:1].contiguous(),
+                             t["C"][:1].contiguous(), None, None, None)  # eager work in between
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+def test_bwd_graph_replays(dev, bbar):
+    """The backward (checkpoint pass, sweep, sums) captured and replayed; its
+    outputs are bit-deterministic, so every replay must equal the eager call."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    inp = synth.make_scan_inputs(ScanConfig("g", 2, 96, 16, 300, "bf16", seed=35))
+    t = {k: to_torch(inp[k], "bf16", dev) for k in ("u", "delta", "B", "C", "z")}
+    A, D, bias = (to_torch(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    dy = torch.randn(t["u"].shape, generator=torch.Generator(device=dev).manual_seed(6), device=dev).to(torch.bfloat16)
+    ws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(2, 96, 16, 300, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: ssm.ssm_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias, dy=dy, bbar=bbar,
+                                   workspace=ws)
+    ref = {k: (None if v is None else v.clone()) for k, v in run().items()}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = run()
+    for i in range(3):
+        for v in out.values():
+            if v is not None:
+                v.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in out.items():
+            if v is not None:
+                assert torch.equal(v, ref[k]), (i, k)
+        ssm.ssm_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], None, None, None)  # eager work in between
+        torch.cuda.synchronize()
