@@ -201,6 +201,9 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   // the Abar part, -)
   using SP = typename std::conditional<ZOH, float4, float2>::type;
   __shared__ SP s_p[G][TR][LDW];
+  // this tile's B, C records of every state group as floats, [g][t][q]: loaded
+  // a tile ahead with the other inputs, read by each wave as broadcasts
+  __shared__ __align__(16) float s_rec[G][TL][R];
   float(*s_y)[TL][LDW] = reinterpret_cast<float(*)[TL][LDW]>(s_buf);
   float(*s_red)[2][N][RW] = reinterpret_cast<float(*)[2][N][RW]>(s_buf);
 
@@ -268,7 +271,6 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   const int rn = (ro / TR) % N;
   const int rw = ro / (TR * N);
 
-  const T* bcw = bc + ((int64_t)b * G + g) * L * R;
   float hist[TL][NS];
 
   // A whole tile (FULL: all TL steps in the segment, rows 16-byte aligned) takes
@@ -280,12 +282,31 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   constexpr bool PF = W <= 4;
   uint32_t pu[W], pd[W], pg[W], pz[W];  // the next whole tile's runs, raw
   float pck[NS];                          // and the state entering it
+  // record staging: pair q of the tile's G * TL * R record values (group q /
+  // (TL R / 2), values 2 (q % (TL R / 2)) and the next), one pair per thread
+  constexpr int NPAIR = G * TL * R / 2;
+  constexpr int PW = (int)sizeof(T) / 2;  // words of a pair
+  static_assert(NPAIR <= 64 * G, "one record pair per thread at most");
+  const bool rec_thread = tid < NPAIR;
+  const int rec_g = tid / (TL * R / 2), rec_e = 2 * (tid % (TL * R / 2));
+  const T* bc_rec = bc + ((int64_t)b * G + (rec_thread ? rec_g : 0)) * L * R + rec_e;
+  uint32_t prec[PW];
+  auto load_rec = [&](int64_t t0, bool guard, uint32_t (&w)[PW]) {
+    const int tt = rec_e / R;  // the step of this pair (both values share it: R is even)
+    if (!rec_thread || (guard && t0 + tt >= L)) {
+#pragma unroll
+      for (int i = 0; i < PW; ++i) w[i] = 0u;
+    } else {
+      load_words<PW>(bc_rec + t0 * R, w);
+    }
+  };
   auto prefetch = [&](int64_t t0) {
     const int64_t off = rowcc * L + t0 + r0;
     load_words<W>(u + off, pu);
     load_words<W>(delta + off, pd);
     load_words<W>(dy + off, pg);
     if (has_z) load_words<W>(z + off, pz);
+    load_rec(t0, false, prec);
 #pragma unroll
     for (int k = 0; k < NS; ++k)
       pck[k] = dvalid ? ckpt[(((int64_t)b * ntiles + t0 / TL) * N + g * NS + k) * p.dim + d] : 0.0f;
@@ -334,10 +355,23 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
         s_in[r0 + e][cc] = make_float4(dt, dt * uu[e], ds, uu[e]);
       }
     }
+    {
+      uint32_t rw[PW];
+      if constexpr (FULL) {
+#pragma unroll
+        for (int i = 0; i < PW; ++i) rw[i] = prec[i];
+      } else {
+        load_rec(t0, true, rw);
+      }
+      if (rec_thread) {
+        float f[2];
+        words_to_floats<T, 2>(rw, f);
+        *reinterpret_cast<float2*>(&s_rec[rec_g][rec_e / R][rec_e % R]) = make_float2(f[0], f[1]);
+      }
+    }
     __syncthreads();
 
     // ---- recompute the tile's states from its checkpoint ------------------------
-    const T* bct = bcw + t0 * R;
     float hp0[NS];
     if constexpr (FULL) {
 #pragma unroll
@@ -362,11 +396,11 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
             const float x2 = v.x * A2[k];
             const float a = exp2_hw(x2);
             if constexpr (ZOH)
-              h[k] = __builtin_fmaf(a, h[k], zoh_coef(a, x2, v.x, rA[k]) * (v.w * bwd_rec<T>(bct + t * R, k)));
+              h[k] = __builtin_fmaf(a, h[k], zoh_coef(a, x2, v.x, rA[k]) * (v.w * s_rec[g][t][k]));
             else
-              h[k] = __builtin_fmaf(a, h[k], v.y * bwd_rec<T>(bct + t * R, k));
+              h[k] = __builtin_fmaf(a, h[k], v.y * s_rec[g][t][k]);
             hist[t][k] = h[k];
-            acc = __builtin_fmaf(bwd_rec<T>(bct + t * R, NS + k), h[k], acc);
+            acc = __builtin_fmaf(s_rec[g][t][NS + k], h[k], acc);
           }
           s_y[g][t][lane] = acc;
         }
@@ -407,21 +441,21 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
           for (int k = 0; k < NS; ++k) {
             const float x2 = v.x * A2[k];
             const float a = exp2_hw(x2);
-            const float lam = __builtin_fmaf(v.z, bwd_rec<T>(bct + t * R, NS + k), carry[k]);
+            const float lam = __builtin_fmaf(v.z, s_rec[g][t][NS + k], carry[k]);
             const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hp0[k];
             const float gh = lam * hp * a;
             dd = __builtin_fmaf(gh, A2[k], dd);
             if constexpr (ZOH) {
               // input term Bbar B u with Bbar = (Abar - 1)/A: dBbar/dDelta = Abar
               const float coef = zoh_coef(a, x2, v.x, rA[k]);
-              const float lB = lam * bwd_rec<T>(bct + t * R, k);
+              const float lB = lam * s_rec[g][t][k];
               dA[k] = __builtin_fmaf(gh, v.x, __builtin_fmaf(lB * v.w, zoh_coef_dA(a, x2, v.x, rA[k]), dA[k]));
               lb = __builtin_fmaf(lB, coef, lb);
               la = __builtin_fmaf(lB, a, la);
               s_red[i][0][g * NS + k][lane] = (lam * coef) * v.w;  // dB term
             } else {
               dA[k] = __builtin_fmaf(gh, v.x, dA[k]);
-              lb = __builtin_fmaf(lam, bwd_rec<T>(bct + t * R, k), lb);
+              lb = __builtin_fmaf(lam, s_rec[g][t][k], lb);
               s_red[i][0][g * NS + k][lane] = lam * v.y;  // dB term
             }
             s_red[i][1][g * NS + k][lane] = v.z * hist[t][k];  // dC term
