@@ -14,11 +14,13 @@
 //   Y     = M X^T + diag(exp(cum_t)) C^T H        (Q x P,  K = Q and K = N)
 //   H    <- exp(cum_Q) H + (B o exp(cum_Q - cum_s) Bbar_s) X^T   (N x P, K = Q)
 //
-// then y = Y + D x, times silu(z).  One workgroup (4 waves) owns a
-// (batch row, head) and walks its chunks in order; H never leaves the
-// matrix-core accumulators (registers), so HBM sees x, delta, z, y and the
-// B, C rows once.  Bbar_s is Delta_s (Euler) or (exp(Delta_s A) - 1)/A
-// (zero-order hold), as in the diagonal scan.
+// then y = Y + D x, times silu(z).  G does not depend on the head: a prep
+// kernel forms its causal tiles once per (batch row, chunk), with C^T, into
+// the workspace.  Then one workgroup (4 waves) owns a (batch row, head) and
+// walks its chunks in order; H never leaves the matrix-core accumulators
+// (registers), so HBM sees x, delta, z and y once, and B, C^T and G once per
+// XCD that runs the row's heads.  Bbar_s is Delta_s (Euler) or
+// (exp(Delta_s A) - 1)/A (zero-order hold), as in the diagonal scan.
 #include "ssm_kernels.hpp"
 #include "ssm_math.hpp"
 
@@ -247,10 +249,6 @@ __device__ __forceinline__ void lds_store_states(typename Mma<T>::Op* row, int n
   }
 }
 
-
-// A raw element of T as a matrix-core operand.
-__device__ __forceinline__ __bf16 as_operand(uint16_t v) { return __builtin_bit_cast(__bf16, v); }
-__device__ __forceinline__ float as_operand(float v) { return v; }
 
 // The 10 causal 16x16 tiles (t-block i, s-block j <= i) of a 64-step chunk
 // matrix, numbered row by row: tile q has i = the largest with i(i+1)/2 <= q.
