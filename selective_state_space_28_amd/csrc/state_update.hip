@@ -11,7 +11,11 @@
 // streaming it: NS = min(N, 4) states per lane (one 16-byte load and store),
 // P = N/NS consecutive lanes per channel, so a wave reads and writes 1 KiB of
 // state contiguously.  The P partial readouts are summed with lane shuffles
-// in a fixed order.
+// in a fixed order.  The state's loads and stores are non-temporal: a
+// channel's state is touched once per token, so keeping it in the caches
+// only displaces other lines (measured on gfx950: 37.5 -> 33 us per step at
+// batch 256, D 5120, N 16, against 35 and 37 us with only the loads or only
+// the stores marked).
 //
 // Optional convolution prologue (the decode step of the causal depthwise
 // conv1d + silu in front of the SSM): u = silu(cb + sum_k w[k] x[t-K+1+k])
@@ -21,6 +25,8 @@
 #include "ssm_math.hpp"
 
 namespace ssm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // A raw element of T as float.
 __device__ __forceinline__ float raw_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
@@ -58,7 +64,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   const float* ap = A + (int64_t)d * N + part * NS;
   uint32_t bw[2], cw[2];  // bf16 B, C of this lane's 4 states (VEC)
   if constexpr (NS == 4 && VEC) {
-    const float4 v = *reinterpret_cast<const float4*>(sp);
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp));
     h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
     const float4 a4 = *reinterpret_cast<const float4*>(ap);
     av[0] = a4.x; av[1] = a4.y; av[2] = a4.z; av[3] = a4.w;
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   } else {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      h[k] = sp[k];
+      h[k] = __builtin_nontemporal_load(sp + k);
       av[k] = ap[k];
       bv[k] = raw_f32(B[nb + k]);
       cv[k] = raw_f32(C[nb + k]);
@@ -141,10 +147,11 @@ __global__ __launch_bounds__(256) void state_update_kernel(
   }
 
   if constexpr (NS == 4 && VEC) {
-    *reinterpret_cast<float4*>(sp) = make_float4(h[0], h[1], h[2], h[3]);
+    const f32x4 o = {h[0], h[1], h[2], h[3]};
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(sp));
   } else {
 #pragma unroll
-    for (int k = 0; k < NS; ++k) sp[k] = h[k];
+    for (int k = 0; k < NS; ++k) __builtin_nontemporal_store(h[k], sp + k);
   }
 
 #pragma unroll
