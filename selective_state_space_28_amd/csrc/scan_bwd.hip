@@ -18,10 +18,11 @@
 //  3. bwd_kernel walks each segment's tiles from last to first: it
 //     recomputes the tile's 16 states from the checkpoint into registers,
 //     then sweeps the steps in reverse, carrying lambda per state and
-//     forming every gradient term.  dB and dC are sums over channels; they
-//     are reduced over the workgroup's 64 channels through LDS in groups of
-//     4 steps and written as per-channel-group partials.  dA, dD and the
-//     bias gradient are per-workgroup partials.
+//     forming every gradient term.  dB and dC are sums over channels: each
+//     wave sums its terms over its 64 channels in registers with lane
+//     exchanges (permlane swaps and DPP), a few steps at a time, and writes
+//     them as per-channel-group partials.  dA, dD and the bias gradient are
+//     per-workgroup partials.  A tile takes three workgroup barriers.
 //  4. Small kernels sum the partials in a fixed order, so results are
 //     deterministic.
 //
@@ -52,6 +53,38 @@ struct BwdSizes {
 };
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+// Sums of 16 values per lane over the 64 lanes of a wave: lane l returns the
+// total of value (l >> 2) & 15.  Each round pairs every lane with a partner;
+// the pair splits its values in halves, each lane keeps one half and adds the
+// partner's copy of it: lanes l, l^32 (v_permlane32_swap), l, l^16
+// (v_permlane16_swap), l, l^8 (DPP row_ror:8, a select for the half kept)
+// and l, l^7 (DPP row_half_mirror).  Two quad permutes then add l^2 and l^1.
+// The order of the additions is fixed, so the sums are deterministic.
+__device__ __forceinline__ float wave_sum16(const float (&v)[16], int lane) {
+  float r[8], q[4], h2[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j + 8]), false, false);
+    r[j] = __uint_as_float(s[0]) + __uint_as_float(s[1]);  // value j + 8 (l >> 5 & 1)
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(r[j]), __float_as_uint(r[j + 4]), false, false);
+    q[j] = __uint_as_float(s[0]) + __uint_as_float(s[1]);  // + 4 (l >> 4 & 1)
+  }
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float keep = b3 ? q[j + 2] : q[j], send = b3 ? q[j] : q[j + 2];
+    h2[j] = keep + dpp_moved<0x128, 0xf>(send);  // + 2 (l >> 3 & 1)
+  }
+  const float keep = b2 ? h2[1] : h2[0], send = b2 ? h2[0] : h2[1];
+  float w = keep + dpp_moved<0x141, 0xf>(send);  // + (l >> 2 & 1)
+  w += dpp_moved<0x4e, 0xf>(w);                  // quad_perm [2,3,0,1]
+  w += dpp_moved<0xb1, 0xf>(w);                  // quad_perm [1,0,3,2]
+  return w;
+}
 
 // Value q of a B, C record (scalar loads; see scan_fwd.hip for the layout).
 template <typename T>
@@ -186,26 +219,21 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
     float* __restrict__ part_bias, const BwdSizes p) {
   constexpr int N = NS * G;
   constexpr int E = TL / G;                   // elements per thread, element role
-  constexpr int TR = 4;                       // steps per dB/dC reduction group
+  constexpr int TRS = 8 / NS;                 // steps per dB/dC wave sum (16 terms a lane)
   constexpr int LDW = 65;                     // padded row, float/float2/float4 arrays
-  constexpr int RW = 68;                      // padded row of the dB/dC terms (16-byte rows)
   constexpr int R = 2 * NS;
-  constexpr int NRED = TR * 2 * N * RW;       // dB/dC terms of one group
-  constexpr int NY = G * TL * LDW;            // readout partials of one tile
-  static_assert(TL % TR == 0, "tile must split into reduction groups");
+  static_assert(NS * TRS == 8 && TL % TRS == 0, "dB/dC sums take 16 terms a lane");
 
   __shared__ float4 s_in[TL][LDW];            // (Delta, Delta*u, ds, u) per (step, channel)
-  __shared__ __align__(16) float s_buf[NRED > NY ? NRED : NY];  // readout partials, then dB/dC terms
+  __shared__ float s_y[G][TL][LDW];           // readout partials of each wave
   // per wave and step, the sums over this wave's states: Euler (sum lambda B,
   // sum of the Abar part of dDelta); ZOH (sum lambda Bbar B, sum lambda Abar B,
   // the Abar part, -)
   using SP = typename std::conditional<ZOH, float4, float2>::type;
-  __shared__ SP s_p[G][TR][LDW];
+  __shared__ SP s_p[G][TL][LDW];
   // this tile's B, C records of every state group as floats, [g][t][q]: loaded
   // a tile ahead with the other inputs, read by each wave as broadcasts
   __shared__ __align__(16) float s_rec[G][TL][R];
-  float(*s_y)[TL][LDW] = reinterpret_cast<float(*)[TL][LDW]>(s_buf);
-  float(*s_red)[2][N][RW] = reinterpret_cast<float(*)[2][N][RW]>(s_buf);
 
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
@@ -260,18 +288,12 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   const bool has_z = z != nullptr;
   float accD = 0.0f, accBias = 0.0f;
 
-  // ---- reduction role (dB/dC): thread -> (output, part of the 64 lanes) --------
-  constexpr int NOUT = TR * 2 * N;
-  constexpr int TPO = (64 * G) / NOUT;        // threads per output
-  constexpr int LPT = 64 / TPO;               // lanes each of them sums
-  static_assert(TPO >= 1 && TPO * NOUT == 64 * G && LPT % 4 == 0, "reduction layout");
-  const int ro = tid / TPO;
-  const int rpart = tid % TPO;
-  const int ri = ro % TR;
-  const int rn = (ro / TR) % N;
-  const int rw = ro / (TR * N);
-
   float hist[TL][NS];
+  // where this lane writes its wave sums of the dB, dC terms (lanes 4o write
+  // term o of a group; see the reverse sweep)
+  const int so = lane >> 2;
+  float* const pbc = part_bc + ((((int64_t)b * p.ncg + cg) * 2 + (so >> 3)) * N + g * NS + (so / TRS) % NS) * L +
+                     so % TRS;
 
   // A whole tile (FULL: all TL steps in the segment, rows 16-byte aligned) takes
   // its element runs and its checkpoint from registers loaded while the
@@ -422,18 +444,20 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
       }
       if (valid > 0) store_run<T, E>(dz, eoff, vec_ok, valid, zo);
     }
-    __syncthreads();  // the readout partials share their memory with the dB/dC terms
 
-    // ---- reverse sweep, in groups of TR steps ------------------------------------
-    float e_du[E], e_dd[E];
+    // ---- reverse sweep, in groups of TRS steps ----------------------------------
+    // A group's 16 dB and dC terms per lane (TRS steps x NS states) are summed
+    // over the wave's 64 channels in registers; the per-step sums over the
+    // wave's states, for du and d(delta), go to LDS for the whole tile.
 #pragma unroll
-    for (int e = 0; e < E; ++e) e_du[e] = e_dd[e] = 0.0f;
+    for (int grp = TL / TRS - 1; grp >= 0; --grp) {
+      if (!FULL && grp * TRS >= tvalid) continue;  // uniform: a ragged last tile
+      float terms[16];  // [w * 8 + k * TRS + i]: w = 0 the dB term, 1 the dC term
 #pragma unroll
-    for (int grp = TL / TR - 1; grp >= 0; --grp) {
-      if (!FULL && grp * TR >= tvalid) continue;  // uniform: a ragged last tile
+      for (int q = 0; q < 16; ++q) terms[q] = 0.0f;
 #pragma unroll
-      for (int i = TR - 1; i >= 0; --i) {
-        const int t = grp * TR + i;
+      for (int i = TRS - 1; i >= 0; --i) {
+        const int t = grp * TRS + i;
         float lb = 0.0f, la = 0.0f, dd = 0.0f;
         if (FULL || t < tvalid) {
           const float4 v = s_in[t][lane];
@@ -452,67 +476,56 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
               dA[k] = __builtin_fmaf(gh, v.x, __builtin_fmaf(lB * v.w, zoh_coef_dA(a, x2, v.x, rA[k]), dA[k]));
               lb = __builtin_fmaf(lB, coef, lb);
               la = __builtin_fmaf(lB, a, la);
-              s_red[i][0][g * NS + k][lane] = (lam * coef) * v.w;  // dB term
+              terms[k * TRS + i] = (lam * coef) * v.w;
             } else {
               dA[k] = __builtin_fmaf(gh, v.x, dA[k]);
               lb = __builtin_fmaf(lam, s_rec[g][t][k], lb);
-              s_red[i][0][g * NS + k][lane] = lam * v.y;  // dB term
+              terms[k * TRS + i] = lam * v.y;
             }
-            s_red[i][1][g * NS + k][lane] = v.z * hist[t][k];  // dC term
+            terms[8 + k * TRS + i] = v.z * hist[t][k];
             carry[k] = a * lam;
           }
+          if constexpr (ZOH) s_p[g][t][lane] = make_float4(lb, la, dd * kLn2, 0.0f);
+          else s_p[g][t][lane] = make_float2(lb, dd * kLn2);
         }
-        if constexpr (ZOH) s_p[g][i][lane] = make_float4(lb, la, dd * kLn2, 0.0f);
-        else s_p[g][i][lane] = make_float2(lb, dd * kLn2);
       }
-      __syncthreads();
+      // dB, dC of this group's steps: the sums over the 64 channels
+      const float sum = wave_sum16(terms, lane);
+      if ((lane & 3) == 0 && (FULL || grp * TRS + so % TRS < tvalid)) pbc[t0 + grp * TRS] = sum;
+    }
+    __syncthreads();
 
-      // dB, dC of this group's steps: the sum over the 64 channels
-      {
-        const float* src = &s_red[ri][rw][rn][rpart * LPT];
-        float sacc = 0.0f;
+    // ---- du and d(delta) of this thread's elements -----------------------------------
+    float e_du[E], e_dd[E];
 #pragma unroll
-        for (int q = 0; q < LPT; q += 4) {
-          const float4 v4 = *reinterpret_cast<const float4*>(src + q);
-          sacc += (v4.x + v4.y) + (v4.z + v4.w);
-        }
-#pragma unroll
-        for (int off = 1; off < TPO; off <<= 1) sacc += __shfl_xor(sacc, off);
-        const int t = grp * TR + ri;
-        if (rpart == 0 && (FULL || t < tvalid))
-          part_bc[((((int64_t)b * p.ncg + cg) * 2 + rw) * N + rn) * L + t0 + t] = sacc;
-      }
-      // du and d(delta) of this group's steps, for this thread's elements
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < E; ++e) {
+      e_du[e] = e_dd[e] = 0.0f;
+      if (e < valid) {
         const int t = r0 + e;
-        if (t / TR == grp && e < valid) {
-          float slb = 0.0f, sla = 0.0f, sdd = 0.0f;
+        float slb = 0.0f, sla = 0.0f, sdd = 0.0f;
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) {
-            const SP q = s_p[gg][t - grp * TR][cc];
-            slb += q.x;
-            if constexpr (ZOH) {
-              sla += q.y;
-              sdd += q.z;
-            } else {
-              sdd += q.y;
-            }
+        for (int gg = 0; gg < G; ++gg) {
+          const SP q = s_p[gg][t][cc];
+          slb += q.x;
+          if constexpr (ZOH) {
+            sla += q.y;
+            sdd += q.z;
+          } else {
+            sdd += q.y;
           }
-          float ddx;
-          if constexpr (ZOH) {  // du = ds D + sum lambda Bbar B; dDelta = u sum lambda Abar B + ...
-            e_du[e] = __builtin_fmaf(e_ds[e], D_cc, slb);
-            ddx = __builtin_fmaf(e_u[e], sla, sdd) * e_sg[e];
-          } else {              // du = ds D + Delta sum lambda B; dDelta = u sum lambda B + ...
-            e_du[e] = __builtin_fmaf(e_ds[e], D_cc, e_dt[e] * slb);
-            ddx = __builtin_fmaf(e_u[e], slb, sdd) * e_sg[e];
-          }
-          e_dd[e] = ddx;
-          accD = __builtin_fmaf(e_ds[e], e_u[e], accD);
-          accBias += ddx;
         }
+        float ddx;
+        if constexpr (ZOH) {  // du = ds D + sum lambda Bbar B; dDelta = u sum lambda Abar B + ...
+          e_du[e] = __builtin_fmaf(e_ds[e], D_cc, slb);
+          ddx = __builtin_fmaf(e_u[e], sla, sdd) * e_sg[e];
+        } else {              // du = ds D + Delta sum lambda B; dDelta = u sum lambda B + ...
+          e_du[e] = __builtin_fmaf(e_ds[e], D_cc, e_dt[e] * slb);
+          ddx = __builtin_fmaf(e_u[e], slb, sdd) * e_sg[e];
+        }
+        e_dd[e] = ddx;
+        accD = __builtin_fmaf(e_ds[e], e_u[e], accD);
+        accBias += ddx;
       }
-      __syncthreads();
     }
     if (valid > 0) {
       store_run<T, E>(du, eoff, vec_ok, valid, e_du);

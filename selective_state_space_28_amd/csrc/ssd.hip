@@ -338,13 +338,6 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const T* __restrict__ B, 
   }
 }
 
-// v from the lane that the DPP control CTRL names (0 where it names none, or
-// in rows that ROW_MASK leaves out).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_moved(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
-}
-
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
 // 16 lanes, then the row totals carried forward by row broadcasts.
 __device__ __forceinline__ float wave_prefix_sum(float v) {

@@ -18,6 +18,13 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// v from the lane that the DPP control CTRL names (0 where it names none, or
+// in rows that ROW_MASK leaves out).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_moved(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
 // ln(1 + w) for w in [0, 1], without branches.  u = fl(1 + w) is rounded;
 // c = w - (u - 1) is the rounding error exactly (u - 1 is exact), and
 // ln(1 + w) = ln(u + c) = ln(u) + c/u + O(c^2).  Replacing c/u by c changes
