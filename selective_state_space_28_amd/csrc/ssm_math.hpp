@@ -39,14 +39,15 @@ __device__ __forceinline__ float log1p_unit(float w) {
 }
 
 // softplus(x) = ln(1 + e^x) = max(x, 0) + ln(1 + e^-|x|): no overflow for
-// large x and no cancellation for very negative x.
+// large x and no cancellation for very negative x.  max(x, 0) is a signed
+// integer max on the bits (one instruction; a float max would first quiet
+// its input): a float with the sign bit clear is a non-negative integer.  A
+// NaN x makes w, and so the result, NaN either way.
 __device__ __forceinline__ float softplus_f32(float x) {
   const float w = exp2_hw(-__builtin_fabsf(x) * kLog2e);
-  return (x > 0.0f ? x : 0.0f) + log1p_unit(w);
+  return __int_as_float(max(__float_as_int(x), 0)) + log1p_unit(w);
 }
 
-// silu(z) = z / (1 + e^-z).  For z -> -inf the reciprocal goes to 0 and the
-// product to -0; no NaN for finite z.
 // Zero-order-hold input coefficient Bbar/B = (exp(Delta A) - 1)/A, given
 // x2 = Delta*A*log2(e), a = exp2(x2), Delta and 1/A.  Where |Delta A| < 0.1
 // the difference a - 1 would carry the rounding error of a magnified by
@@ -86,6 +87,8 @@ __device__ __forceinline__ float zoh_coef_dA(float a, float x2, float dt, float 
   return __builtin_fabsf(x) < 0.25f ? series : direct;
 }
 
+// silu(z) = z / (1 + e^-z).  For z -> -inf the reciprocal goes to 0 and the
+// product to -0; no NaN for finite z.
 __device__ __forceinline__ float silu_f32(float z) {
   return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
 }
