@@ -57,11 +57,11 @@ def oracle_ssd(inp, h0=None, bbar="euler", softplus=True, heads=None, nthreads=8
                                nthreads=nthreads, bbar=bbar)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n", [16, 32, 64, 128])
+# float32 storage takes N <= 64 (the library rejects N = 128 with it, which
+# test_abi.py checks without a GPU)
+@pytest.mark.parametrize("dtype,n", [("f32", 16), ("f32", 32), ("f32", 64),
+                                     ("bf16", 16), ("bf16", 32), ("bf16", 64), ("bf16", 128)])
 def test_ssd_dstate_variants(dev, dtype, n):
-    if dtype == "f32" and n == 128:
-        pytest.skip("128 states need the bf16 operand path (LDS)")
     inp = synth.make_ssd_inputs(SsdConfig("t", 2, 3, 64, n, 200, dtype, seed=500 + n))
     y, last = gpu_ssd(inp, dev)
     yr, lr = oracle_ssd(inp)
