@@ -467,7 +467,8 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
             const float a = exp2_hw(x2);
             const float lam = __builtin_fmaf(v.z, s_rec[g][t][NS + k], carry[k]);
             const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hp0[k];
-            const float gh = lam * hp * a;
+            const float cn = a * lam;  // the carry into step t - 1
+            const float gh = cn * hp;
             dd = __builtin_fmaf(gh, A2[k], dd);
             if constexpr (ZOH) {
               // input term Bbar B u with Bbar = (Abar - 1)/A: dBbar/dDelta = Abar
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
               terms[k * TRS + i] = lam * v.y;
             }
             terms[8 + k * TRS + i] = v.z * hist[t][k];
-            carry[k] = a * lam;
+            carry[k] = cn;
           }
           if constexpr (ZOH) s_p[g][t][lane] = make_float4(lb, la, dd * kLn2, 0.0f);
           else s_p[g][t][lane] = make_float2(lb, dd * kLn2);
