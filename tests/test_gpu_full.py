@@ -102,3 +102,43 @@ def test_full_size_decode_64_steps(dev):
     ref = np.concatenate([ref_state[b][0] for b in sample])
     serr = assert_parity(got, ref, "f32", "decode state after 64 steps")
     print(f"decode: worst y error {worst:.3e}, state error {serr:.3e}", flush=True)
+
+
+def test_full_size_c3_backward_sampled(dev):
+    """ssm_scan_bwd over the whole c3 workload (bf16, batch 16, D 5120,
+    N 16, L 2048), as bench.py times it.  The per-channel gradients (du,
+    d(delta), dz over every batch row, and dA, dD, d(bias), which sum over
+    the batch and the sequence of one channel) of a sample of channels are
+    checked against the oracle's backward of those channels alone: a
+    channel's adjoint depends only on its own inputs and the shared B, C.
+    dB and dC sum over every channel; they are checked over whole problems
+    at smaller sizes (test_gpu_bwd.py)."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    cfg = synth.SCAN_CONFIGS["c3"]
+    inp = synth.make_scan_inputs(cfg)
+    rng = np.random.default_rng([cfg.seed, 2_000_003])
+    dy = synth.bf16_bits(rng.standard_normal((cfg.batch, cfg.dim, cfg.seqlen), dtype=np.float32))
+    t = {k: to_torch(inp.get(k), cfg.dtype, dev) for k in ("u", "delta", "B", "C", "z")}
+    A, D, bias = (to_torch(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    g = ssm.ssm_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias,
+                         dy=to_torch(dy, cfg.dtype, dev))
+    torch.cuda.synchronize(dev)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
+        assert bool(torch.isfinite(g[k].float()).all()), f"{k}: non-finite values"
+    ds = _sample_channels(cfg.dim, np.random.default_rng(300 + cfg.seed), n_random=8)
+    sub = {k: (None if inp.get(k) is None else np.ascontiguousarray(inp[k][:, ds]))
+           for k in ("u", "delta", "z")}
+    w = {k: synth.widen(v, cfg.dtype) for k, v in sub.items()}
+    Bw, Cw = synth.widen(inp["B"], cfg.dtype), synth.widen(inp["C"], cfg.dtype)
+    r = oracle.scan_bwd(w["u"], w["delta"], inp["A"][ds].astype(np.float64), Bw, Cw,
+                        inp["D"][ds].astype(np.float64), w["z"], inp["delta_bias"][ds].astype(np.float64),
+                        True, None, dy=synth.widen(np.ascontiguousarray(dy[:, ds]), cfg.dtype),
+                        nthreads=16)
+    idx = torch.tensor(ds, device=dev)
+    got = {k: g[k].index_select(1, idx).float().cpu().numpy() for k in ("du", "ddelta", "dz")}
+    got.update({k: g[k].index_select(0, idx).float().cpu().numpy() for k in ("dA", "dD", "ddelta_bias")})
+    if r.get("dh0") is not None:
+        got["dh0"] = g["dh0"].index_select(1, idx).cpu().numpy()
+    errs = {k: assert_parity(got[k], r[k], "bf16", f"c3 backward {k}") for k in got}
+    print("c3 backward, sampled channels: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
