@@ -32,12 +32,13 @@ def _sample_channels(dim, rng, n_random=12):
     return sorted(c for c in fixed | rand if 0 <= c < dim)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
-def test_full_size_scan(dev, name):
+# c3 also with the zero-order-hold input term, which bench.py times too
+@pytest.mark.parametrize("name,bbar", [("c1", "euler"), ("c2", "euler"), ("c3", "euler"), ("c3", "zoh")])
+def test_full_size_scan(dev, name, bbar):
     cfg = synth.SCAN_CONFIGS[name]
-    print(f"{name}: generating {cfg.batch}x{cfg.dim}x{cfg.seqlen} N={cfg.dstate} {cfg.dtype}", flush=True)
+    print(f"{name}: generating {cfg.batch}x{cfg.dim}x{cfg.seqlen} N={cfg.dstate} {cfg.dtype} {bbar}", flush=True)
     inp = synth.make_scan_inputs(cfg)
-    y, last = gpu_scan(inp, dev)
+    y, last = gpu_scan(inp, dev, bbar=bbar)
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(last))
     rng = np.random.default_rng(100 + cfg.seed)
     batches = sorted({0, cfg.batch - 1, int(rng.integers(cfg.batch))})
@@ -45,7 +46,7 @@ def test_full_size_scan(dev, name):
     for b in batches:
         ds = _sample_channels(cfg.dim, rng)
         sub = sub_problem(inp, b, ds)
-        yr, lr = oracle_scan(sub, nthreads=16)
+        yr, lr = oracle_scan(sub, nthreads=16, bbar=bbar)
         err = assert_parity(y[b:b + 1, ds], yr, cfg.dtype, f"{name} y batch {b}")
         assert_parity(last[b:b + 1, ds], lr, "f32", f"{name} last_state batch {b}")
         worst = max(worst, err)
@@ -104,7 +105,8 @@ def test_full_size_decode_64_steps(dev):
     print(f"decode: worst y error {worst:.3e}, state error {serr:.3e}", flush=True)
 
 
-def test_full_size_c3_backward_sampled(dev):
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+def test_full_size_c3_backward_sampled(dev, bbar):
     """ssm_scan_bwd over the whole c3 workload (bf16, batch 16, D 5120,
     N 16, L 2048), as bench.py times it.  The per-channel gradients (du,
     d(delta), dz over every batch row, and dA, dD, d(bias), which sum over
@@ -122,7 +124,7 @@ def test_full_size_c3_backward_sampled(dev):
     t = {k: to_torch(inp.get(k), cfg.dtype, dev) for k in ("u", "delta", "B", "C", "z")}
     A, D, bias = (to_torch(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
     g = ssm.ssm_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias,
-                         dy=to_torch(dy, cfg.dtype, dev))
+                         dy=to_torch(dy, cfg.dtype, dev), bbar=bbar)
     torch.cuda.synchronize(dev)
     for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dh0"):
         assert bool(torch.isfinite(g[k].float()).all()), f"{k}: non-finite values"
@@ -134,11 +136,11 @@ def test_full_size_c3_backward_sampled(dev):
     r = oracle.scan_bwd(w["u"], w["delta"], inp["A"][ds].astype(np.float64), Bw, Cw,
                         inp["D"][ds].astype(np.float64), w["z"], inp["delta_bias"][ds].astype(np.float64),
                         True, None, dy=synth.widen(np.ascontiguousarray(dy[:, ds]), cfg.dtype),
-                        nthreads=16)
+                        nthreads=16, bbar=bbar)
     idx = torch.tensor(ds, device=dev)
     got = {k: g[k].index_select(1, idx).float().cpu().numpy() for k in ("du", "ddelta", "dz")}
     got.update({k: g[k].index_select(0, idx).float().cpu().numpy() for k in ("dA", "dD", "ddelta_bias")})
     if r.get("dh0") is not None:
         got["dh0"] = g["dh0"].index_select(1, idx).cpu().numpy()
     errs = {k: assert_parity(got[k], r[k], "bf16", f"c3 backward {k}") for k in got}
-    print("c3 backward, sampled channels: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+    print(f"c3 backward ({bbar}), sampled channels: " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
