@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the long-sequence workloads (c1, c2) that split the sequence")
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for the "
@@ -341,6 +343,9 @@ def main():
     del gy, bws
     del u, delta, B, C, z, y, ws
 
+    if not args.no_split:
+        for name in ("c1", "c2"):
+            out[f"split_{name}"] = bench_split(dev, name, args.steps, args.warmup)
     if not args.no_decode:
         out["decode"] = bench_decode(dev, args.decode_steps)
     if not args.no_ssd:
@@ -351,6 +356,62 @@ def main():
     out["input_generation_s"] = round(gen_s, 2)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def bench_split(dev, name, steps, warmup):
+    """A workload whose channels alone do not fill the GPU, so the library
+    splits the sequence into segments and composes their aggregates (an
+    aggregate launch, then the main launch): c1 (batch 8, D 1536, L 2048,
+    fp32) or c2 (batch 1, D 2048, L 65536, bf16), N 16, timed like the main
+    step.  Parity for these is tested, not benchmarked elsewhere."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    import synth
+    cfg = synth.SCAN_CONFIGS[name]
+    inp = synth.make_scan_inputs(cfg)
+
+    def dev_t(a, dt):
+        if a is None:
+            return None
+        if dt == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    u, delta, B, C, z = (dev_t(inp.get(k), cfg.dtype) for k in ("u", "delta", "B", "C", "z"))
+    A, D, bias = (dev_t(inp.get(k), "f32") for k in ("A", "D", "delta_bias"))
+    y = torch.empty_like(u)
+    ws = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen,
+                                                            u.dtype)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssm.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, out=y, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    elements = cfg.batch * cfg.dim * cfg.seqlen
+    ops = elements * cfg.dstate * OPS_PER_ELEMENT_STATE
+    tops = ops / (ms * 1e-3) / 1e12
+    nbytes = scan_bytes(cfg)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"{cfg.batch}x{cfg.dim}x{cfg.seqlen}, N {cfg.dstate}, {cfg.dtype} I/O, "
+                        f"gate {'on' if cfg.gate else 'off'}, D-skip {'on' if cfg.dskip else 'off'}; "
+                        "the sequence split into segments (aggregate launch + main launch)",
+            "steps": steps, "ms_per_step": ms, "value": elements / (ms * 1e-3), "unit": "elements/s",
+            "hbm": {"algorithmic_bytes": nbytes, "algorithmic_GBps": round(gbps, 1),
+                    "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+            "roofline": {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
+                         "unit": "TOP/s", "frac": round(tops / VALU_PEAK_TOPS, 4),
+                         "ops_per_launch": ops,
+                         "note": "ops count the result pass only; the aggregate pass is extra work"}}
 
 
 def bench_decode(dev, steps):
