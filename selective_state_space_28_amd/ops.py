@@ -74,6 +74,8 @@ def _scan(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, bbar, return_
     need = int(lib.ssm_scan_fwd_workspace_bytes(batch, dim, N, L, code))
     ws_bytes = 0
     if need > 0:
+        if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
@@ -230,6 +232,8 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     need = int(lib.ssm_scan_bwd_workspace_bytes(batch, dim, N, L, code))
     ws_bytes = 0
     if need > 0:
+        if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()
@@ -284,6 +288,8 @@ def ssm_ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, delta_softplu
     need = int(lib.ssm_ssd_scan_fwd_workspace_bytes(batch, N, L, code))
     ws_bytes = 0
     if need > 0:
+        if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         ws_bytes = workspace.numel() * workspace.element_size()

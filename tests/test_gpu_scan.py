@@ -175,6 +175,9 @@ def test_workspace_error(dev, monkeypatch):
                           None, None, None, 1, None, y.data_ptr(), None, 1, 64, 16, 256, 0,
                           None, 0, torch.cuda.current_stream().cuda_stream)
     assert rc == -5
+    # the binding rejects a workspace that is not device memory of the inputs' GPU
+    with pytest.raises(ValueError, match="workspace"):
+        ssm.ssm_scan_fwd(u, u, A, Bm, Bm, workspace=torch.empty(need, dtype=torch.uint8))
 
 
 def test_softplus_and_zoh_accuracy(dev):
