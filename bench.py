@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-split", action="store_true",
                     help="skip the long-sequence workloads (c1, c2) that split the sequence")
+    ap.add_argument("--split-only", action="store_true",
+                    help="run only the long-sequence workloads (c1, c2) and print their objects")
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for the "
@@ -162,6 +164,10 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
         return 0
     ssm.load()
+    if args.split_only:
+        print(json.dumps({f"split_{name}": bench_split(dev, name, args.steps, args.warmup)
+                          for name in ("c1", "c2")}), flush=True)
+        return 0
     cfg = synth.SCAN_CONFIGS["c3"]
     t_gen = time.time()
     inp = synth.make_scan_inputs(cfg)
