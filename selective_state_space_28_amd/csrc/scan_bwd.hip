@@ -206,9 +206,12 @@ __global__ __launch_bounds__(64 * G) void bwd_agg_kernel(
 }
 
 // ---- 3. the main backward sweep --------------------------------------------------
-// The zero-order-hold instantiation carries more live values per (element,
-// state) and takes the whole register file (one workgroup per CU).
-template <typename T, int NS, int G, int TL, bool ZOH>
+// Wave g holds NS states of each of the workgroup's 64 channels.  The B, C
+// records are packed in groups of RNS states (the forward pass's layout);
+// RNS may be larger than NS.  The zero-order-hold instantiation carries more
+// live values per (element, state), so it runs with fewer states per wave and
+// more waves (NS = RNS / 2, one workgroup per CU).
+template <typename T, int NS, int G, int TL, bool ZOH, int RNS>
 __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
@@ -221,19 +224,20 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   constexpr int E = TL / G;                   // elements per thread, element role
   constexpr int TRS = 8 / NS;                 // steps per dB/dC wave sum (16 terms a lane)
   constexpr int LDW = 65;                     // padded row, float/float2/float4 arrays
-  constexpr int R = 2 * NS;
+  constexpr int R = 2 * RNS;                  // values of a record: RNS B values, then RNS C values
+  constexpr int RG = N / RNS;                 // record groups
   static_assert(NS * TRS == 8 && TL % TRS == 0, "dB/dC sums take 16 terms a lane");
+  static_assert(RNS % NS == 0 && N % RNS == 0 && TL % G == 0, "state groups");
 
   __shared__ float4 s_in[TL][LDW];            // (Delta, Delta*u, ds, u) per (step, channel)
   __shared__ float s_y[G][TL][LDW];           // readout partials of each wave
   // per wave and step, the sums over this wave's states: Euler (sum lambda B,
-  // sum of the Abar part of dDelta); ZOH (sum lambda Bbar B, sum lambda Abar B,
-  // the Abar part, -)
-  using SP = typename std::conditional<ZOH, float4, float2>::type;
-  __shared__ SP s_p[G][TL][LDW];
-  // this tile's B, C records of every state group as floats, [g][t][q]: loaded
-  // a tile ahead with the other inputs, read by each wave as broadcasts
-  __shared__ __align__(16) float s_rec[G][TL][R];
+  // the Abar part of dDelta); ZOH (sum lambda Bbar B, u sum lambda Abar B plus
+  // the Abar part of dDelta)
+  __shared__ float2 s_p[G][TL][LDW];
+  // this tile's B, C records of every record group as floats, [group][t][q]:
+  // loaded a tile ahead with the other inputs, read by each wave as broadcasts
+  __shared__ __align__(16) float s_rec[RG][TL][R];
 
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
@@ -253,6 +257,9 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   const int64_t seg_begin = (int64_t)seg * p.seglen;
   const int64_t seg_end = seg_begin + p.seglen < L ? seg_begin + p.seglen : L;
   const int64_t ntiles = (L + TL - 1) / TL;
+  // this wave's states n = g NS + k sit in record group n / RNS at position
+  // n % RNS: B of state k at rec_w[t R + k], C at rec_w[t R + RNS + k]
+  const float* const rec_w = &s_rec[0][0][0] + (g * NS / RNS) * (TL * R) + (g * NS) % RNS;
   const int64_t plane = (int64_t)p.batch * p.dim;
 
   // ---- recurrence role: parameters and the carry entering the segment's end --
@@ -306,12 +313,12 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   float pck[NS];                          // and the state entering it
   // record staging: pair q of the tile's G * TL * R record values (group q /
   // (TL R / 2), values 2 (q % (TL R / 2)) and the next), one pair per thread
-  constexpr int NPAIR = G * TL * R / 2;
+  constexpr int NPAIR = RG * TL * R / 2;
   constexpr int PW = (int)sizeof(T) / 2;  // words of a pair
   static_assert(NPAIR <= 64 * G, "one record pair per thread at most");
   const bool rec_thread = tid < NPAIR;
   const int rec_g = tid / (TL * R / 2), rec_e = 2 * (tid % (TL * R / 2));
-  const T* bc_rec = bc + ((int64_t)b * G + (rec_thread ? rec_g : 0)) * L * R + rec_e;
+  const T* bc_rec = bc + ((int64_t)b * RG + (rec_thread ? rec_g : 0)) * L * R + rec_e;
   uint32_t prec[PW];
   auto load_rec = [&](int64_t t0, bool guard, uint32_t (&w)[PW]) {
     const int tt = rec_e / R;  // the step of this pair (both values share it: R is even)
@@ -418,11 +425,11 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
             const float x2 = v.x * A2[k];
             const float a = exp2_hw(x2);
             if constexpr (ZOH)
-              h[k] = __builtin_fmaf(a, h[k], zoh_coef(a, x2, v.x, rA[k]) * (v.w * s_rec[g][t][k]));
+              h[k] = __builtin_fmaf(a, h[k], zoh_coef(a, x2, v.x, rA[k]) * (v.w * rec_w[t * R + k]));
             else
-              h[k] = __builtin_fmaf(a, h[k], v.y * s_rec[g][t][k]);
+              h[k] = __builtin_fmaf(a, h[k], v.y * rec_w[t * R + k]);
             hist[t][k] = h[k];
-            acc = __builtin_fmaf(s_rec[g][t][NS + k], h[k], acc);
+            acc = __builtin_fmaf(rec_w[t * R + RNS + k], h[k], acc);
           }
           s_y[g][t][lane] = acc;
         }
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
           for (int k = 0; k < NS; ++k) {
             const float x2 = v.x * A2[k];
             const float a = exp2_hw(x2);
-            const float lam = __builtin_fmaf(v.z, s_rec[g][t][NS + k], carry[k]);
+            const float lam = __builtin_fmaf(v.z, rec_w[t * R + RNS + k], carry[k]);
             const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hp0[k];
             const float cn = a * lam;  // the carry into step t - 1
             const float gh = cn * hp;
@@ -473,20 +480,20 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
             if constexpr (ZOH) {
               // input term Bbar B u with Bbar = (Abar - 1)/A: dBbar/dDelta = Abar
               const float coef = zoh_coef(a, x2, v.x, rA[k]);
-              const float lB = lam * s_rec[g][t][k];
+              const float lB = lam * rec_w[t * R + k];
               dA[k] = __builtin_fmaf(gh, v.x, __builtin_fmaf(lB * v.w, zoh_coef_dA(a, x2, v.x, rA[k]), dA[k]));
               lb = __builtin_fmaf(lB, coef, lb);
               la = __builtin_fmaf(lB, a, la);
               terms[k * TRS + i] = (lam * coef) * v.w;
             } else {
               dA[k] = __builtin_fmaf(gh, v.x, dA[k]);
-              lb = __builtin_fmaf(lam, s_rec[g][t][k], lb);
+              lb = __builtin_fmaf(lam, rec_w[t * R + k], lb);
               terms[k * TRS + i] = lam * v.y;
             }
             terms[8 + k * TRS + i] = v.z * hist[t][k];
             carry[k] = cn;
           }
-          if constexpr (ZOH) s_p[g][t][lane] = make_float4(lb, la, dd * kLn2, 0.0f);
+          if constexpr (ZOH) s_p[g][t][lane] = make_float2(lb, __builtin_fmaf(v.w, la, dd * kLn2));
           else s_p[g][t][lane] = make_float2(lb, dd * kLn2);
         }
       }
@@ -503,22 +510,17 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
       e_du[e] = e_dd[e] = 0.0f;
       if (e < valid) {
         const int t = r0 + e;
-        float slb = 0.0f, sla = 0.0f, sdd = 0.0f;
+        float slb = 0.0f, sdd = 0.0f;
 #pragma unroll
         for (int gg = 0; gg < G; ++gg) {
-          const SP q = s_p[gg][t][cc];
+          const float2 q = s_p[gg][t][cc];
           slb += q.x;
-          if constexpr (ZOH) {
-            sla += q.y;
-            sdd += q.z;
-          } else {
-            sdd += q.y;
-          }
+          sdd += q.y;
         }
         float ddx;
         if constexpr (ZOH) {  // du = ds D + sum lambda Bbar B; dDelta = u sum lambda Abar B + ...
           e_du[e] = __builtin_fmaf(e_ds[e], D_cc, slb);
-          ddx = __builtin_fmaf(e_u[e], sla, sdd) * e_sg[e];
+          ddx = sdd * e_sg[e];
         } else {              // du = ds D + Delta sum lambda B; dDelta = u sum lambda B + ...
           e_du[e] = __builtin_fmaf(e_ds[e], D_cc, e_dt[e] * slb);
           ddx = __builtin_fmaf(e_u[e], slb, sdd) * e_sg[e];
@@ -622,8 +624,13 @@ static hipError_t launch_bwd_typed(const BwdLaunch& a, hipStream_t stream) {
     bwd_agg_kernel<T, NS, G, TL><<<(unsigned)(base * (a.nseg - 1)), 64 * G, 0, stream>>>(
         dl, a.A, bc, z, a.bias, gy, a.ws_lagg, a.ws_lsum, s);
   }
-  auto kernel = a.zoh ? bwd_kernel<T, NS, G, TL, true> : bwd_kernel<T, NS, G, TL, false>;
-  kernel<<<(unsigned)(base * a.nseg), 64 * G, 0, stream>>>(
+  // zero-order hold: half the states per wave, twice the waves (records still
+  // in groups of NS)
+  constexpr int ZNS = NS >= 2 ? NS / 2 : 1;
+  constexpr int ZG = NS * G / ZNS;
+  auto kernel = a.zoh ? bwd_kernel<T, ZNS, ZG, TL, true, NS> : bwd_kernel<T, NS, G, TL, false, NS>;
+  const int threads = 64 * (a.zoh ? ZG : G);
+  kernel<<<(unsigned)(base * a.nseg), threads, 0, stream>>>(
       u, dl, a.A, bc, a.Dskip, z, a.bias, gy, a.dlast, a.ws_ckpt, a.ws_lagg, a.ws_lsum,
       static_cast<T*>(a.du), static_cast<T*>(a.ddelta), static_cast<T*>(a.dz), a.dh0, a.ws_part_bc,
       a.ws_part_a, a.ws_part_d, a.ws_part_bias, s);

@@ -145,7 +145,7 @@ def test_bwd_full_size_c1(dev):
 # ---- the zero-order-hold input term (Bbar = (Abar - 1)/A) ---------------------------
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n", [1, 4, 16])
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16])
 def test_bwd_zoh_dstate_variants(dev, dtype, n):
     inp = _case(dtype, n=n, L=93, seed=400 + n)
     _compare(gpu_bwd(inp, dev, bbar="zoh"), oracle_bwd(inp, bbar="zoh"), dtype)
