@@ -145,8 +145,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the scan is data-parallel over channels; multi-GPU sharding is described "
-              "in DESIGN.md but not built).", file=sys.stderr)
+              "(the scan is data-parallel over channels and batch rows, so shards would need "
+              "no communication, but no multi-GPU path is built).", file=sys.stderr)
         return 2
 
     import torch
