@@ -327,7 +327,7 @@ def main():
                   "roofline": {"bound": "alu", "achieved": round(tops_b, 3),
                                "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
                                "frac": round(tops_b / VALU_PEAK_TOPS, 4),
-                               "kernel": "ssm::bwd_kernel<unsigned short, 4, 4, 16, false> (+ "
+                               "kernel": "ssm::bwd_kernel<unsigned short, 4, 4, 16, false, 4> (+ "
                                          "checkpoint pass and sums)",
                                "ops_per_launch": ops_b}}
 
