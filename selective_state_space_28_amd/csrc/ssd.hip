@@ -396,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
   __shared__ __align__(16) float sCoef[Q];
   // Per-step factors, written after the prefix sum and read in step 2 (cum_t
   // as above, c_i = cum_{16i}):
-  //   sE0[t]    = exp2(cum_t)                      scales row t of C^T
+  //   sE0[t]    = exp2(cum_t)                      scales row t of C^T H
   //   sW[s]     = exp2(cum_Q - cum_s) Bbar_s       scales x for the state update
   //   sE1[t]    = exp2(cum_t - c_{t/16})
   //   sW2[i][s] = exp2(c_i - cum_s) Bbar_s, s < 16i
@@ -619,22 +619,16 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     if constexpr (FULL) load_part_b(next);  // B and Delta are in LDS / used
     __syncthreads();
 
-    // ---- (2) C^T scaled, x o w, the mask (the next chunk's loads in between) --------------
+    // ---- (2) C^T, x o w, the mask (the next chunk's loads in between) ----------------------
     const float cum2Q = sCum2[Q - 1];
-    // C^T rows scaled by exp2(cum_t), so the state part of Y leaves the
-    // product already decayed
+    // C^T as loaded (the decay exp2(cum_t) of the state part is applied to
+    // the product's rows in step 3)
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
       const int item = tid + 256 * k;
       if (NR % 256 == 0 || item < NR) {
         const int t = item / (N / 8), n8 = 8 * (item % (N / 8));
-        const float e = sE0[t];
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = run_elem<T>(rct[k], j) * e;
-        uint32_t wv[RW];
-        pack_floats<T, 8>(v, wv);
-        lds_store_states<T>(&sCt[t][0], n8, wv);
+        lds_store_states<T>(&sCt[t][0], n8, rct[k]);
       }
     }
 #pragma unroll
@@ -686,7 +680,7 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     if constexpr (FULL) load_part_g(next);  // this chunk's G tiles are used
     __syncthreads();
 
-    // ---- (3) Y = M X^T + (diag(exp(cum_t)) C^T) H for this wave's channels, staged [p][t]
+    // ---- (3) Y = M X^T + diag(exp(cum_t)) C^T H for this wave's channels, staged [p][t]
     // ----------------------------------------------------------------------------------
     {
       typename Mma<T>::StatePack hp[NPK];
@@ -704,14 +698,17 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         // the state entering the chunk
 #pragma unroll
         for (int m = 0; m < NPK; ++m) yo = Mma<T>::mma_state(&sCt[16 * i][PS * m], LN, hp[m], yo, lane);
-        // y = (Y + D x) silu(z) for this lane's 4 steps, staged in the storage type
+        // y = (Y + D x) silu(z) for this lane's 4 steps, staged in the storage type;
+        // the state part takes its decay exp2(cum_t) here
         const int tc = 16 * i + ty;
         uint32_t xr[RW / 2];
         load_words<RW / 2>(&sX[py][tc], xr);
+        const float4 e4 = *reinterpret_cast<const float4*>(&sE0[tc]);
+        const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
         float yv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = __builtin_fmaf(Dp, run_elem4<T>(xr, r), yd[r] + yo[r]);
+          float v = __builtin_fmaf(Dp, run_elem4<T>(xr, r), __builtin_fmaf(ev[r], yo[r], yd[r]));
           if constexpr (GATE) v *= silu_f32(run_elem4<T>(rz[i], r));
           yv[r] = v;
         }
