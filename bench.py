@@ -129,7 +129,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU's clock ramps up over the first ~35 ms of sustained load after
+    # idling (c3 step: about 0.70 ms for the first calls, 0.58 ms from about
+    # the 50th on), so the default warm-up covers that ramp and the timed steps
+    # see the sustained rate.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
@@ -311,7 +315,7 @@ def main():
     def step_bwd():
         ssm.ssm_scan_bwd(u, delta, A, B, C, D, z, bias, dy=gy, workspace=bws)
 
-    for _ in range(max(1, args.warmup // 2)):
+    for _ in range(max(1, min(args.warmup, 3))):  # the GPU is warm by now
         step_bwd()
     torch.cuda.synchronize(dev)
     nb = max(1, args.steps // 5)
