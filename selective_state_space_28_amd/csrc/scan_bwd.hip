@@ -209,8 +209,8 @@ __global__ __launch_bounds__(64 * G) void bwd_agg_kernel(
 // Wave g holds NS states of each of the workgroup's 64 channels.  The B, C
 // records are packed in groups of RNS states (the forward pass's layout);
 // RNS may be larger than NS.  The zero-order-hold instantiation carries more
-// live values per (element, state), so it runs with fewer states per wave and
-// more waves (NS = RNS / 2, one workgroup per CU).
+// live values per (element, state), so it runs with half the states per wave
+// and twice the waves where RNS >= 2 (NS = RNS / 2, one workgroup per CU).
 template <typename T, int NS, int G, int TL, bool ZOH, int RNS>
 __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
