@@ -52,8 +52,22 @@
  *    outputs or workspace on different streams race.
  *  - Arguments are validated before any HIP call; on an error nothing is
  *    enqueued.  A launch failure returns SSM_ERR_HIP.
- *  - NaN and Inf inputs propagate; A is not checked for sign (A > 0 is an
+ *  - NaN and Inf inputs propagate as in the formula: a non-finite u, delta
+ *    or z of channel (b, d) at step t makes that channel's outputs from t
+ *    on non-finite where the formula does (NaN where it gives NaN, Inf of
+ *    the same sign where it gives Inf) and leaves other channels alone; a
+ *    non-finite B or C reaches every channel of its batch row.  (ssm_ssd_
+ *    scan_fwd differs: see there.)  Exception, float32 range: where one
+ *    step's decay exp(Delta*A) underflows to 0 in float32 (Delta*A below
+ *    about -87) an infinite state meets it as 0 * Inf = NaN; the decay of a
+ *    whole segment of a split sequence is kept at or above the smallest
+ *    normal float for that reason.  A is not checked for sign (A > 0 is an
  *    unstable system and its state grows, as the pages note).
+ *  - Buffers the call writes (y, last_state, conv_state_out, the decode
+ *    state and conv_state, the gradients, the workspace) must not overlap
+ *    each other or any buffer the call reads, judged on their byte ranges
+ *    (SSM_ERR_ALIAS otherwise); buffers that are only read may overlap.  In
+ *    particular last_state must not be h0.
  *  - With SSM_BBAR_ZOH the coefficient (Abar - 1)/A is taken from the Taylor
  *    series Delta (1 + x/2 + x^2/6 + x^3/24), x = Delta A, where |x| < 0.1,
  *    and from (Abar - 1)/A elsewhere, so its float32 relative error stays
@@ -81,7 +95,7 @@ typedef enum {
   SSM_ERR_ALIGN = -4,     /* a pointer not aligned to its element size           */
   SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query's answer   */
   SSM_ERR_HIP = -6,       /* the HIP runtime reported an error at launch         */
-  SSM_ERR_ALIAS = -7,     /* y (or the decode state) is the same buffer as an input */
+  SSM_ERR_ALIAS = -7,     /* a buffer the call writes overlaps another of its buffers */
   SSM_ERR_FLAGS = -8      /* flags holds a bit that is not an ssm_flag_t value   */
 } ssm_status_t;
 
@@ -282,6 +296,12 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
  * bf16 storage feeds the matrix cores bf16 operands: the chunk matrix, the
  * decayed x and the state are rounded to bf16 for the products, which are
  * accumulated in float32; the state itself is carried in float32.
+ * Non-finite inputs: a NaN or Inf in x at (channel, step t) makes that
+ * channel's outputs non-finite from t on, as in the recurrence, and can
+ * also reach its outputs of the same 64-step chunk before t (the chunk's
+ * masked product multiplies it by the zeros above the diagonal, and
+ * 0 * Inf is NaN); a non-finite dt, B or C reaches the whole chunk of its
+ * head (dt) or batch row (B, C).  Outputs before the chunk are unaffected.
  * Otherwise as ssm_scan_fwd.
  */
 int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const void* B,

@@ -33,12 +33,16 @@ def build() -> str:
 
 
 def _load():
+    """Load liboracle.so (building it if absent).  SSM_ORACLE_LIB names
+    another build of the same source to load instead (the sanitizer build
+    of the CPU tests)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
+    path = os.environ.get("SSM_ORACLE_LIB") or _LIB
+    if path == _LIB and not os.path.exists(_LIB):
         build()
-    lib = ctypes.CDLL(_LIB)
+    lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     L = ctypes.c_long
     lib.oracle_scan_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int,

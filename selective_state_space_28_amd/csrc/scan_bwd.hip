@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
       const float sdt = lsum[(int64_t)(j - 1) * plane + row];
 #pragma unroll
       for (int k = 0; k < NS; ++k)
-        carry[k] = __builtin_fmaf(exp2_hw(sdt * A2[k]), carry[k],
+        carry[k] = __builtin_fmaf(segment_decay(sdt * A2[k]), carry[k],
                                   lagg[((int64_t)(j - 1) * plane + row) * N + g * NS + k]);
     }
   }

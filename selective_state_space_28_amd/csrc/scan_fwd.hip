@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
       const float sdt = ws_sumdt[j * plane + row];
 #pragma unroll
       for (int k = 0; k < NS; ++k)
-        h[k] = __builtin_fmaf(exp2_hw(sdt * A2[k]), h[k], ws_hend[(j * plane + row) * N + g * NS + k]);
+        h[k] = __builtin_fmaf(segment_decay(sdt * A2[k]), h[k], ws_hend[(j * plane + row) * N + g * NS + k]);
     }
   }
 

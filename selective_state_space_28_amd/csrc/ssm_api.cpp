@@ -149,6 +149,37 @@ BwdWsLayout bwd_workspace_layout(int batch, int dim, int dstate, int64_t L, int 
 
 bool aligned(const void* p, size_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The byte range [lo, hi) a buffer occupies; a null pointer or zero bytes
+// occupies none.  Aliasing is judged on these ranges, not on pointer
+// equality, so an output that starts inside an input (or ends inside one) is
+// rejected too.
+struct Span {
+  uintptr_t lo, hi;
+};
+
+Span span(const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (p == nullptr || bytes == 0) return Span{0, 0};
+  return Span{lo, lo + bytes};
+}
+
+bool overlap(const Span& a, const Span& b) {
+  return a.hi > a.lo && b.hi > b.lo && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Whether a buffer the call writes overlaps another buffer the call writes,
+// or one it reads.  Inputs may overlap each other (they are only read).
+template <size_t NO, size_t NI>
+bool writes_overlap(const Span (&outs)[NO], const Span (&ins)[NI]) {
+  for (size_t i = 0; i < NO; ++i) {
+    for (size_t j = i + 1; j < NO; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+    for (size_t j = 0; j < NI; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
 bool shapes_fit(int batch, int dim, int64_t seqlen) {
   if (batch < 0 || dim < 0 || seqlen < 0) return false;
   const long double total = (long double)batch * (long double)dim * (long double)(seqlen > 0 ? seqlen : 1);
@@ -205,12 +236,25 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
       !aligned(workspace, 256))
     return SSM_ERR_ALIGN;
   if (!conv_aligned(cv)) return SSM_ERR_ALIGN;
-  if (y != nullptr && (y == u || y == delta || (z != nullptr && y == z))) return SSM_ERR_ALIAS;
-  if (cv != nullptr && cv->state_out != nullptr &&
-      (cv->state_out == cv->state_in || (void*)cv->state_out == y || cv->state_out == last_state))
-    return SSM_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (empty) return SSM_OK;
+  {
+    const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
+    const size_t bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
+    const size_t per_dim = (size_t)dim * sizeof(float);
+    const size_t state = (size_t)batch * (size_t)dim * (size_t)dstate * sizeof(float);
+    const size_t ck = cv != nullptr && cv->k > 1 ? (size_t)batch * (size_t)dim * (size_t)(cv->k - 1) * 4 : 0;
+    const size_t cw = cv != nullptr ? (size_t)dim * (size_t)cv->k * 4 : 0;
+    const Span outs[] = {span(y, tok), span(last_state, state),
+                         span(cv != nullptr ? cv->state_out : nullptr, ck)};
+    const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(B, bc), span(C, bc),
+                        span(A, per_dim * (size_t)dstate), span(D_skip, per_dim),
+                        span(delta_bias, per_dim), span(h0, state),
+                        span(cv != nullptr ? cv->w : nullptr, cw),
+                        span(cv != nullptr ? cv->b : nullptr, cv != nullptr ? per_dim : 0),
+                        span(cv != nullptr ? cv->state_in : nullptr, ck)};
+    if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
+  }
 
   if (seqlen == 0) {  // nothing to scan: the states stay as they came in (or zero)
     if (last_state != nullptr) {
@@ -231,6 +275,17 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
   if (blocks > INT_MAX || pack_blocks > INT_MAX) return SSM_ERR_SHAPE;
   const WsLayout wl = workspace_layout(batch, dim, dstate, seqlen, dtype, sp);
   if (workspace == nullptr || workspace_bytes < wl.total) return SSM_ERR_WORKSPACE;
+  {
+    const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
+    const size_t bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
+    const size_t state = (size_t)batch * (size_t)dim * (size_t)dstate * sizeof(float);
+    const Span outs[] = {span(workspace, wl.total)};
+    const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(B, bc), span(C, bc),
+                        span(A, (size_t)dim * (size_t)dstate * 4), span(D_skip, (size_t)dim * 4),
+                        span(delta_bias, (size_t)dim * 4), span(h0, state), span(y, tok),
+                        span(last_state, state)};
+    if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
+  }
 
   ssm::ScanLaunch a{};
   a.u = u;
@@ -291,12 +346,22 @@ int update_impl(float* state, const void* u, const void* delta, const float* A, 
       !aligned(D_skip, 4) || !aligned(delta_bias, 4))
     return SSM_ERR_ALIGN;
   if (!conv_aligned(cv)) return SSM_ERR_ALIGN;
-  if (y != nullptr && (y == u || y == delta || y == state || (z != nullptr && y == z)))
-    return SSM_ERR_ALIAS;
-  if (cv != nullptr && cv->state != nullptr &&
-      (cv->state == state || (void*)cv->state == y || (const void*)cv->state == u))
-    return SSM_ERR_ALIAS;
   if (empty) return SSM_OK;
+  {
+    const size_t tok = (size_t)batch * (size_t)dim * es;
+    const size_t bc = (size_t)batch * (size_t)dstate * es;
+    const size_t per_dim = (size_t)dim * sizeof(float);
+    const size_t ck = cv != nullptr && cv->k > 1 ? (size_t)batch * (size_t)dim * (size_t)(cv->k - 1) * 4 : 0;
+    // the state and the carried convolution inputs are read and written in place
+    const Span outs[] = {span(y, tok), span(state, (size_t)batch * (size_t)dim * (size_t)dstate * 4),
+                         span(cv != nullptr ? cv->state : nullptr, ck)};
+    const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(B, bc), span(C, bc),
+                        span(A, per_dim * (size_t)dstate), span(D_skip, per_dim),
+                        span(delta_bias, per_dim),
+                        span(cv != nullptr ? cv->w : nullptr, cv != nullptr ? per_dim * (size_t)cv->k : 0),
+                        span(cv != nullptr ? cv->b : nullptr, cv != nullptr ? per_dim : 0)};
+    if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
+  }
   // one grid row per batch row: its lanes (P per channel) are indexed in 32 bits
   if ((int64_t)dim * (dstate >= 4 ? dstate / 4 : 1) + 255 > INT_MAX) return SSM_ERR_SHAPE;
 
@@ -402,17 +467,21 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
       !aligned(dA, 4) || !aligned(dD, 4) || !aligned(ddelta_bias, 4) || !aligned(dh0, 4) ||
       !aligned(workspace, 256))
     return SSM_ERR_ALIGN;
-  {
-    const void* ins[] = {u, delta, B, C, z, dy};
-    const void* outs[] = {du, ddelta, dB, dC, dz};
-    for (const void* o : outs) {
-      if (o == nullptr) continue;
-      for (const void* i : ins)
-        if (o == i) return SSM_ERR_ALIAS;
-    }
-  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (empty) return SSM_OK;
+  {
+    const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
+    const size_t bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
+    const size_t per_dim = (size_t)dim * sizeof(float);
+    const size_t state = (size_t)batch * (size_t)dim * (size_t)dstate * sizeof(float);
+    const Span outs[] = {span(du, tok), span(ddelta, tok), span(dz, tok), span(dB, bc), span(dC, bc),
+                         span(dA, per_dim * (size_t)dstate), span(dD, per_dim),
+                         span(ddelta_bias, per_dim), span(dh0, state)};
+    const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(dy, tok), span(B, bc),
+                        span(C, bc), span(A, per_dim * (size_t)dstate), span(D_skip, per_dim),
+                        span(delta_bias, per_dim), span(h0, state), span(dlast_state, state)};
+    if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
+  }
 
   if (seqlen == 0) {  // no steps: zero parameter gradients, dh0 = dlast
     hipError_t e = ssm::launch_fill_state(dA, nullptr, (int64_t)dim * dstate, st);
@@ -431,6 +500,20 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   if (blocks > INT_MAX || pack_blocks > INT_MAX || red_blocks > INT_MAX) return SSM_ERR_SHAPE;
   const BwdWsLayout wl = bwd_workspace_layout(batch, dim, dstate, seqlen, dtype, sp);
   if (workspace == nullptr || workspace_bytes < wl.total) return SSM_ERR_WORKSPACE;
+  {
+    const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
+    const size_t bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
+    const size_t per_dim = (size_t)dim * sizeof(float);
+    const size_t state = (size_t)batch * (size_t)dim * (size_t)dstate * sizeof(float);
+    const Span outs[] = {span(workspace, wl.total)};
+    const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(dy, tok), span(B, bc),
+                        span(C, bc), span(A, per_dim * (size_t)dstate), span(D_skip, per_dim),
+                        span(delta_bias, per_dim), span(h0, state), span(dlast_state, state),
+                        span(du, tok), span(ddelta, tok), span(dz, tok), span(dB, bc), span(dC, bc),
+                        span(dA, per_dim * (size_t)dstate), span(dD, per_dim),
+                        span(ddelta_bias, per_dim), span(dh0, state)};
+    if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
+  }
   char* ws = static_cast<char*>(workspace);
   const bool rows16 = ((int64_t)es * seqlen) % 16 == 0;
 
@@ -532,7 +615,6 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
       !aligned(z, es) || !aligned(y, es) || !aligned(A_head, 4) || !aligned(D_skip, 4) ||
       !aligned(dt_bias, 4) || !aligned(h0, 4) || !aligned(last_state, 4) || !aligned(workspace, 256))
     return SSM_ERR_ALIGN;
-  if (y != nullptr && (y == x || y == dt || (z != nullptr && y == z))) return SSM_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (empty) return SSM_OK;
   if (seqlen == 0) {
@@ -546,8 +628,30 @@ int ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A_head, const v
   // chunk tiles with 32-bit byte offsets
   const int64_t widest = dstate > ssm::kSsdHeadDim ? dstate : ssm::kSsdHeadDim;
   if (seqlen * widest * (int64_t)es > INT_MAX || (seqlen + 63) / 64 * 10240 > INT_MAX) return SSM_ERR_SHAPE;
-  if (workspace == nullptr || workspace_bytes < ssm_ssd_scan_fwd_workspace_bytes(batch, dstate, seqlen, dtype))
-    return SSM_ERR_WORKSPACE;
+  const size_t ssd_tok = (size_t)batch * (size_t)nheads * (size_t)headdim * (size_t)seqlen * es;
+  const size_t ssd_bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
+  const size_t ssd_state = (size_t)batch * (size_t)nheads * (size_t)headdim * (size_t)dstate * 4;
+  {
+    const Span outs[] = {span(y, ssd_tok), span(last_state, ssd_state)};
+    const Span ins[] = {span(x, ssd_tok), span(z, ssd_tok),
+                        span(dt, (size_t)batch * (size_t)nheads * (size_t)seqlen * es),
+                        span(B, ssd_bc), span(C, ssd_bc), span(A_head, (size_t)nheads * 4),
+                        span(D_skip, (size_t)nheads * (size_t)headdim * 4),
+                        span(dt_bias, (size_t)nheads * 4), span(h0, ssd_state)};
+    if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
+  }
+  const size_t ssd_ws = ssm_ssd_scan_fwd_workspace_bytes(batch, dstate, seqlen, dtype);
+  if (workspace == nullptr || workspace_bytes < ssd_ws) return SSM_ERR_WORKSPACE;
+  {
+    const Span outs[] = {span(workspace, ssd_ws)};
+    const Span ins[] = {span(x, ssd_tok), span(z, ssd_tok),
+                        span(dt, (size_t)batch * (size_t)nheads * (size_t)seqlen * es),
+                        span(B, ssd_bc), span(C, ssd_bc), span(A_head, (size_t)nheads * 4),
+                        span(D_skip, (size_t)nheads * (size_t)headdim * 4),
+                        span(dt_bias, (size_t)nheads * 4), span(h0, ssd_state), span(y, ssd_tok),
+                        span(last_state, ssd_state)};
+    if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
+  }
   ssm::SsdLaunch a{};
   a.x = x;
   a.dt = dt;
@@ -584,7 +688,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN: a pointer is not aligned to its element size";
     case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE: workspace missing or too small";
     case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported a launch error";
-    case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: an output is the same buffer as an input";
+    case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: a buffer the call writes overlaps another buffer of the call";
     case SSM_ERR_FLAGS: return "SSM_ERR_FLAGS: flags holds an unknown bit";
     default: return "unknown ssm status";
   }

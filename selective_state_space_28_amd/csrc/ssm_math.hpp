@@ -87,6 +87,21 @@ __device__ __forceinline__ float zoh_coef_dA(float a, float x2, float dt, float 
   return __builtin_fabsf(x) < 0.25f ? series : direct;
 }
 
+// The decay exp(A * SumDelta) of a whole segment, for composing segment
+// aggregates: exp2(x), x = A*log2(e)*SumDelta, except that a result below
+// the smallest normal float is raised to it while x is finite.  The decay
+// over many steps can underflow where no single step's factor does; keeping
+// it positive lets an infinite state stay infinite through the composition,
+// as it does step by step (0 * inf would be NaN).  x = -inf (a step with
+// Delta = inf, whose factor is exactly 0) still gives 0; NaN stays NaN.  On
+// finite states the raise changes a result by at most 2^-126 times the
+// state.
+constexpr float kMinNormal = 1.17549435e-38f;
+__device__ __forceinline__ float segment_decay(float x) {
+  const float f = exp2_hw(x);
+  return (f < kMinNormal && x > -__builtin_inff()) ? kMinNormal : f;
+}
+
 // silu(z) = z / (1 + e^-z).  For z -> -inf the reciprocal goes to 0 and the
 // product to -0; no NaN for finite z.
 __device__ __forceinline__ float silu_f32(float z) {

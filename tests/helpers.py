@@ -90,3 +90,65 @@ def sub_problem(inp: dict, b: int, ds) -> dict:
     for k in ("D", "delta_bias"):
         out[k] = None if inp.get(k) is None else np.ascontiguousarray(inp[k][ds])
     return out
+
+
+class MaxErr:
+    """Running max|got - ref| and max|ref| over the pieces of one tensor, so a
+    tensor too large to widen at once is compared in blocks with exactly the
+    whole-tensor criterion max|got - ref| <= tol * max|ref|."""
+
+    def __init__(self, what: str):
+        self.what = what
+        self.err = 0.0
+        self.ref = 0.0
+        self.count = 0
+
+    def add(self, got, ref):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, f"{self.what}: shape {got.shape} != {ref.shape}"
+        if ref.size == 0:
+            return
+        assert np.all(np.isfinite(got)), f"{self.what}: non-finite values"
+        self.err = max(self.err, float(np.max(np.abs(got - ref))))
+        self.ref = max(self.ref, float(np.max(np.abs(ref))))
+        self.count += ref.size
+
+    def scaled(self) -> float:
+        return self.err / self.ref if self.ref > 0 else self.err
+
+    def check(self, dtype: str, expect_count: int | None = None) -> float:
+        if expect_count is not None:
+            assert self.count == expect_count, f"{self.what}: compared {self.count} of {expect_count}"
+        err = self.scaled()
+        assert err <= TOL[dtype], f"{self.what}: scaled max error {err:.3e} > {TOL[dtype]:.0e}"
+        return err
+
+
+def block_problem(inp: dict, b: int, d0: int, d1: int) -> dict:
+    """Channels d0..d1-1 of batch row b as a batch-1 problem of its own
+    (slices, no fancy indexing)."""
+    out = {"dtype": inp["dtype"]}
+    for k in ("u", "delta", "z"):
+        out[k] = None if inp.get(k) is None else inp[k][b:b + 1, d0:d1]
+    for k in ("B", "C"):
+        out[k] = inp[k][b:b + 1]
+    out["A"] = inp["A"][d0:d1]
+    for k in ("D", "delta_bias"):
+        out[k] = None if inp.get(k) is None else inp[k][d0:d1]
+    return out
+
+
+def channel_blocks(dim: int, seqlen: int, max_elements: int = 1 << 24):
+    """(d0, d1) ranges covering 0..dim-1, each of at most about max_elements
+    elements of a (1, d1-d0, seqlen) block."""
+    step = max(1, min(dim, max_elements // max(1, seqlen)))
+    return [(d0, min(dim, d0 + step)) for d0 in range(0, dim, step)]
+
+
+def oracle_threads() -> int:
+    """Worker threads for the oracle: the host's cores, at most 16 (the CPU
+    share of one GPU on a shared host)."""
+    import os
+    env = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return max(1, min(16, env or (os.cpu_count() or 1)))

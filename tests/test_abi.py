@@ -9,6 +9,12 @@ from selective_state_space_28_amd._lib import header_functions, load
 
 OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS, FLAGS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 P = 0x10000  # a 256-byte aligned fake device address, never dereferenced
+R = 0x1000000  # 16 MiB: distinct buffers of a call sit R apart, so none overlaps
+
+
+def at(k):
+    """Fake device address of the k-th distinct buffer of a call."""
+    return 0x40000000 + k * R
 
 
 def test_exports_every_declared_symbol():
@@ -30,7 +36,7 @@ def test_status_strings():
 
 
 def _scan(**kw):
-    a = dict(u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=1, h0=None, y=P + 0x100000,
+    a = dict(u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=1, h0=None, y=at(1),
              last=None, batch=1, dim=64, dstate=16, L=2048, dtype=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     return load().ssm_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
@@ -40,8 +46,8 @@ def _scan(**kw):
 
 
 def _upd(**kw):
-    a = dict(state=P, u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=1,
-             y=P + 0x100000, batch=4, dim=64, dstate=16, dtype=1, stream=None)
+    a = dict(state=at(2), u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=1,
+             y=at(1), batch=4, dim=64, dstate=16, dtype=1, stream=None)
     a.update(kw)
     return load().ssm_state_update(a["state"], a["u"], a["delta"], a["A"], a["B"], a["C"],
                                    a["D"], a["z"], a["bias"], a["sp"], a["y"], a["batch"],
@@ -56,7 +62,12 @@ def _upd(**kw):
     (dict(C=None), NULL), (dict(y=None), NULL),
     (dict(u=P + 1), ALIGN), (dict(A=P + 2), ALIGN), (dict(h0=P + 1), ALIGN),
     (dict(dtype=0, u=P + 2), ALIGN), (dict(last=P + 3), ALIGN), (dict(ws=P + 16), ALIGN),
-    (dict(y=P), ALIAS), (dict(z=P + 0x100000), ALIAS),
+    (dict(y=P), ALIAS), (dict(z=at(1)), ALIAS),
+    # overlapping ranges, not only equal pointers: y starting inside u, u
+    # starting inside y, last_state inside B, h0 shared with last_state
+    (dict(y=P + 0x100), ALIAS), (dict(u=at(1) + 0x1000, delta=at(1) + 0x1000), ALIAS),
+    (dict(last=P + 0x40), ALIAS), (dict(h0=at(2), last=at(2)), ALIAS),
+    (dict(last=at(1) + 64 * 2048 * 2 - 4), ALIAS), (dict(last=at(1) + 64 * 2048 * 2), WS),
     (dict(sp=4), FLAGS), (dict(sp=-1), FLAGS), (dict(sp=8 | 1), FLAGS),
 ])
 def test_scan_validation(kw, code):
@@ -67,7 +78,10 @@ def test_scan_workspace_checked_before_launch(monkeypatch):
     need = load().ssm_scan_fwd_workspace_bytes(1, 64, 16, 2048, 1)
     assert need > 0
     assert _scan(ws=None, wsb=0) == WS
-    assert _scan(ws=P, wsb=need - 1) == WS
+    assert _scan(ws=at(3), wsb=need - 1) == WS
+    # the workspace must not overlap a buffer of the call
+    assert _scan(ws=at(1) - 256, wsb=need) == ALIAS
+    assert _scan(ws=P, wsb=need) == ALIAS
 
 
 def test_empty_problems_need_no_gpu():
@@ -80,8 +94,9 @@ def test_empty_problems_need_no_gpu():
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=5), DTYPE), (dict(dstate=6), SHAPE), (dict(batch=-2), SHAPE),
     (dict(state=None), NULL), (dict(u=None), NULL), (dict(B=None), NULL), (dict(y=None), NULL),
-    (dict(state=P + 2), ALIGN), (dict(u=P + 1), ALIGN), (dict(bias=P + 1), ALIGN),
+    (dict(state=at(2) + 2), ALIGN), (dict(u=P + 1), ALIGN), (dict(bias=P + 1), ALIGN),
     (dict(y=P), ALIAS), (dict(sp=6), FLAGS), (dict(sp=1 << 30), FLAGS),
+    (dict(y=at(2) + 4096), ALIAS), (dict(state=P + 256), ALIAS), (dict(state=at(1) - 16), ALIAS),
 ])
 def test_update_validation(kw, code):
     assert _upd(**kw) == code
@@ -118,8 +133,8 @@ def test_python_bbar_mode_is_checked():
 
 
 def _cscan(**kw):
-    a = dict(x=P, w=P + 0x200000, cb=None, K=4, sin=None, sout=None, delta=P, A=P, B=P, C=P, D=None,
-             z=None, bias=None, fl=1, h0=None, y=P + 0x100000, last=None, batch=1, dim=64,
+    a = dict(x=P, w=at(2), cb=None, K=4, sin=None, sout=None, delta=P, A=P, B=P, C=P, D=None,
+             z=None, bias=None, fl=1, h0=None, y=at(1), last=None, batch=1, dim=64,
              dstate=16, L=2048, dtype=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     return load().ssm_conv_scan_fwd(a["x"], a["w"], a["cb"], a["K"], a["sin"], a["sout"], a["delta"],
@@ -129,8 +144,8 @@ def _cscan(**kw):
 
 
 def _cupd(**kw):
-    a = dict(cs=P + 0x300000, state=P, x=P, w=P + 0x200000, cb=None, K=4, delta=P, A=P, B=P, C=P,
-             D=None, z=None, bias=None, fl=1, y=P + 0x100000, batch=4, dim=64, dstate=16, dtype=1,
+    a = dict(cs=at(3), state=at(4), x=P, w=at(2), cb=None, K=4, delta=P, A=P, B=P, C=P,
+             D=None, z=None, bias=None, fl=1, y=at(1), batch=4, dim=64, dstate=16, dtype=1,
              stream=None)
     a.update(kw)
     return load().ssm_conv_state_update(a["cs"], a["state"], a["x"], a["w"], a["cb"], a["K"],
@@ -142,9 +157,10 @@ def _cupd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(K=0), SHAPE), (dict(K=5), SHAPE), (dict(K=-1), SHAPE),
     (dict(w=None), NULL), (dict(x=None), NULL),
-    (dict(w=P + 0x200002), ALIGN), (dict(cb=P + 1), ALIGN), (dict(sin=P + 2), ALIGN),
+    (dict(w=at(2) + 2), ALIGN), (dict(cb=P + 1), ALIGN), (dict(sin=P + 2), ALIGN),
     (dict(sout=P + 3), ALIGN),
-    (dict(sin=P + 0x400000, sout=P + 0x400000), ALIAS), (dict(sout=P + 0x100000), ALIAS),
+    (dict(sin=at(4), sout=at(4)), ALIAS), (dict(sout=at(1)), ALIAS),
+    (dict(sin=at(4), sout=at(4) + 64), ALIAS), (dict(sout=at(2) + 16), ALIAS),
     (dict(y=P), ALIAS), (dict(fl=4), FLAGS), (dict(dtype=3), DTYPE), (dict(dstate=5), SHAPE),
 ])
 def test_conv_scan_validation(kw, code):
@@ -158,7 +174,8 @@ def test_conv_scan_workspace_checked_before_launch():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(K=0), SHAPE), (dict(K=7), SHAPE), (dict(w=None), NULL), (dict(cs=None), NULL),
-    (dict(cs=P + 0x300002), ALIGN), (dict(cs=P), ALIAS), (dict(cs=P + 0x100000), ALIAS),
+    (dict(cs=at(3) + 2), ALIGN), (dict(cs=P), ALIAS), (dict(cs=at(1)), ALIAS),
+    (dict(cs=at(4) + 512), ALIAS), (dict(cs=at(2) + 4), ALIAS),
     (dict(fl=8), FLAGS), (dict(state=None), NULL),
 ])
 def test_conv_update_validation(kw, code):
@@ -171,9 +188,9 @@ def test_conv_update_width_one_needs_no_state():
 
 
 def _bwd(**kw):
-    a = dict(u=P, delta=P + 0x10000, A=P + 0x20000, B=P + 0x30000, C=P + 0x40000, D=None, z=None,
-             bias=None, fl=1, h0=None, dy=P + 0x50000, dlast=None, du=P + 0x60000, dd=P + 0x70000,
-             dA=P + 0x80000, dB=P + 0x90000, dC=P + 0xA0000, dD=None, dz=None, dbias=None, dh0=None,
+    a = dict(u=P, delta=at(1), A=at(2), B=at(3), C=at(4), D=None, z=None,
+             bias=None, fl=1, h0=None, dy=at(5), dlast=None, du=at(6), dd=at(7),
+             dA=at(8), dB=at(9), dC=at(10), dD=None, dz=None, dbias=None, dh0=None,
              batch=1, dim=64, dstate=16, L=2048, dtype=1, ws=None, wsb=0, stream=None)
     a.update(kw)
     return load().ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
@@ -187,9 +204,11 @@ def _bwd(**kw):
     (dict(fl=4), FLAGS), (dict(fl=5), FLAGS), (dict(fl=-1), FLAGS), (dict(dtype=7), DTYPE),
     (dict(dstate=12), SHAPE), (dict(L=-3), SHAPE),
     (dict(dy=None), NULL), (dict(du=None), NULL), (dict(dA=None), NULL), (dict(dB=None), NULL),
-    (dict(z=P + 0xB0000), NULL),
+    (dict(z=at(11)), NULL),
     (dict(du=P + 1), ALIGN), (dict(dA=P + 2), ALIGN), (dict(dlast=P + 1), ALIGN),
-    (dict(du=P), ALIAS), (dict(dB=P + 0x30000), ALIAS), (dict(ddelta=None, dd=P + 0x50000), ALIAS),
+    (dict(du=P), ALIAS), (dict(dB=at(3)), ALIAS), (dict(ddelta=None, dd=at(5)), ALIAS),
+    (dict(dB=at(3) + 64), ALIAS), (dict(dC=at(9) + 2), ALIAS), (dict(dh0=at(6) + 1024), ALIAS),
+    (dict(dD=at(2) + 4), ALIAS),
 ])
 def test_bwd_validation(kw, code):
     assert _bwd(**kw) == code
@@ -203,14 +222,15 @@ def test_bwd_workspace_query_and_check():
     assert need >= fwd + 128 * 16 * 64 * 4 + 2 * 16 * 2048 * 4
     assert lib.ssm_scan_bwd_workspace_bytes(0, 64, 16, 2048, 1) == 0
     assert _bwd(ws=None, wsb=0) == WS
-    assert _bwd(ws=P, wsb=need - 1) == WS
+    assert _bwd(ws=at(12), wsb=need - 1) == WS
+    assert _bwd(ws=at(6) + 256, wsb=need) == ALIAS   # overlaps du
     assert _bwd(batch=0) == OK
 
 
 def _ssd(**kw):
-    a = dict(x=P, dt=P + 0x10000, A=P + 0x20000, B=P + 0x30000, C=P + 0x40000, D=None, z=None,
-             bias=None, fl=1, h0=None, y=P + 0x50000, last=None, batch=1, H=4, hd=64, N=128, L=2048,
-             dtype=1, ws=P + 0x1000000, wsb=1 << 24, stream=None)
+    a = dict(x=P, dt=at(1), A=at(2), B=at(3), C=at(4), D=None, z=None,
+             bias=None, fl=1, h0=None, y=at(5), last=None, batch=1, H=4, hd=64, N=128, L=2048,
+             dtype=1, ws=at(6), wsb=1 << 24, stream=None)
     a.update(kw)
     return load().ssm_ssd_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
                                    a["fl"], a["h0"], a["y"], a["last"], a["batch"], a["H"], a["hd"],
@@ -221,8 +241,9 @@ def _ssd(**kw):
     (dict(hd=32), SHAPE), (dict(N=8), SHAPE), (dict(N=128, dtype=0), SHAPE), (dict(N=256), SHAPE),
     (dict(H=-1), SHAPE), (dict(L=-1), SHAPE), (dict(dtype=4), DTYPE), (dict(fl=8), FLAGS),
     (dict(x=None), NULL), (dict(dt=None), NULL), (dict(A=None), NULL), (dict(y=None), NULL),
-    (dict(x=P + 1), ALIGN), (dict(A=P + 0x20002), ALIGN), (dict(y=P), ALIAS),
-    (dict(ws=P + 0x1000010), ALIGN), (dict(ws=None), WS), (dict(wsb=1000), WS),
+    (dict(x=P + 1), ALIGN), (dict(A=at(2) + 2), ALIGN), (dict(y=P), ALIAS),
+    (dict(y=at(1) + 256), ALIAS), (dict(last=at(5) + 0x10000), ALIAS), (dict(ws=at(4) + 4096), ALIAS),
+    (dict(ws=at(6) + 16), ALIGN), (dict(ws=None), WS), (dict(wsb=1000), WS),
     # 32-bit byte offsets within a head's rows and a batch row's B, C^T
     (dict(L=1 << 23), SHAPE), (dict(L=1 << 23, N=64, dtype=0), SHAPE),
 ])

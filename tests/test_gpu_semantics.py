@@ -1,0 +1,209 @@
+"""GPU checks of what include/ssm.h promises beyond finite, stable inputs:
+
+* NaN and Inf inputs propagate: planted into u, delta and z (and the decode
+  state), the non-finite outputs appear exactly where the fp64 oracle puts
+  them (NaN where it has NaN, Inf of the same sign where it has Inf), and
+  every other output still matches the oracle within the usual tolerance.
+* A > 0 is not rejected: the state grows ("Exercises -- State-space models
+  (Mamba, S4)", the stability exercise: |Abar| > 1 diverges; NN LAB "Mamba",
+  "Proof of Spectral Stability & Contraction Mapping": the bound needs
+  A < 0), and the growing results still match the oracle.
+* The SSD form: a non-finite x at step s makes its channel's outputs
+  non-finite from s on, as in the recurrence, and may also reach the
+  channel's earlier outputs in the same 64-step chunk (the chunk's masked
+  product multiplies it by zeros above the diagonal: 0 * NaN is NaN); every
+  output before that chunk and every other channel stays as the oracle has
+  it."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.configs import ScanConfig, SsdConfig
+from tests.helpers import TOL, assert_parity, gpu_scan, oracle_scan, to_torch
+
+pytestmark = pytest.mark.gpu
+
+NAN, PINF, NINF = float("nan"), float("inf"), float("-inf")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import selective_state_space_28_amd as ssm
+    ssm.load()
+    return torch.device("cuda:0")
+
+
+def _plant(arr, dtype, idx, value):
+    """Set one stored element (float32 value or bf16 bit pattern)."""
+    if dtype == "bf16":
+        arr[idx] = synth.bf16_bits(np.array([value], np.float32))[0] if np.isfinite(value) else \
+            {"nan": 0x7FC0, "inf": 0x7F80, "-inf": 0xFF80}[repr(value)]
+    else:
+        arr[idx] = value
+
+
+def _same_nonfinite(got, ref, what):
+    """NaN exactly where ref has NaN; +-Inf exactly where ref has +-Inf; the
+    finite rest within tolerance of the finite rest of ref."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    gn, rn = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(gn, rn), (f"{what}: NaN at {np.argwhere(gn & ~rn)[:5].tolist()} (GPU only), "
+                                    f"{np.argwhere(rn & ~gn)[:5].tolist()} (oracle only)")
+    gp, rp = np.isposinf(got), np.isposinf(ref)
+    gm, rm = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(gp, rp) and np.array_equal(gm, rm), f"{what}: Inf positions differ"
+    fin = np.isfinite(ref)
+    return int((~fin).sum()), fin
+
+
+PLANTS = [  # (array, (b, d, t), value)
+    ("u", (0, 5, 17), NAN),
+    ("u", (1, 64, 5), PINF),
+    ("u", (0, 66, 120), NINF),
+    ("delta", (0, 70, 100), PINF),
+    ("delta", (1, 3, 40), NINF),
+    ("delta", (1, 100, 200), NAN),
+    ("z", (1, 129, 250), NAN),
+    ("z", (0, 8, 33), NINF),
+    ("z", (0, 9, 34), PINF),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+@pytest.mark.parametrize("segs", [None, 3])
+def test_scan_nan_inf_propagate(dev, dtype, bbar, segs, monkeypatch):
+    if segs is not None:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+    cfg = ScanConfig("naninf", 2, 130, 16, 300, dtype, seed=21, a_jitter=0.1)
+    inp = synth.make_scan_inputs(cfg)
+    for key, idx, v in PLANTS:
+        _plant(inp[key], dtype, idx, v)
+    y, last = gpu_scan(inp, dev, bbar=bbar)
+    yr, lr = oracle_scan(inp, bbar=bbar)
+    ny, fin = _same_nonfinite(y, yr, f"y ({dtype}, {bbar}, segments {segs})")
+    assert ny > 0
+    assert_parity(y[fin], yr[fin], dtype, "finite part of y")
+    nl, finl = _same_nonfinite(last, lr, "last_state")
+    assert_parity(last[finl], lr[finl], "f32", "finite part of last_state")
+    # the planted channels are the only ones with non-finite outputs
+    bad = {(int(b), int(d)) for b, d, _ in np.argwhere(~np.isfinite(y))}
+    assert bad <= {(b, d) for _, (b, d, _), _v in PLANTS}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_nan_inf_propagate(dev, dtype):
+    import torch
+    import selective_state_space_28_amd as ssm
+    from synth.configs import DecodeConfig
+    cfg = DecodeConfig("naninf", 3, 130, 16, 1, dtype, seed=22)
+    p = synth.make_decode_params(cfg)
+    tok = synth.make_decode_step(cfg, 0)
+    h0 = p["h0"].copy()
+    h0[2, 7, 3] = np.nan
+    h0[2, 8, 0] = np.inf
+    for key, idx, v in [("u", (0, 5), NAN), ("u", (1, 64), PINF), ("delta", (0, 70), PINF),
+                        ("delta", (1, 3), NINF), ("delta", (2, 100), NAN), ("z", (1, 129), NAN),
+                        ("z", (0, 8), NINF), ("z", (0, 9), PINF)]:
+        _plant(tok[key], dtype, idx, v)
+    st = to_torch(h0, "f32", dev)
+    t = {k: to_torch(tok[k], dtype, dev) for k in ("u", "delta", "B", "C", "z")}
+    A, D, bias = (to_torch(p[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    y = ssm.ssm_state_update(st, t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias)
+    torch.cuda.synchronize()
+    w = {k: synth.widen(tok[k], dtype) for k in ("u", "delta", "B", "C", "z")}
+    yr, sr = oracle.state_update(h0, w["u"], w["delta"], p["A"], w["B"], w["C"], p["D"], w["z"],
+                                 p["delta_bias"])
+    yg, sg = y.float().cpu().numpy(), st.cpu().numpy()
+    ny, fin = _same_nonfinite(yg, yr, f"decode y ({dtype})")
+    assert ny > 0
+    assert_parity(yg[fin], yr[fin], dtype, "finite part of decode y")
+    _, fins = _same_nonfinite(sg, sr, "decode state")
+    assert_parity(sg[fins], sr[fins], "f32", "finite part of decode state")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+@pytest.mark.parametrize("segs", [None, 4])
+def test_positive_A_grows(dev, dtype, bbar, segs, monkeypatch):
+    """A > 0: every state of every channel grows; the GPU still matches the
+    oracle (tolerance relative to the largest output, as everywhere)."""
+    if segs is not None:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+    cfg = ScanConfig("growth", 2, 70, 16, 400, dtype, seed=23)
+    inp = synth.make_scan_inputs(cfg)
+    inp["A"] = (0.02 * (1 + np.arange(16, dtype=np.float32)))[None, :].repeat(70, 0)
+    y, last = gpu_scan(inp, dev, bbar=bbar)
+    yr, lr = oracle_scan(inp, bbar=bbar)
+    ey = assert_parity(y, yr, dtype, f"y with A > 0 ({bbar})")
+    el = assert_parity(last, lr, "f32", f"last_state with A > 0 ({bbar})")
+    # the oracle's states did grow: the last quarter of the sequence has far
+    # larger outputs than the first quarter
+    q = cfg.seqlen // 4
+    assert np.abs(yr[..., -q:]).max() > 10 * np.abs(yr[..., :q]).max()
+    print(f"A > 0 ({dtype}, {bbar}, segments {segs}): y {ey:.2e}, last_state {el:.2e}, "
+          f"max|y| {np.abs(yr).max():.3g}", flush=True)
+
+
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+def test_positive_A_decode(dev, bbar):
+    import torch
+    import selective_state_space_28_amd as ssm
+    from synth.configs import DecodeConfig
+    cfg = DecodeConfig("growth", 2, 70, 16, 8, "f32", seed=24)
+    p = synth.make_decode_params(cfg)
+    p["A"] = (0.3 * (1 + np.arange(16, dtype=np.float32)))[None, :].repeat(70, 0)
+    st = to_torch(p["h0"], "f32", dev)
+    ref = p["h0"].astype(np.float64)
+    A, D, bias = (to_torch(p[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    for s in range(cfg.steps):
+        tok = synth.make_decode_step(cfg, s)
+        t = {k: to_torch(tok[k], "f32", dev) for k in ("u", "delta", "B", "C", "z")}
+        y = ssm.ssm_state_update(st, t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias, bbar=bbar)
+        torch.cuda.synchronize()
+        w = {k: synth.widen(tok[k], "f32") for k in ("u", "delta", "B", "C", "z")}
+        yr, ref = oracle.state_update(ref, w["u"], w["delta"], p["A"], w["B"], w["C"], p["D"], w["z"],
+                                      p["delta_bias"], bbar=bbar)
+        assert_parity(y.cpu().numpy(), yr, "f32", f"decode y step {s} with A > 0")
+    assert_parity(st.cpu().numpy(), ref, "f32", "decode state with A > 0")
+    assert np.abs(ref).max() > 2 * np.abs(p["h0"]).max()
+
+
+def test_ssd_positive_A(dev):
+    from tests.test_gpu_ssd import gpu_ssd, oracle_ssd
+    cfg = SsdConfig("growth", 1, 3, 64, 16, 300, "f32", seed=25)
+    inp = synth.make_ssd_inputs(cfg)
+    inp["A"] = np.array([0.05, 0.2, 0.5], np.float32)
+    y, last = gpu_ssd(inp, dev)
+    yr, lr = oracle_ssd(inp)
+    assert_parity(y, yr, "f32", "ssd y with A > 0")
+    assert_parity(last, lr, "f32", "ssd last_state with A > 0")
+
+
+def test_ssd_nan_stays_in_its_channel(dev):
+    """A NaN in x at (channel c, step s): channel c's outputs are NaN from s
+    on; its outputs before s's 64-step chunk match the oracle; those in the
+    chunk before s are NaN or match the oracle; every other channel matches
+    the oracle."""
+    from tests.test_gpu_ssd import gpu_ssd, oracle_ssd
+    cfg = SsdConfig("naninf", 1, 2, 64, 16, 300, "f32", seed=26)
+    inp = synth.make_ssd_inputs(cfg)
+    c, s = 70, 150                      # head 1; chunk 2 starts at step 128
+    inp["x"][0, c, s] = np.nan
+    y, _ = gpu_ssd(inp, dev)
+    yr, _ = oracle_ssd(inp)
+    assert np.isnan(yr[0, c, s:]).all() and np.isfinite(yr[0, c, :s]).all()
+    assert np.isnan(y[0, c, s:]).all()
+    others = np.ones(y.shape[1], bool)
+    others[c] = False
+    assert_parity(y[:, others], yr[:, others], "f32", "ssd y of the other channels")
+    assert_parity(y[0, c, :128], yr[0, c, :128], "f32", "ssd y before the chunk")
+    mid = y[0, c, 128:s]
+    ok = np.isfinite(mid)
+    assert np.all(np.isnan(mid[~ok]))
+    if ok.any():
+        assert np.max(np.abs(mid[ok] - yr[0, c, 128:s][ok])) <= TOL["f32"] * np.abs(yr[0, c, :s]).max()

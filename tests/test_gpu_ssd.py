@@ -113,21 +113,3 @@ def test_ssd_matches_diagonal_scan(dev):
     torch.cuda.synchronize()
     assert_parity(y, y2.cpu().numpy().astype(np.float64), "f32", "ssd vs diagonal scan")
 
-
-def test_ssd_full_size_sampled_heads(dev):
-    """The Mamba-2-shaped workload (batch 16, 80 heads x 64, N 128, L 2048,
-    bf16): every output computed, sampled heads of two batch rows checked."""
-    cfg = synth.SSD_CONFIG
-    print("ssd full size: generating", flush=True)
-    inp = synth.make_ssd_inputs(cfg)
-    y, last = gpu_ssd(inp, dev)
-    assert np.all(np.isfinite(y))
-    heads = [0, 37, cfg.nheads - 1]
-    for b in (0, cfg.batch - 1):
-        sub = {k: (v[b:b + 1] if isinstance(v, np.ndarray) and k in ("x", "dt", "B", "C", "z") else v)
-               for k, v in inp.items()}
-        yr, lr = oracle_ssd(sub, heads=heads, nthreads=16)
-        ch = np.concatenate([np.arange(h * 64, (h + 1) * 64) for h in heads])
-        err = assert_parity(y[b:b + 1, ch], yr, "bf16", f"ssd y batch {b}")
-        assert_parity(last[b:b + 1, ch], lr, "bf16", f"ssd last_state batch {b}")
-        print(f"ssd full size batch {b}: y err {err:.2e}", flush=True)

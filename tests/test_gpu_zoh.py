@@ -1,6 +1,6 @@
 """GPU parity of the zero-order-hold input term (bbar='zoh') against the
-oracle: scan (every state count, both storage types, split sequences, a
-full-size sampled run) and the decode step.
+oracle: scan (every state count, both storage types, split sequences; the
+full-size runs are in test_gpu_full.py) and the decode step.
 
 Zero-order hold: "Paper: Mamba" course module, "Math & data structures"
 (Bbar = (exp(Delta A) - 1)/A B); NN LAB "Mamba" page, "Derivation of the
@@ -13,7 +13,7 @@ import pytest
 import oracle
 import synth
 from synth.configs import DecodeConfig, ScanConfig
-from tests.helpers import TOL, assert_parity, gpu_scan, oracle_scan, sub_problem, to_torch
+from tests.helpers import TOL, assert_parity, gpu_scan, oracle_scan, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -85,21 +85,6 @@ def test_zoh_single_state_is_the_gated_recurrence(dev):
             ref[d, t] = h
     assert_parity(y[0], ref, "f32")
     assert_parity(last[0, :, 0], ref[:, -1], "f32", "last_state")
-
-
-def test_zoh_full_size_c1_sampled(dev):
-    """The 130M-shaped fp32 workload with the zero-order-hold term, default
-    launch plan; sampled channels against the oracle."""
-    cfg = synth.SCAN_CONFIGS["c1"]
-    inp = synth.make_scan_inputs(cfg)
-    y, last = gpu_scan(inp, dev, bbar="zoh")
-    assert np.all(np.isfinite(y))
-    rng = np.random.default_rng(62)
-    for b in (0, cfg.batch - 1):
-        ds = sorted({0, 63, 64, cfg.dim - 1, *rng.choice(cfg.dim, size=8, replace=False).tolist()})
-        yr, lr = oracle_scan(sub_problem(inp, b, ds), nthreads=16, bbar="zoh")
-        assert_parity(y[b:b + 1, ds], yr, "f32", f"c1 zoh y batch {b}")
-        assert_parity(last[b:b + 1, ds], lr, "f32", f"c1 zoh last_state batch {b}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

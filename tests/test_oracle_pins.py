@@ -225,6 +225,79 @@ def test_dskip_and_gate_by_definition():
     np.testing.assert_allclose(y60 / 60.0, kw["D"][None, :, None] * kw["u"], rtol=1e-14)
 
 
+def _oracle_gate(z):
+    """silu(z) read off the scan oracle: B = 0 keeps the state at 0, D = 1
+    and u = 1, so y = (C.h + D u) silu(z) = silu(z)."""
+    z = np.asarray(z, np.float64)
+    L = z.size
+    y, _ = oracle.scan_fwd(np.ones((1, 1, L)), np.zeros((1, 1, L)), np.full((1, 1), -1.0),
+                           np.zeros((1, 1, L)), np.ones((1, 1, L)), D=np.ones(1),
+                           z=z.reshape(1, 1, L))
+    return y[0, 0]
+
+
+def _oracle_conv_silu(x):
+    """silu(x) read off the convolution oracle: one identity tap, no bias."""
+    x = np.asarray(x, np.float64)
+    u, _ = oracle.causal_conv1d_silu(x.reshape(1, 1, -1), np.ones((1, 1)))
+    return u[0, 0]
+
+
+def _oracle_decode_gate(z):
+    """silu(z) read off the decode oracle, as _oracle_gate."""
+    z = np.asarray(z, np.float64)
+    n = z.size
+    y, _ = oracle.state_update(np.zeros((1, n, 1)), np.ones((1, n)), np.zeros((1, n)),
+                               np.full((n, 1), -1.0), np.zeros((1, 1)), np.ones((1, 1)),
+                               D=np.ones(n), z=z.reshape(1, n))
+    return y[0]
+
+
+_Z = np.linspace(-30.0, 30.0, 2401)
+
+
+def _silu_identities_hold(f):
+    """The two identities that fix silu(z) = z sigma(z) = z / (1 + e^-z):
+    silu(z) - silu(-z) = z (as sigma(z) + sigma(-z) = 1), and
+    silu(z) = (z/2)(1 + tanh(z/2)) (as sigma(z) = (1 + tanh(z/2))/2, with
+    numpy's tanh on the right; 1 + tanh(z/2) cancels for negative z, so the
+    absolute tolerance is a few ulps of z there)."""
+    pos, neg = f(_Z), f(-_Z)
+    odd = np.allclose(pos - neg, _Z, rtol=0.0, atol=1e-12)
+    tanh_form = np.allclose(pos, 0.5 * _Z * (1.0 + np.tanh(0.5 * _Z)), rtol=1e-13, atol=1e-13)
+    return odd and tanh_form
+
+
+@pytest.mark.parametrize("reader", [_oracle_gate, _oracle_conv_silu, _oracle_decode_gate])
+def test_silu_identities(reader):
+    assert _silu_identities_hold(reader)
+
+
+@pytest.mark.parametrize("wrong", [
+    lambda z: z / (1.0 + np.exp(-z / 2)),        # z sigma(z/2): odd identity holds, tanh form fails
+    lambda z: z / (1.0 + np.exp(z)),             # z sigma(-z)
+    lambda z: z / (2.0 + np.exp(-z)),            # a wrong constant
+    lambda z: np.tanh(z) * z,                    # a different gate
+])
+def test_silu_identities_reject_wrong_shapes(wrong):
+    assert not _silu_identities_hold(wrong)
+
+
+def test_dskip_enters_linearly_as_D_times_u():
+    """The D-skip term adds exactly D u (gated) to the readout: y is affine
+    in D with slope u silu(z), and D = 0 leaves the state-space part."""
+    rng = np.random.default_rng(14)
+    kw = _tiny_case(rng, batch=2, dim=3, N=4, L=11)
+    y1, _ = oracle.scan_fwd(**kw)
+    kw0 = dict(kw, D=np.zeros_like(kw["D"]))
+    y0, _ = oracle.scan_fwd(**kw0)
+    kw2 = dict(kw, D=2.0 * kw["D"])
+    y2, _ = oracle.scan_fwd(**kw2)
+    slope = kw["u"] * _oracle_gate(kw["z"].ravel()).reshape(kw["z"].shape)
+    np.testing.assert_allclose(y1 - y0, kw["D"][None, :, None] * slope, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(y2 - y1, y1 - y0, rtol=1e-12, atol=1e-14)
+
+
 # ------------------------------------------------------- scans and the operator
 @pytest.mark.parametrize("L", [1, 7, 16, 33])
 def test_scans_equal_sequential_and_oracle(L):
