@@ -10,15 +10,29 @@ workload (ssm_state_update, batch 256, D 5120, N 16, 64 steps) as a second
 object, the roofline of the dominant kernel, and the fp64 CPU oracle timed on
 a bounded sample of the same workload on this host.
 
+HBM traffic is read from the GPU's counters in the same run: before this
+process touches the GPU it starts three child processes under rocprofv3
+(FETCH_SIZE, then WRITE_SIZE, each with a plain device copy of known size as
+the calibration, then a kernel trace), each running the same scan step
+(`bench.py --counters-child`), and parses their CSV output.
+
+Every timed workload first runs its warm-up calls and then a settle phase of
+back-to-back calls lasting at least --settle-ms, so that the timed calls see
+the GPU's sustained clock whatever --warmup is.
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
+import csv
+import glob
 import json
 import os
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -53,12 +67,13 @@ OPS_PER_ELEMENT_CONV = CONV_WIDTH + 4
 # FMA, dB and dC terms, the carry Abar*lambda) and one add each for the
 # channel sums of dB and dC.
 OPS_PER_ELEMENT_STATE_BWD = 16
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_kernel_c3_traffic.json")
 KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 0>"
 KERNEL_NAME_ZOH = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 1>"
 KERNEL_NAME_CONV = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 2>"
-KERNEL_SOURCES = ["selective_state_space_28_amd/csrc/scan_fwd.hip",
-                  "selective_state_space_28_amd/csrc/ssm_math.hpp"]
+PACK_KERNEL_NAME = "ssm::pack_bc_kernel<unsigned short, 4, 4>"
+# the plain device copy that calibrates the byte counters: 1 GiB, three times
+CALIB_BYTES = 1 << 30
+CALIB_COPIES = 3
 
 
 def scan_bytes(cfg) -> int:
@@ -104,72 +119,105 @@ def decode_bytes(cfg) -> int:
     return state + tok + bc + params
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+def _to_dev(a, dt, dev):
+    import torch
+    if a is None:
+        return None
+    if dt == "bf16" and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 
-def traffic_per_launch():
-    """HBM bytes per launch measured by rocprofv3 counters (committed under
-    profiles/), or None when absent or taken on a different kernel source."""
-    try:
-        with open(PROFILE_TRAFFIC) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+def settle(step, dev, min_ms):
+    """Back-to-back calls until at least min_ms of wall time has passed (the
+    GPU's clock ramps up over the first tens of milliseconds of sustained
+    load after idling).  Returns (calls, ms)."""
+    import torch
+    if min_ms <= 0:
+        return 0, 0.0
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        for _ in range(8):
+            step()
+        calls += 8
+        torch.cuda.synchronize(dev)
+        ms = (time.perf_counter() - t0) * 1e3
+        if ms >= min_ms:
+            return calls, round(ms, 1)
+
+
+def timed(step, dev, stream, steps):
+    """Mean milliseconds per call over `steps` calls, each bracketed by HIP
+    events recorded on the stream the kernels run on."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        s_.record(stream)
+        step()
+        e_.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = np.array([s_.elapsed_time(e_) for s_, e_ in ev])
+    return float(per.mean()), wall
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     # The GPU's clock ramps up over the first ~35 ms of sustained load after
-    # idling (c3 step: about 0.70 ms for the first calls, 0.58 ms from about
-    # the 50th on), so the default warm-up covers that ramp and the timed steps
-    # see the sustained rate.
-    ap.add_argument("--warmup", type=int, default=100)
+    # idling (c3 step: about 0.70 ms for the first calls, 0.58 ms once
+    # settled), and the ramp repeats after about two seconds of idle; every
+    # workload therefore runs a settle phase of this length before its timed
+    # calls, whatever --warmup is.
+    ap.add_argument("--settle-ms", type=float, default=300.0)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--no-counters", action="store_true",
+                    help="skip the rocprofv3 child runs (counters and kernel trace)")
+    ap.add_argument("--prof-dir", default=None,
+                    help="keep the child runs' rocprofv3 output in this directory")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-split", action="store_true",
                     help="skip the long-sequence workloads (c1, c2) that split the sequence")
     ap.add_argument("--split-only", action="store_true",
                     help="run only the long-sequence workloads (c1, c2) and print their objects")
     ap.add_argument("--no-ssd", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy three times (reference for the "
-                         "HBM byte counters) and exit")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--counters-child", action="store_true",
+                    help="(internal) the program the rocprofv3 child runs execute")
+    ap.add_argument("--child-steps", type=int, default=3)
+    ap.add_argument("--child-calibrate", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the scan is data-parallel over channels and batch rows, so shards would need "
               "no communication, but no multi-GPU path is built).", file=sys.stderr)
         return 2
+    if args.counters_child:
+        return counters_child(args)
+
+    # counters and kernel trace first, in child processes, before this
+    # process touches the GPU
+    prof = None
+    if not args.no_counters and not args.split_only:
+        prof = collect_profiles(args)
 
     import torch
     import selective_state_space_28_amd as ssm
     import synth
 
     dev = torch.device("cuda:0")
-    if args.copy_calibration:
-        n = 1 << 30
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize(dev)
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
-        return 0
     ssm.load()
     if args.split_only:
-        print(json.dumps({f"split_{name}": bench_split(dev, name, args.steps, args.warmup)
+        print(json.dumps({f"split_{name}": bench_split(dev, name, args.steps, args.warmup,
+                                                       args.settle_ms)
                           for name in ("c1", "c2")}), flush=True)
         return 0
     cfg = synth.SCAN_CONFIGS["c3"]
@@ -177,16 +225,9 @@ def main():
     inp = synth.make_scan_inputs(cfg)
     gen_s = time.time() - t_gen
 
-    def dev_t(a, dt):
-        if a is None:
-            return None
-        if dt == "bf16" and a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
-
     dt = cfg.dtype
-    u, delta, B, C, z = (dev_t(inp[k], dt) for k in ("u", "delta", "B", "C", "z"))
-    A, D, bias = (dev_t(inp[k], "f32") for k in ("A", "D", "delta_bias"))
+    u, delta, B, C, z = (_to_dev(inp[k], dt, dev) for k in ("u", "delta", "B", "C", "z"))
+    A, D, bias = (_to_dev(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
     y = torch.empty_like(u)
     need = ssm.ssm_scan_fwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen, u.dtype)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -197,41 +238,39 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize(dev)
-    # per-launch events on the stream the kernels run on (torch's current one)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
-        step()
-        e.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    per = np.array([s.elapsed_time(e) for s, e in ev])  # ms
-    ms = float(per.mean())
-    wall_ms = wall * 1e3 / args.steps
+    settle_calls, settle_ms = settle(step, dev, args.settle_ms)
+    ms, wall_ms = timed(step, dev, stream, args.steps)
     elements = cfg.batch * cfg.dim * cfg.seqlen
     value = elements / (ms * 1e-3)
     alg_bytes = scan_bytes(cfg)
     alg_gbps = alg_bytes / (ms * 1e-3) / 1e9
     ops = elements * cfg.dstate * OPS_PER_ELEMENT_STATE
     alu_tops = ops / (ms * 1e-3) / 1e12
-    # the binding roof is the one whose lower-bound time is larger
+    scan_prof = (prof or {}).get("kernels", {}).get(KERNEL_NAME, {})
+    traffic = scan_prof.get("hbm_bytes_per_launch")
+    trace_ns = scan_prof.get("trace_avg_ns")
+    hbm_view = {"achieved": round(alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(alg_gbps / HBM_PEAK_GBPS, 4),
+                "note": "algorithmic bytes per launch / event-timed step"}
+    if traffic:
+        hbm_view["measured_GBps"] = round(traffic / (ms * 1e-3) / 1e9, 1)
+        hbm_view["measured_frac"] = round(traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+    # The binding roof is the one whose lower-bound time is larger: here the
+    # VALU (5 fp32 instructions per (element, state) at one per lane per
+    # clock) rather than HBM.
     t_hbm = alg_bytes / (HBM_PEAK_GBPS * 1e9)
     t_alu = ops / (VALU_PEAK_TOPS * 1e12)
-    traffic = traffic_per_launch()
-    if t_alu >= t_hbm:
-        roof = {"bound": "alu", "achieved": round(alu_tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
-                "unit": "TOP/s", "frac": round(alu_tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
-                "kernel": KERNEL_NAME,
-                "work_per_launch": {"ops": ops, "bytes": alg_bytes}}
-    else:
-        roof = {"bound": "hbm", "achieved": round(alg_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(alg_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": KERNEL_NAME,
-                "work_per_launch": {"ops": ops, "bytes": alg_bytes}}
+    roof = {"bound": "alu" if t_alu >= t_hbm else "hbm",
+            "achieved": round(alu_tops, 3), "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
+            "frac": round(alu_tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
+            "kernel": KERNEL_NAME,
+            "work_per_launch": {"ops": ops, "bytes": alg_bytes},
+            "lower_bound_us": {"alu": round(t_alu * 1e6, 1), "hbm": round(t_hbm * 1e6, 1)},
+            "hbm": hbm_view,
+            "kernel_trace_avg_ms": (round(trace_ns / 1e6, 4) if trace_ns else None)}
+    if t_alu < t_hbm:
+        roof.update({"achieved": round(alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(alg_gbps / HBM_PEAK_GBPS, 4)})
 
     out = {
         "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
@@ -241,16 +280,19 @@ def main():
         "config": {"workload": "mamba-2.8b-shaped layer scan: batch 16, D 5120, N 16, L 2048, "
                                "bf16 inputs/output, fp32 state, silu gate, D-skip, A jittered",
                    "batch": cfg.batch, "dim": cfg.dim, "dstate": cfg.dstate,
-                   "seqlen": cfg.seqlen, "io_dtype": "bf16", "seed": cfg.seed},
+                   "seqlen": cfg.seqlen, "io_dtype": "bf16", "state_dtype": "f32", "seed": cfg.seed},
+        "settle": {"calls": settle_calls, "ms": settle_ms, "min_ms": args.settle_ms},
         "hbm": {"algorithmic_bytes": alg_bytes, "algorithmic_GBps": round(alg_gbps, 1),
                 "frac_of_peak": round(alg_gbps / HBM_PEAK_GBPS, 4),
                 "measured_bytes_per_launch": traffic,
-                "measured_GBps": (round(traffic / (ms * 1e-3) / 1e9, 1) if traffic else None),
+                "measured_GBps": hbm_view.get("measured_GBps"),
                 "copy_GBps": copy_rate(dev, stream),
                 "copy_note": "practical roof: torch device-to-device copy of 1 GiB buffers (bytes read + written)"},
         "wall_ms_per_step": wall_ms,
         "roofline": roof,
     }
+    if prof is not None:
+        out["counters"] = prof
 
     # the same workload with the zero-order-hold input term (flag of the same
     # entry point), timed the same way
@@ -259,13 +301,8 @@ def main():
 
     for _ in range(args.warmup):
         step_zoh()
-    torch.cuda.synchronize(dev)
-    for s, e in ev:
-        s.record(stream)
-        step_zoh()
-        e.record(stream)
-    torch.cuda.synchronize(dev)
-    ms_z = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    settle(step_zoh, dev, args.settle_ms)
+    ms_z, _ = timed(step_zoh, dev, stream, args.steps)
     ops_z = elements * cfg.dstate * OPS_PER_ELEMENT_STATE_ZOH
     tops_z = ops_z / (ms_z * 1e-3) / 1e12
     out["zoh"] = {"workload": "the same scan with the zero-order-hold input term (bbar='zoh')",
@@ -275,7 +312,8 @@ def main():
                                "frac": round(tops_z / VALU_PEAK_TOPS, 4),
                                "kernel": KERNEL_NAME_ZOH,
                                "ops_per_launch": ops_z,
-                               "ops_executed_per_element_state": OPS_EXECUTED_PER_ELEMENT_STATE_ZOH}}
+                               "ops_executed_per_element_state": OPS_EXECUTED_PER_ELEMENT_STATE_ZOH,
+                               "hbm_frac": round(alg_bytes / (ms_z * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
 
     # the same workload with the width-4 convolution prologue fused in (x is
     # the u draw; taps and bias from the generator)
@@ -288,15 +326,11 @@ def main():
 
     for _ in range(args.warmup):
         step_conv()
-    torch.cuda.synchronize(dev)
-    for s, e in ev:
-        s.record(stream)
-        step_conv()
-        e.record(stream)
-    torch.cuda.synchronize(dev)
-    ms_c = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    settle(step_conv, dev, args.settle_ms)
+    ms_c, _ = timed(step_conv, dev, stream, args.steps)
     ops_c = elements * (cfg.dstate * OPS_PER_ELEMENT_STATE + OPS_PER_ELEMENT_CONV)
     tops_c = ops_c / (ms_c * 1e-3) / 1e12
+    conv_prof = (prof or {}).get("kernels", {}).get(KERNEL_NAME_CONV, {})
     out["conv"] = {"workload": f"the same scan with the causal depthwise conv1d + silu prologue "
                                f"fused in (width {CONV_WIDTH}, ssm_conv_scan_fwd)",
                    "ms_per_step": ms_c, "value": elements / (ms_c * 1e-3), "unit": "elements/s",
@@ -304,70 +338,262 @@ def main():
                                 "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
                                 "frac": round(tops_c / VALU_PEAK_TOPS, 4),
                                 "kernel": KERNEL_NAME_CONV,
-                                "ops_per_launch": ops_c}}
+                                "ops_per_launch": ops_c,
+                                "traffic": conv_prof.get("hbm_bytes_per_launch"),
+                                "hbm_frac": round(alg_bytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}}
 
-    # the backward pass of the same workload (dy ~ N(0, 1), bf16)
-    gy = torch.randn(u.shape, generator=torch.Generator(device=dev).manual_seed(5), device=dev,
-                     dtype=torch.float32).to(u.dtype)
-    bws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen,
-                                                       u.dtype), dtype=torch.uint8, device=dev)
+    if not args.no_bwd:
+        # the backward pass of the same workload (dy ~ N(0, 1), bf16)
+        gy = torch.randn(u.shape, generator=torch.Generator(device=dev).manual_seed(5), device=dev,
+                         dtype=torch.float32).to(u.dtype)
+        bws = torch.empty(ssm.ssm_scan_bwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate,
+                                                           cfg.seqlen, u.dtype),
+                          dtype=torch.uint8, device=dev)
 
-    def step_bwd():
-        ssm.ssm_scan_bwd(u, delta, A, B, C, D, z, bias, dy=gy, workspace=bws)
+        def step_bwd():
+            ssm.ssm_scan_bwd(u, delta, A, B, C, D, z, bias, dy=gy, workspace=bws)
 
-    for _ in range(max(1, min(args.warmup, 3))):  # the GPU is warm by now
         step_bwd()
-    torch.cuda.synchronize(dev)
-    nb = max(1, args.steps // 5)
-    for s, e in ev[:nb]:
-        s.record(stream)
-        step_bwd()
-        e.record(stream)
-    torch.cuda.synchronize(dev)
-    ms_b = float(np.mean([s.elapsed_time(e) for s, e in ev[:nb]]))
-    ops_b = elements * cfg.dstate * OPS_PER_ELEMENT_STATE_BWD
-    tops_b = ops_b / (ms_b * 1e-3) / 1e12
-    out["bwd"] = {"workload": "ssm_scan_bwd of the same scan (all gradients, states recomputed)",
-                  "steps": nb, "ms_per_step": ms_b, "value": elements / (ms_b * 1e-3),
-                  "unit": "elements/s",
-                  "roofline": {"bound": "alu", "achieved": round(tops_b, 3),
-                               "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
-                               "frac": round(tops_b / VALU_PEAK_TOPS, 4),
-                               "kernel": "ssm::bwd_kernel<unsigned short, 4, 4, 16, false, 4> (+ "
-                                         "checkpoint pass and sums)",
-                               "ops_per_launch": ops_b}}
+        settle(step_bwd, dev, args.settle_ms)
+        nb = max(1, args.steps // 5)
+        ms_b, _ = timed(step_bwd, dev, stream, nb)
+        ops_b = elements * cfg.dstate * OPS_PER_ELEMENT_STATE_BWD
+        tops_b = ops_b / (ms_b * 1e-3) / 1e12
+        out["bwd"] = {"workload": "ssm_scan_bwd of the same scan (all gradients, states recomputed)",
+                      "steps": nb, "ms_per_step": ms_b, "value": elements / (ms_b * 1e-3),
+                      "unit": "elements/s",
+                      "roofline": {"bound": "alu", "achieved": round(tops_b, 3),
+                                   "peak": round(VALU_PEAK_TOPS, 3), "unit": "TOP/s",
+                                   "frac": round(tops_b / VALU_PEAK_TOPS, 4),
+                                   "kernel": "ssm::bwd_kernel<unsigned short, 4, 4, 16, false, 4> (+ "
+                                             "checkpoint pass and sums)",
+                                   "ops_per_launch": ops_b}}
 
-    # the same backward with the zero-order-hold input term
-    def step_bwd_zoh():
-        ssm.ssm_scan_bwd(u, delta, A, B, C, D, z, bias, dy=gy, bbar="zoh", workspace=bws)
+        # the same backward with the zero-order-hold input term
+        def step_bwd_zoh():
+            ssm.ssm_scan_bwd(u, delta, A, B, C, D, z, bias, dy=gy, bbar="zoh", workspace=bws)
 
-    step_bwd_zoh()
-    torch.cuda.synchronize(dev)
-    for s, e in ev[:nb]:
-        s.record(stream)
         step_bwd_zoh()
-        e.record(stream)
-    torch.cuda.synchronize(dev)
-    ms_bz = float(np.mean([s.elapsed_time(e) for s, e in ev[:nb]]))
-    out["bwd_zoh"] = {"workload": "ssm_scan_bwd of the same scan with the zero-order-hold input term",
-                      "steps": nb, "ms_per_step": ms_bz, "value": elements / (ms_bz * 1e-3),
-                      "unit": "elements/s"}
-    del gy, bws
+        settle(step_bwd_zoh, dev, args.settle_ms)
+        ms_bz, _ = timed(step_bwd_zoh, dev, stream, nb)
+        out["bwd_zoh"] = {"workload": "ssm_scan_bwd of the same scan with the zero-order-hold input term",
+                          "steps": nb, "ms_per_step": ms_bz, "value": elements / (ms_bz * 1e-3),
+                          "unit": "elements/s"}
+        del gy, bws
     del u, delta, B, C, z, y, ws
 
     if not args.no_split:
         for name in ("c1", "c2"):
-            out[f"split_{name}"] = bench_split(dev, name, args.steps, args.warmup)
+            out[f"split_{name}"] = bench_split(dev, name, args.steps, args.warmup, args.settle_ms)
     if not args.no_decode:
         out["decode"] = bench_decode(dev, args.decode_steps)
     if not args.no_ssd:
-        out["ssd"] = bench_ssd(dev, args.steps, args.warmup)
+        out["ssd"] = bench_ssd(dev, args.steps, args.warmup, args.settle_ms)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp)
     out["input_generation_s"] = round(gen_s, 2)
     print(json.dumps(out), flush=True)
     return 0
+
+
+# ---------------------------------------------------------------- rocprofv3 children
+def counters_child(args):
+    """The program each rocprofv3 child run executes: the c3 scan step
+    (warm-up, settle, then --child-steps calls) and, with --child-calibrate,
+    afterwards CALIB_COPIES plain device copies of CALIB_BYTES (the known
+    size that calibrates the byte counters).  Prints one JSON line."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    import synth
+    dev = torch.device("cuda:0")
+    ssm.load()
+    cfg = synth.SCAN_CONFIGS["c3"]
+    inp = synth.make_scan_inputs(cfg)
+    u, delta, B, C, z = (_to_dev(inp[k], cfg.dtype, dev) for k in ("u", "delta", "B", "C", "z"))
+    A, D, bias = (_to_dev(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    y = torch.empty_like(u)
+    ws = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate,
+                                                             cfg.seqlen, u.dtype)),
+                     dtype=torch.uint8, device=dev)
+    cp = synth.make_conv_params(cfg.dim, CONV_WIDTH, cfg.seed)
+    cw, cb = torch.from_numpy(cp["conv_w"]).to(dev), torch.from_numpy(cp["conv_b"]).to(dev)
+
+    def step():
+        ssm.ssm_scan_fwd(u, delta, A, B, C, D, z, bias, out=y, workspace=ws)
+
+    def step_conv():
+        ssm.ssm_conv_scan_fwd(u, cw, cb, delta, A, B, C, D, z, bias, out=y, workspace=ws)
+
+    for fn in (step, step_conv):
+        fn()
+        settle(fn, dev, args.settle_ms if args.child_steps > 3 else 0.0)
+        for _ in range(args.child_steps):
+            fn()
+        torch.cuda.synchronize(dev)
+    del u, delta, B, C, z, y, ws
+    if args.child_calibrate:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        for _ in range(CALIB_COPIES):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+    print(json.dumps({"counters_child": "ok", "steps": args.child_steps}), flush=True)
+    return 0
+
+
+def _csv_rows(directory, suffix):
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _field(row, *names):
+    for n in names:
+        if n in row and row[n] not in (None, ""):
+            return row[n]
+    low = {k.lower(): v for k, v in row.items() if k}
+    for n in names:
+        v = low.get(n.lower())
+        if v not in (None, ""):
+            return v
+    return None
+
+
+def _kname(row):
+    name = _field(row, "Kernel_Name", "KernelName", "Kernel-Name") or ""
+    return name[5:] if name.startswith("void ") else name
+
+
+def _counter_per_dispatch(rows, counter):
+    """{dispatch id: (kernel name, summed value)} of one counter."""
+    out = {}
+    for r in rows:
+        if (_field(r, "Counter_Name", "Counter-Name") or "") != counter:
+            continue
+        did = int(float(_field(r, "Dispatch_Id", "Dispatch_ID", "Dispatch-Id") or -1))
+        val = float(_field(r, "Counter_Value", "Counter-Value") or 0.0)
+        name, acc = out.get(did, (_kname(r), 0.0))
+        out[did] = (name, acc + val)
+    return out
+
+
+def _starts(name, prefix):
+    return name == prefix or name.startswith(prefix + "(") or name.startswith(prefix + " ")
+
+
+def parse_profile_dirs(dirs, steps):
+    """Bytes per launch and traced durations from the child runs' CSV files.
+
+    dirs: {"fetch": dir, "write": dir, "trace": dir} (any may be missing).
+    In the fetch and write runs, the copies after the last scan dispatch are
+    the calibration: CALIB_COPIES x CALIB_BYTES read and written, so
+    scale = known bytes / counted bytes turns a counter reading into bytes.
+    Returns (calibration, {kernel: figures}, first error or None)."""
+    kernels, calib, err = {}, {}, None
+    for tag, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        if tag not in dirs:
+            continue
+        per = _counter_per_dispatch(_csv_rows(dirs[tag], "counter_collection.csv"), counter)
+        if not per:
+            err = err or f"no {counter} rows in the '{tag}' run's output"
+            continue
+        last_scan = max((i for i, (n, _) in per.items() if _starts(n, KERNEL_NAME)), default=-1)
+        copy_kib = sum(v for i, (n, v) in per.items() if i > last_scan and "copy" in n.lower())
+        if copy_kib <= 0:
+            err = err or f"no calibration copy found in the '{tag}' run"
+            continue
+        scale = CALIB_COPIES * CALIB_BYTES / (copy_kib * 1024.0)
+        calib[counter] = {"copy_KiB": round(copy_kib, 1), "scale": round(scale, 4)}
+        for name in (KERNEL_NAME, KERNEL_NAME_CONV, PACK_KERNEL_NAME):
+            vals = [v for i, (n, v) in per.items() if _starts(n, name)]
+            if vals:
+                k = kernels.setdefault(name, {})
+                k[f"{counter}_KiB"] = round(float(np.mean(vals)), 1)
+                k["read_bytes" if counter == "FETCH_SIZE" else "write_bytes"] = \
+                    round(float(np.mean(vals)) * 1024.0 * scale)
+                k[f"{counter}_dispatches"] = len(vals)
+    for name, k in kernels.items():
+        if "read_bytes" in k and "write_bytes" in k:
+            k["hbm_bytes_per_launch"] = k["read_bytes"] + k["write_bytes"]
+    if "trace" in dirs:
+        rows = _csv_rows(dirs["trace"], "kernel_trace.csv")
+        for name in (KERNEL_NAME, KERNEL_NAME_CONV, PACK_KERNEL_NAME):
+            durs = []
+            for r in rows:
+                if not _starts(_kname(r), name):
+                    continue
+                t0 = float(_field(r, "Start_Timestamp", "Start-Timestamp", "BeginNs") or 0)
+                t1 = float(_field(r, "End_Timestamp", "End-Timestamp", "EndNs") or 0)
+                durs.append((t0, t1 - t0))
+            durs.sort()
+            if durs:
+                last = [d for _, d in durs[-steps:]]
+                k = kernels.setdefault(name, {})
+                k["trace_avg_ns"] = round(float(np.mean(last)), 1)
+                k["trace_dispatches_averaged"] = len(last)
+    return calib, kernels, err
+
+
+def collect_profiles(args):
+    """Three child runs of this program under rocprofv3, before this process
+    touches the GPU: FETCH_SIZE and WRITE_SIZE per dispatch (each run ends
+    with plain copies of known size, whose counter reading gives the factor
+    that turns the counter into bytes), then a kernel trace of the same step
+    after a settle phase.  Returns per-kernel bytes per launch and the traced
+    mean duration of the last --steps dispatches; or an 'error' entry."""
+    exe = shutil.which("rocprofv3")
+    if exe is None:
+        return {"error": "rocprofv3 not found: traffic not measured"}
+    keep = args.prof_dir is not None
+    base = os.path.abspath(args.prof_dir) if keep else tempfile.mkdtemp(prefix="ssm_bench_prof_")
+    os.makedirs(base, exist_ok=True)
+    env = dict(os.environ)
+    env.setdefault("TMPDIR", "/tmp")
+    me = os.path.abspath(__file__)
+    runs = [("fetch", ["--kernel-trace", "--pmc", "FETCH_SIZE"], ["--child-calibrate"], 3),
+            ("write", ["--kernel-trace", "--pmc", "WRITE_SIZE"], ["--child-calibrate"], 3),
+            ("trace", ["--kernel-trace", "--stats"], [], args.steps)]
+    res = {"commands": [], "note": "child runs of this program under rocprofv3, in this bench run"}
+    dirs = {}
+    for tag, popts, copts, nsteps in runs:
+        d = os.path.join(base, tag)
+        cmd = ["timeout", "-s", "KILL", "240", exe, *popts, "-f", "csv", "-d", d, "-o", tag, "--",
+               sys.executable, me, "--counters-child", "--child-steps", str(nsteps),
+               "--settle-ms", str(args.settle_ms), *copts]
+        res["commands"].append(" ".join(["rocprofv3", *popts, "-f", "csv", "-d", "<dir>", "-o", tag,
+                                         "--", "python3", "bench.py", "--counters-child",
+                                         "--child-steps", str(nsteps), *copts]))
+        print(f"[bench] rocprofv3 child run '{tag}' ...", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        try:
+            r = subprocess.run(cmd, cwd=base, env=env, capture_output=True, text=True, timeout=270)
+        except subprocess.TimeoutExpired:
+            res["error"] = f"child run '{tag}' timed out"
+            break
+        ok = '"counters_child": "ok"' in r.stdout
+        print(f"[bench]   rc {r.returncode}, {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+        if not ok:
+            res["error"] = (f"child run '{tag}' failed (rc {r.returncode}): "
+                            + (r.stderr or r.stdout)[-400:])
+            break
+        dirs[tag] = d
+    try:
+        calib, kernels, err = parse_profile_dirs(dirs, args.steps)
+        if err:
+            res.setdefault("error", err)
+        res["calibration"] = calib
+        res["kernels"] = kernels
+    except Exception as e:  # a malformed profiler output must not lose the bench line
+        res["error"] = f"parsing the rocprofv3 output failed: {type(e).__name__}: {e}"
+    if not keep:
+        shutil.rmtree(base, ignore_errors=True)
+    else:
+        res["dir"] = base
+    return res
 
 
 def copy_rate(dev, stream, nbytes=1 << 30, reps=10):
@@ -390,27 +616,19 @@ def copy_rate(dev, stream, nbytes=1 << 30, reps=10):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def bench_split(dev, name, steps, warmup):
+def bench_split(dev, name, steps, warmup, settle_ms):
     """A workload whose channels alone do not fill the GPU, so the library
     splits the sequence into segments and composes their aggregates (an
     aggregate launch, then the main launch): c1 (batch 8, D 1536, L 2048,
     fp32) or c2 (batch 1, D 2048, L 65536, bf16), N 16, timed like the main
-    step.  Parity for these is tested, not benchmarked elsewhere."""
+    step."""
     import torch
     import selective_state_space_28_amd as ssm
     import synth
     cfg = synth.SCAN_CONFIGS[name]
     inp = synth.make_scan_inputs(cfg)
-
-    def dev_t(a, dt):
-        if a is None:
-            return None
-        if dt == "bf16" and a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
-
-    u, delta, B, C, z = (dev_t(inp.get(k), cfg.dtype) for k in ("u", "delta", "B", "C", "z"))
-    A, D, bias = (dev_t(inp.get(k), "f32") for k in ("A", "D", "delta_bias"))
+    u, delta, B, C, z = (_to_dev(inp.get(k), cfg.dtype, dev) for k in ("u", "delta", "B", "C", "z"))
+    A, D, bias = (_to_dev(inp.get(k), "f32", dev) for k in ("A", "D", "delta_bias"))
     y = torch.empty_like(u)
     ws = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate, cfg.seqlen,
                                                             u.dtype)), dtype=torch.uint8, device=dev)
@@ -421,14 +639,8 @@ def bench_split(dev, name, steps, warmup):
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for s, e in ev:
-        s.record(stream)
-        step()
-        e.record(stream)
-    torch.cuda.synchronize(dev)
-    ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    settle(step, dev, settle_ms)
+    ms, _ = timed(step, dev, stream, steps)
     elements = cfg.batch * cfg.dim * cfg.seqlen
     ops = elements * cfg.dstate * OPS_PER_ELEMENT_STATE
     tops = ops / (ms * 1e-3) / 1e12
@@ -472,7 +684,7 @@ def bench_decode(dev, steps):
             ssm.ssm_state_update(st, t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias, out=ys[s])
 
     run()  # warm-up (the state keeps evolving; the work per step is the same)
-    torch.cuda.synchronize(dev)
+    settle(run, dev, 300.0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     run()
@@ -510,7 +722,7 @@ def bench_decode(dev, steps):
                                  "in-place read-modify-write)"}}
 
 
-def bench_ssd(dev, steps, warmup):
+def bench_ssd(dev, steps, warmup, settle_ms):
     """The SSD (scalar A per head) workload: the 2.8B token grid (batch 16,
     L 2048, 5120 channels) as 80 heads of 64 with 128 states, bf16."""
     import torch
@@ -538,15 +750,8 @@ def bench_ssd(dev, steps, warmup):
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for s_, e_ in ev:
-        s_.record(stream)
-        step()
-        e_.record(stream)
-    torch.cuda.synchronize(dev)
-    ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev]))
+    settle(step, dev, settle_ms)
+    ms, _ = timed(step, dev, stream, steps)
     nbytes = ssd_bytes(cfg)
     flops = ssd_flops(cfg)
     gbps = nbytes / (ms * 1e-3) / 1e9
@@ -569,14 +774,33 @@ def bench_ssd(dev, steps, warmup):
             "unit": "elements/s", "roofline": roof}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, inp, min_core_seconds=12.0):
     """The fp64 oracle as it stands, timed on this host over a bounded sample
     of the same workload: whole batch rows (all channels, whole sequences),
     four at a time, until about `min_core_seconds` of CPU time (threads x
-    wall) is spent or the whole batch is done."""
+    wall) is spent or the whole batch is done.  Threads: every CPU this
+    process may run on, capped by OMP_NUM_THREADS when that is set (on a
+    shared GPU host it states the CPU share of one GPU)."""
     import oracle
     import synth
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(os.cpu_count() or 1, 16)
+    host = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = host
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = max(1, min(usable, omp) if omp > 0 else usable)
     sec, nb, chunk = 0.0, 0, 4
     while nb < cfg.batch and sec * threads < min_core_seconds:
         sl = slice(nb, min(nb + chunk, cfg.batch))
@@ -589,6 +813,8 @@ def cpu_baseline(cfg, inp, min_core_seconds=12.0):
         del w
     el = nb * cfg.dim * cfg.seqlen
     return {"value": el / sec, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "host_cpus": host, "usable_cpus": usable, "omp_num_threads": omp or None,
+            "cpu_model": _cpu_model(),
             "sample": f"batch rows 0..{nb - 1} of the same workload ({nb}x{cfg.dim}x{cfg.seqlen} "
                       f"elements, N {cfg.dstate}), fp64, {threads} threads, {sec:.1f} s wall, "
                       f"{sec * threads:.0f} core-s"}
