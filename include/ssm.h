@@ -96,7 +96,8 @@ typedef enum {
   SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query's answer   */
   SSM_ERR_HIP = -6,       /* the HIP runtime reported an error at launch         */
   SSM_ERR_ALIAS = -7,     /* a buffer the call writes overlaps another of its buffers */
-  SSM_ERR_FLAGS = -8      /* flags holds a bit that is not an ssm_flag_t value   */
+  SSM_ERR_FLAGS = -8,     /* flags holds a bit that is not an ssm_flag_t value   */
+  SSM_ERR_SCRATCH = -9    /* ssm_scan_fwd_noalloc: needs more than its static scratch */
 } ssm_status_t;
 
 /* Bits of the `flags` argument (0 and 1 keep the meaning of the plain
@@ -144,6 +145,37 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  const float* delta_bias, int flags, const float* h0, void* y,
                  float* last_state, int batch, int dim, int dstate, int64_t seqlen,
                  int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the static per-device scratch of ssm_scan_fwd_noalloc. */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * ssm_scan_fwd_noalloc -- ssm_scan_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Instead of a caller's workspace it uses a static
+ * device array of the library, SSM_NOALLOC_SCRATCH_BYTES on each device the
+ * library runs on, held from the library's load on that device until the
+ * process ends.  The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first use on a device looks up the
+ * array's device address once (hipGetSymbolAddress).  The caller passes every
+ * input and output.
+ *
+ *   Arguments, layouts, results and errors as ssm_scan_fwd, without the
+ *   workspace arguments.
+ *   Problems whose ssm_scan_fwd_workspace_bytes(...) exceeds
+ *   SSM_NOALLOC_SCRATCH_BYTES return SSM_ERR_SCRATCH before any HIP call
+ *   (the 2.8B-shaped layer, batch 16, D 5120, N 16, L 2048 bf16, needs 2 MiB).
+ *   Every call on one device shares that device's scratch, which keeps the
+ *   last call's contents (no part of it needs to be zero on entry).  Calls
+ *   that can run at the same time on one device -- on different streams, or
+ *   from host threads whose streams run concurrently -- race on it; the
+ *   caller must order them (one stream, or events).
+ */
+int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D_skip, const void* z,
+                         const float* delta_bias, int flags, const float* h0, void* y,
+                         float* last_state, int batch, int dim, int dstate, int64_t seqlen,
+                         int dtype, void* stream);
 
 /*
  * ssm_state_update -- one decode step for a single new token per sequence:

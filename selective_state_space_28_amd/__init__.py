@@ -19,11 +19,12 @@ from __future__ import annotations
 
 from ._lib import SSM_BF16, SSM_F32, SsmError, header_functions, load, status_string  # noqa: F401
 from .ops import (ssm_conv_scan_fwd, ssm_conv_state_update, ssm_scan_bwd,  # noqa: F401
-                  ssm_scan_bwd_workspace_bytes, ssm_scan_fwd, ssm_scan_fwd_workspace_bytes,
+                  ssm_scan_bwd_workspace_bytes, ssm_scan_fwd, ssm_scan_fwd_noalloc,
+                  ssm_scan_fwd_workspace_bytes,
                   ssm_ssd_scan_fwd, ssm_ssd_scan_fwd_workspace_bytes, ssm_state_update,
                   ssm_status_string)
 
-__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_workspace_bytes", "ssm_state_update",
+__all__ = ["ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_workspace_bytes", "ssm_state_update",
            "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_scan_bwd",
            "ssm_scan_bwd_workspace_bytes", "ssm_ssd_scan_fwd", "ssm_ssd_scan_fwd_workspace_bytes",
            "ssm_status_string", "SsmError", "load"]

@@ -61,6 +61,10 @@ def load():
     lib.ssm_ssd_scan_fwd_workspace_bytes.argtypes = [i32, i32, i64, i32]
     lib.ssm_ssd_scan_fwd_workspace_bytes.restype = sz
     lib.ssm_ssd_scan_fwd.restype = i32
+    if hasattr(lib, "ssm_scan_fwd_noalloc"):
+        lib.ssm_scan_fwd_noalloc.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp,
+                                             i32, i32, i32, i64, i32, vp]
+        lib.ssm_scan_fwd_noalloc.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -202,6 +202,31 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
 
 namespace {
 
+// ---- scratch of the allocation-free entry point ------------------------------
+// ssm_scan_fwd_noalloc keeps its workspace (the B, C records and the segment
+// aggregates) in this file-scope device array instead of a caller's buffer.
+// Each device holds its own copy, at its own address, from the time the
+// library's code object is loaded on it until the process ends.  In host code
+// `scratch` only stands in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
+constexpr int kStatusScratch = SSM_ERR_SCRATCH;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> ptrs[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  ptrs[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 // Operands of the convolution prologue (all null / zero: no convolution).
 struct ConvIn {
   const float* w;
@@ -221,7 +246,7 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
               const float* D_skip, const void* z, const float* delta_bias, int flags,
               const float* h0, void* y, float* last_state, int batch, int dim, int dstate,
               int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-              const ConvIn* cv) {
+              const ConvIn* cv, bool use_scratch = false) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return SSM_ERR_SHAPE;
@@ -274,6 +299,13 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
   const int64_t pack_blocks = (int64_t)batch * ((seqlen + 255) / 256);
   if (blocks > INT_MAX || pack_blocks > INT_MAX) return SSM_ERR_SHAPE;
   const WsLayout wl = workspace_layout(batch, dim, dstate, seqlen, dtype, sp);
+  if (use_scratch) {
+    // every argument is valid by now: the first HIP call is the symbol lookup
+    if (wl.total > kNoAllocScratchBytes) return kStatusScratch;
+    workspace = noalloc_scratch();
+    if (workspace == nullptr) return SSM_ERR_HIP;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (workspace == nullptr || workspace_bytes < wl.total) return SSM_ERR_WORKSPACE;
   {
     const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
@@ -405,6 +437,14 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  void* stream) {
   return scan_impl(u, delta, A, B, C, D_skip, z, delta_bias, flags, h0, y, last_state, batch, dim,
                    dstate, seqlen, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D_skip, const void* z, const float* delta_bias,
+                         int flags, const float* h0, void* y, float* last_state, int batch, int dim,
+                         int dstate, int64_t seqlen, int dtype, void* stream) {
+  return scan_impl(u, delta, A, B, C, D_skip, z, delta_bias, flags, h0, y, last_state, batch, dim,
+                   dstate, seqlen, dtype, nullptr, 0, stream, nullptr, true);
 }
 
 int ssm_conv_scan_fwd(const void* x, const float* conv_w, const float* conv_b, int conv_width,
@@ -690,6 +730,9 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_HIP: return "SSM_ERR_HIP: the HIP runtime reported a launch error";
     case SSM_ERR_ALIAS: return "SSM_ERR_ALIAS: a buffer the call writes overlaps another buffer of the call";
     case SSM_ERR_FLAGS: return "SSM_ERR_FLAGS: flags holds an unknown bit";
+    case kStatusScratch:
+      return "SSM_ERR_SCRATCH: the problem needs more workspace than the 16 MiB static scratch of "
+             "ssm_scan_fwd_noalloc holds (ssm_scan_fwd_workspace_bytes gives the need)";
     default: return "unknown ssm status";
   }
 }

@@ -124,6 +124,39 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
                  out, workspace, None)
 
 
+def ssm_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                         h0=None, *, out, last_state=None, bbar="euler"):
+    """ssm_scan_fwd without any allocation: the library's static scratch
+    stands in for the workspace, and the caller passes the outputs (out, and
+    last_state if wanted).  Nothing here allocates device memory either."""
+    lib = load()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("libssm runs on the GPU: tensors must be on a cuda device")
+    dt = u.dtype
+    code = _code(u)
+    batch, dim, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    _check("u", u, (batch, dim, L), dt, dev)
+    _check("delta", delta, (batch, dim, L), dt, dev)
+    _check("A", A, (dim, N), torch.float32, dev)
+    _check("B", B, (batch, N, L), dt, dev)
+    _check("C", C, (batch, N, L), dt, dev)
+    _check("D", D, (dim,), torch.float32, dev, required=False)
+    _check("z", z, (batch, dim, L), dt, dev, required=False)
+    _check("delta_bias", delta_bias, (dim,), torch.float32, dev, required=False)
+    _check("h0", h0, (batch, dim, N), torch.float32, dev, required=False)
+    _check("out", out, (batch, dim, L), dt, dev)
+    _check("last_state", last_state, (batch, dim, N), torch.float32, dev, required=False)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                  _ptr(delta_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(out),
+                                  _ptr(last_state), batch, dim, N, L, code, stream)
+    if rc != 0:
+        raise SsmError(rc, "ssm_scan_fwd_noalloc")
+    return out
+
+
 def ssm_conv_scan_fwd(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
                       delta_softplus=True, h0=None, *, conv_state_in=None, return_conv_state=False,
                       bbar="euler", return_last_state=False, out=None, workspace=None):

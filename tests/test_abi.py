@@ -1,13 +1,14 @@
 """The C ABI without a GPU: libssm.so loads, exports every function that
 include/ssm.h declares, and rejects bad arguments before any HIP call."""
 import ctypes
+import os
 
 import pytest
 
 import selective_state_space_28_amd as ssm
 from selective_state_space_28_amd._lib import header_functions, load
 
-OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS, FLAGS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS, FLAGS, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 P = 0x10000  # a 256-byte aligned fake device address, never dereferenced
 R = 0x1000000  # 16 MiB: distinct buffers of a call sit R apart, so none overlaps
 
@@ -22,14 +23,14 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
                           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_scan_bwd_workspace_bytes",
                           "ssm_scan_bwd", "ssm_ssd_scan_fwd", "ssm_ssd_scan_fwd_workspace_bytes",
-                          "ssm_status_string"}
+                          "ssm_scan_fwd_noalloc", "ssm_status_string"}
     lib = ctypes.CDLL(load()._name)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings():
-    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS, FLAGS):
+    for code in (OK, NULL, SHAPE, DTYPE, ALIGN, WS, HIP, ALIAS, FLAGS, SCRATCH):
         s = ssm.ssm_status_string(code)
         assert s.startswith("SSM_")
     assert "unknown" in ssm.ssm_status_string(42)
@@ -262,3 +263,36 @@ def test_ssd_workspace_query():
 def test_ssd_empty_needs_no_gpu():
     assert _ssd(batch=0) == OK
     assert _ssd(H=0, x=None) == OK
+
+
+def _noalloc(**kw):
+    a = dict(u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=1, h0=None, y=at(1),
+             last=None, batch=1, dim=64, dstate=16, L=2048, dtype=1, stream=None)
+    a.update(kw)
+    return load().ssm_scan_fwd_noalloc(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                       a["bias"], a["sp"], a["h0"], a["y"], a["last"], a["batch"],
+                                       a["dim"], a["dstate"], a["L"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), DTYPE), (dict(dstate=3), SHAPE), (dict(u=None), NULL), (dict(y=P + 1), ALIGN),
+    (dict(y=P), ALIAS), (dict(sp=4), FLAGS), (dict(batch=0), OK),
+    # B, C records alone of batch 1 x 2^20 steps x 32 values of bf16: 64 MiB > 16 MiB
+    (dict(L=1 << 20, y=at(8)), SCRATCH),
+])
+def test_noalloc_validation_without_gpu(kw, code):
+    """Everything the allocation-free scan checks, its scratch limit included,
+    is checked before its first HIP call."""
+    assert _noalloc(**kw) == code
+
+
+def test_noalloc_limit_matches_the_header():
+    import re
+    from selective_state_space_28_amd.build import INCLUDE
+    with open(os.path.join(INCLUDE, "ssm.h")) as f:
+        m = re.search(r"#define SSM_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", f.read())
+    assert m is not None
+    limit = int(m.group(1)) << int(m.group(2))
+    q = load().ssm_scan_fwd_workspace_bytes
+    assert q(16, 5120, 16, 2048, 1) <= limit          # the 2.8B-shaped layer fits
+    assert q(1, 64, 16, 1 << 20, 1) > limit
