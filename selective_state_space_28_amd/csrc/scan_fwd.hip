@@ -260,6 +260,19 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 
   const T* bcw = bc + ((int64_t)b * G + g) * L * R;  // wave-uniform records
 
+  // Whole load blocks go through buffer descriptors over the workgroup's rows
+  // of u, delta, z and y: a lane's offset (channel cc, step r0) is fixed and
+  // the block's step offset is a scalar, so no lane holds 64-bit addresses.
+  // Rows past dim lie beyond the extent: they read 0 and their stores drop.
+  // (vec is set only when the rows of 64 channels span < 2^31 bytes.)
+  const int64_t grow = (int64_t)b * p.dim + (int64_t)cg * 64;
+  const int64_t gbytes = (int64_t)min(64, p.dim - cg * 64) * L * (int64_t)sizeof(T);
+  const Buf bu = make_buf(u + grow * L, vec ? gbytes : 0);
+  const Buf bd = make_buf(delta + grow * L, vec ? gbytes : 0);
+  const Buf bz = make_buf(has_z ? z + grow * L : u, (vec && has_z) ? gbytes : 0);
+  const Buf by = make_buf(READOUT ? y + grow * L : u, (vec && READOUT) ? gbytes : 0);
+  const uint32_t voff = vec ? (uint32_t)(((int64_t)cc * L + r0) * (int64_t)sizeof(T)) : 0u;
+
   // raw words of this thread's runs in the KT tiles of the current load block,
   // and the packed y of those runs, stored together at the end of the block
   // so each 128-byte row line is written whole
@@ -268,13 +281,13 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   auto fetch_block = [&](int64_t tb) {
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
-      const int64_t off = rowcc * L + tb + j * TL + r0;
-      load_words<W>(u + off, pu[j]);
-      load_words<W>(delta + off, pd[j]);
-      if (has_z) load_words<W>(z + off, pz[j]);
+      const uint32_t soff = (uint32_t)((tb + j * TL) * (int64_t)sizeof(T));
+      buf_load_words<W>(bu, voff, soff, pu[j]);
+      buf_load_words<W>(bd, voff, soff, pd[j]);
+      if (has_z) buf_load_words<W>(bz, voff, soff, pz[j]);
     }
   };
-  if (ccvalid && block_full(seg_begin)) fetch_block(seg_begin);
+  if (block_full(seg_begin)) fetch_block(seg_begin);
 
   double sumdt = 0.0;
 
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 
       // ---- this tile's u, delta (z) -> Delta, Delta*u in LDS ------------------
       float uu[E], dd[E], zz[E];
-      if (fast && ccvalid) {
+      if (fast) {
         words_to_floats<T, E>(pu[j], uu);
         words_to_floats<T, E>(pd[j], dd);
         if (has_z) words_to_floats<T, E>(pz[j], zz);
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
       // ---- after the block's last tile is staged, issue the next block ------
       if (j == KT - 1) {
         const int64_t tn = tb + KT * TL;
-        if (ccvalid && tn < seg_end && block_full(tn)) fetch_block(tn);
+        if (tn < seg_end && block_full(tn)) fetch_block(tn);
       }
 
       // ---- checkpoint: the state entering this tile, (batch, tile, N, dim) ----
@@ -454,7 +467,8 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
             pack_floats<T, E>(yv, py[j]);
             if (j == KT - 1) {
 #pragma unroll
-              for (int jj = 0; jj < KT; ++jj) store_words<W>(y + rowcc * L + tb + jj * TL + r0, py[jj]);
+              for (int jj = 0; jj < KT; ++jj)
+                buf_store_words<W>(by, voff, (uint32_t)((tb + jj * TL) * (int64_t)sizeof(T)), py[jj]);
             }
           } else {
             const int64_t off = rowcc * L + t0 + r0;

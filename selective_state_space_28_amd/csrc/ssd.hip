@@ -145,18 +145,10 @@ __device__ __forceinline__ void load_run8(const T* __restrict__ p, bool vec, int
   }
 }
 
-// Buffer accesses: a descriptor (base and byte extent of a per-block region,
-// in scalar registers), a 32-bit per-lane offset that stays fixed from chunk
-// to chunk and a scalar offset that moves with the chunk -- no per-lane
-// 64-bit address arithmetic.  Extents are below 2^31 bytes (checked on the
-// host).
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-struct Buf {
-  __amdgpu_buffer_rsrc_t r;
-};
-__device__ __forceinline__ Buf make_buf(const void* base, int64_t bytes) {
-  return Buf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000)};
-}
+// Buffer accesses (Buf, make_buf in ssm_math.hpp): a descriptor per block
+// region, a 32-bit per-lane offset that stays fixed from chunk to chunk and a
+// scalar offset that moves with the chunk.  Extents are below 2^31 bytes
+// (checked on the host).
 
 // A run of 8 elements of T (16 or 32 bytes) at voff + soff.
 template <typename T>
@@ -174,7 +166,6 @@ template <typename T>
 __device__ __forceinline__ void buf_load_run4(const Buf& b, uint32_t voff, uint32_t soff,
                                               uint32_t (&w)[kRunWords<T> / 2]) {
   if constexpr (sizeof(T) == 2) {
-    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(b.r, voff, soff, 0);
     w[0] = v.x; w[1] = v.y;
   } else {

@@ -146,6 +146,59 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// ---- buffer accesses ------------------------------------------------------------
+// A buffer descriptor (base address and byte extent of a region, held in
+// scalar registers) lets a lane address the region with a 32-bit offset that
+// stays fixed while a scalar offset moves along the sequence: no per-lane
+// 64-bit address arithmetic and two fewer VGPRs per stream.  Loads past the
+// extent read 0 and stores past it are dropped.  Extents must be below 2^31
+// bytes (the callers check it on the host).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ Buf make_buf(const void* base, int64_t bytes) {
+  return Buf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000)};
+}
+
+// W 32-bit words at voff + soff (W = 2: one 8-byte access; W = 4k: 16-byte ones).
+template <int W>
+__device__ __forceinline__ void buf_load_words(const Buf& b, uint32_t voff, uint32_t soff, uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(b.r, voff + 16 * i, soff, 0);
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (W == 2) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(b.r, voff, soff, 0);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(b.r, voff + 4 * i, soff, 0);
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void buf_store_words(const Buf& b, uint32_t voff, uint32_t soff, const uint32_t (&w)[W]) {
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      u32x4_t v;
+      v.x = w[4 * i]; v.y = w[4 * i + 1]; v.z = w[4 * i + 2]; v.w = w[4 * i + 3];
+      __builtin_amdgcn_raw_buffer_store_b128(v, b.r, voff + 16 * i, soff, 0);
+    }
+  } else if constexpr (W == 2) {
+    u32x2_t v;
+    v.x = w[0]; v.y = w[1];
+    __builtin_amdgcn_raw_buffer_store_b64(v, b.r, voff, soff, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; ++i) __builtin_amdgcn_raw_buffer_store_b32(w[i], b.r, voff + 4 * i, soff, 0);
+  }
+}
+
 // ---- vectorised runs of E consecutive elements ---------------------------------
 // A run of E elements of T is W = E*sizeof(T)/4 32-bit words.  Callers pass
 // pointers aligned to the run size (16 bytes when W is a multiple of 4).
