@@ -179,6 +179,13 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
 
   __shared__ float2 s_ddu[TL][LDW];                           // (Delta, Delta*u), ZOH: (Delta, u)
   __shared__ float s_y[READOUT ? G : 1][READOUT ? TL : 1][LDW];  // partial readouts
+  // convolution taps (right-aligned in 4, tap 3 on the current input) and bias
+  // of each channel of the group: read from LDS at each tile's staging rather
+  // than held in registers through the whole sequence
+  __shared__ float4 s_cw[CONV ? 64 : 1];
+  __shared__ float s_cb[CONV ? 64 : 1];
+  // the last 3 inputs of each channel's previous tile (convolution halo)
+  __shared__ float s_tail[CONV ? kMaxConvWidth - 1 : 1][CONV ? 64 : 1];
 
   // ---- block -> (batch row, channel group, segment) --------------------------
   // Consecutive block ids go to different XCDs; regroup so that the blocks an
@@ -199,8 +206,10 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   const bool dvalid = d < p.dim;
   const int64_t row = (int64_t)b * p.dim + d;
 
-  const int64_t seg_begin = (int64_t)seg * p.seglen;
-  const int64_t seg_end = seg_begin + p.seglen < L ? seg_begin + p.seglen : L;
+  // step positions fit in 32 bits (the host rejects longer sequences), so the
+  // uniform tile bookkeeping stays in scalar registers and scalar compares
+  const int seg_begin = seg * (int)p.seglen;
+  const int seg_end = (int)min((int64_t)seg_begin + p.seglen, L);
 
   // ---- per-lane parameters and initial state ---------------------------------
   float A2[NS], h[NS], rA[NS];
@@ -238,24 +247,32 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   const bool has_z = READOUT && (z != nullptr);
   const bool vec = p.vec != 0;
 
-  // convolution taps of channel cc, right-aligned in 4 (tap 3 on the current
-  // input), its bias, and the last 3 inputs of this thread's previous run
-  float cw[kMaxConvWidth] = {}, cbias = 0.0f, tailp[kMaxConvWidth - 1] = {};
   if constexpr (CONV) {
     const int K = p.conv_k;
-    if (ccvalid) {
+    if (tid < 64) {
+      const int dw = cg * 64 + tid;
+      float w4[kMaxConvWidth] = {};
+      if (dw < p.dim) {
 #pragma unroll
-      for (int j = 0; j < kMaxConvWidth; ++j) {
-        const int k = j - (kMaxConvWidth - K);
-        if (k >= 0) cw[j] = cv.w[(int64_t)dcc * K + k];
+        for (int j = 0; j < kMaxConvWidth; ++j) {
+          const int k = j - (kMaxConvWidth - K);
+          if (k >= 0) w4[j] = cv.w[(int64_t)dw * K + k];
+        }
       }
-      cbias = cv.b != nullptr ? cv.b[dcc] : 0.0f;
-      // before the segment's first tile, every thread's "previous run" ends
-      // at the segment start
+      s_cw[tid] = make_float4(w4[0], w4[1], w4[2], w4[3]);
+      s_cb[tid] = (dw < p.dim && cv.b != nullptr) ? cv.b[dw] : 0.0f;
+    }
+    if (tid < 64) {
+      // before the segment's first tile, the "previous tile" ends at the
+      // segment start
+      const int dw = cg * 64 + tid;
+      const int64_t roww = (int64_t)b * p.dim + (dw < p.dim ? dw : 0);
 #pragma unroll
       for (int i = 0; i < kMaxConvWidth - 1; ++i)
-        tailp[i] = conv_input<T>(u, cv.state_in, rowcc, L, seg_begin - (kMaxConvWidth - 1) + i, K);
+        s_tail[i][tid] = dw < p.dim ? conv_input<T>(u, cv.state_in, roww, L, seg_begin - (kMaxConvWidth - 1) + i, K)
+                                    : 0.0f;
     }
+    __syncthreads();
   }
 
   const T* bcw = bc + ((int64_t)b * G + g) * L * R;  // wave-uniform records
@@ -277,11 +294,11 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   // and the packed y of those runs, stored together at the end of the block
   // so each 128-byte row line is written whole
   uint32_t pu[KT][W], pd[KT][W], pz[KT][W], py[KT][W];
-  auto block_full = [&](int64_t tb) { return vec && tb + KT * TL <= seg_end; };
-  auto fetch_block = [&](int64_t tb) {
+  auto block_full = [&](int tb) { return vec && tb + KT * TL <= seg_end; };
+  auto fetch_block = [&](int tb) {
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
-      const uint32_t soff = (uint32_t)((tb + j * TL) * (int64_t)sizeof(T));
+      const uint32_t soff = (uint32_t)(tb + j * TL) * (uint32_t)sizeof(T);
       buf_load_words<W>(bu, voff, soff, pu[j]);
       buf_load_words<W>(bd, voff, soff, pd[j]);
       if (has_z) buf_load_words<W>(bz, voff, soff, pz[j]);
@@ -297,189 +314,208 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   // the CUs, so blockIdx / ncu is a block's age rank on its CU; rotating a
   // raised wave priority over the ranks keeps them progressing together.
   const int prio_rank = (int)(blockIdx.x / (unsigned)p.ncu) % 5;
-  const int64_t nblocks = (seg_end - seg_begin + KT * TL - 1) / (KT * TL);
-  const int64_t epoch_len = p.prio_epochs > 0 ? (nblocks + p.prio_epochs - 1) / p.prio_epochs : 0;
-  int64_t blk = 0;
+  const int nblocks = (seg_end - seg_begin + KT * TL - 1) / (KT * TL);
+  const int epoch_len = p.prio_epochs > 0 ? (nblocks + p.prio_epochs - 1) / p.prio_epochs : 0;
 
-  for (int64_t tb = seg_begin; tb < seg_end; tb += KT * TL, ++blk) {
-    const bool fast = block_full(tb);
+  // One tile of TL steps.  FAST: a whole tile of a whole load block, its runs
+  // already in registers (pu, pd, pz) and its y packed into py; otherwise a
+  // ragged or unaligned tile with element loads and guards.
+  auto tile = [&](auto fast_c, int j, int tb, int t0, int tvalid) {
+    constexpr bool FAST = decltype(fast_c)::value;
+    // ---- this tile's u, delta (z) -> Delta, Delta*u in LDS --------------------
+    float uu[E], dd[E], zz[E];
+    if constexpr (FAST) {
+      words_to_floats<T, E>(pu[j], uu);
+      words_to_floats<T, E>(pd[j], dd);
+      if (has_z) words_to_floats<T, E>(pz[j], zz);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool ok = ccvalid && r0 + e < tvalid;
+        const int64_t off = rowcc * L + t0 + r0 + e;
+        uu[e] = ok ? Elem<T>::load(u + off) : 0.0f;
+        dd[e] = ok ? Elem<T>::load(delta + off) : 0.0f;
+        zz[e] = (ok && has_z) ? Elem<T>::load(z + off) : 0.0f;
+      }
+    }
+    float xlast[kMaxConvWidth - 1] = {};  // this run's last 3 inputs (convolution)
+    if constexpr (CONV) {
+#pragma unroll
+      for (int i = 0; i < kMaxConvWidth - 1; ++i) xlast[i] = uu[E - (kMaxConvWidth - 1) + i];
+      // the 3 inputs before this run: from the run of the lane before (same
+      // tile, a lane shuffle), or for a channel's first run from the last 3
+      // inputs of the previous tile, which that tile's last run left in LDS
+      // (written before two barriers, read after them)
+      const int lw = tid & 63;
+      float xw[E + kMaxConvWidth - 1];
+#pragma unroll
+      for (int i = 0; i < kMaxConvWidth - 1; ++i) {
+        const float left = __shfl(uu[E - (kMaxConvWidth - 1) + i], chunk > 0 ? lw - 1 : lw);
+        xw[i] = chunk > 0 ? left : s_tail[i][cc];
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) xw[kMaxConvWidth - 1 + e] = uu[e];
+      const float4 w4 = s_cw[cc];
+      const float cw[kMaxConvWidth] = {w4.x, w4.y, w4.z, w4.w};
+      const float cbias = s_cb[cc];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float sacc = cbias;
+#pragma unroll
+        for (int q = 0; q < kMaxConvWidth; ++q) sacc = __builtin_fmaf(cw[q], xw[e + q], sacc);
+        uu[e] = silu_f32(sacc);
+      }
+    }
+    // Entries of channels past dim, or of steps past the tile end, hold
+    // harmless values (u = 0 there, so Delta*u = 0): those steps are never
+    // run and those lanes never store.
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float x = dd[e] + bias_cc;
+      const float dt = p.softplus ? softplus_f32(x) : x;
+      s_ddu[r0 + e][cc] = make_float2(dt, ZOH ? uu[e] : dt * uu[e]);
+    }
+    __syncthreads();
+    if constexpr (CONV) {
+      // this tile's last 3 inputs for the next tile (the reads above of the
+      // previous tile's are ordered before this by the barrier)
+      if (chunk == G - 1) {
+#pragma unroll
+        for (int i = 0; i < kMaxConvWidth - 1; ++i) s_tail[i][cc] = xlast[i];
+      }
+    }
+
+    // ---- after the block's last tile is staged, issue the next block --------
+    if (FAST && j == KT - 1) {
+      const int tn = tb + KT * TL;
+      if (block_full(tn)) fetch_block(tn);
+    }
+
+    // ---- checkpoint: the state entering this tile, (batch, tile, N, dim) ------
+    if constexpr (CKPT) {
+      if (dvalid) {
+        const int64_t ntiles = (L + TL - 1) / TL;
+        float* cp = ws_ckpt + (((int64_t)b * ntiles + t0 / TL) * N + g * NS) * p.dim + d;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) cp[(int64_t)k * p.dim] = h[k];
+      }
+    }
+
+    // ---- the recurrence: TL steps x NS states per lane -----------------------
+    const T* bct = bcw + (int64_t)t0 * R;
+    if (FAST || tvalid == TL) {
+      // chunks of CH steps; the next chunk's LDS and scalar loads are issued
+      // before the current chunk's arithmetic so their latency is covered
+      float2 vc[CH], vn[CH];
+      float rc[CH][R], rn[CH][R];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        vc[i] = s_ddu[i][lane];
+#pragma unroll
+        for (int q = 0; q < R; ++q) rc[i][q] = rec_value<T>(bct + i * R, q);
+      }
+#pragma unroll
+      for (int c = 0; c < TL / CH; ++c) {
+        if (c + 1 < TL / CH) {
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            vn[i] = s_ddu[(c + 1) * CH + i][lane];
+#pragma unroll
+            for (int q = 0; q < R; ++q) rn[i][q] = rec_value<T>(bct + ((c + 1) * CH + i) * R, q);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < NS; ++k) {
+            const float x2 = vc[i].x * A2[k];
+            const float a = exp2_hw(x2);
+            h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, vc[i].x, vc[i].y * rc[i][k], rA[k]));
+            acc = __builtin_fmaf(rc[i][NS + k], h[k], acc);
+          }
+          if constexpr (READOUT) {
+            s_y[g][c * CH + i][lane] = acc;
+          } else if constexpr (AGG) {
+            if (g == 0) sumdt += (double)vc[i].x;
+          }
+        }
+        if (c + 1 < TL / CH) {
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            vc[i] = vn[i];
+#pragma unroll
+            for (int q = 0; q < R; ++q) rc[i][q] = rn[i][q];
+          }
+        }
+      }
+    } else {
+      for (int t = 0; t < tvalid; ++t) {
+        const float2 v = s_ddu[t][lane];
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+          const float x2 = v.x * A2[k];
+          const float a = exp2_hw(x2);
+          h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, v.x, v.y * rec_value<T>(bct + t * R, k), rA[k]));
+          acc = __builtin_fmaf(rec_value<T>(bct + t * R, NS + k), h[k], acc);
+        }
+        if constexpr (READOUT) {
+          s_y[g][t][lane] = acc;
+        } else if constexpr (AGG) {
+          if (g == 0) sumdt += (double)v.x;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- readout: sum the G partials, D-skip, gate, store y --------------------
+    if constexpr (READOUT) {
+      float yv[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float sum = s_y[0][r0 + e][cc];
+#pragma unroll
+        for (int gg = 1; gg < G; ++gg) sum += s_y[gg][r0 + e][cc];
+        sum = __builtin_fmaf(D_cc, uu[e], sum);
+        if (has_z) sum *= silu_f32(zz[e]);
+        yv[e] = sum;
+      }
+      if constexpr (FAST) {
+        // rows past dim are beyond the buffer's extent: their stores drop
+        pack_floats<T, E>(yv, py[j]);
+        if (j == KT - 1) {
+#pragma unroll
+          for (int jj = 0; jj < KT; ++jj)
+            buf_store_words<W>(by, voff, (uint32_t)(tb + jj * TL) * (uint32_t)sizeof(T), py[jj]);
+        }
+      } else if (ccvalid) {
+        const int64_t off = rowcc * L + t0 + r0;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (r0 + e < tvalid) Elem<T>::store(y + off + e, yv[e]);
+      }
+    }
+    // The next tile's LDS writes (s_ddu) are not read by this readout, and its
+    // s_y writes come after the next barrier, so no third barrier is needed.
+  };
+
+  int blk = 0;
+  for (int tb = seg_begin; tb < seg_end; tb += KT * TL, ++blk) {
     if (epoch_len > 0 && blk % epoch_len == 0) {
-      const int lvl = (int)((prio_rank + blk / epoch_len) % 5);
+      const int lvl = (prio_rank + blk / epoch_len) % 5;
       if (lvl <= 1) __builtin_amdgcn_s_setprio(0);
       else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
       else if (lvl == 3) __builtin_amdgcn_s_setprio(2);
       else __builtin_amdgcn_s_setprio(3);
     }
+    const bool fast = block_full(tb);
 #pragma unroll
     for (int j = 0; j < KT; ++j) {
-      const int64_t t0 = tb + j * TL;
+      const int t0 = tb + j * TL;
       if (t0 >= seg_end) break;
-      const int tvalid = (int)((seg_end - t0) < TL ? (seg_end - t0) : TL);
-
-      // ---- this tile's u, delta (z) -> Delta, Delta*u in LDS ------------------
-      float uu[E], dd[E], zz[E];
-      if (fast) {
-        words_to_floats<T, E>(pu[j], uu);
-        words_to_floats<T, E>(pd[j], dd);
-        if (has_z) words_to_floats<T, E>(pz[j], zz);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const bool ok = ccvalid && r0 + e < tvalid;
-          const int64_t off = rowcc * L + t0 + r0 + e;
-          uu[e] = ok ? Elem<T>::load(u + off) : 0.0f;
-          dd[e] = ok ? Elem<T>::load(delta + off) : 0.0f;
-          zz[e] = (ok && has_z) ? Elem<T>::load(z + off) : 0.0f;
-        }
-      }
-      if constexpr (CONV) {
-        // the 3 inputs before this run: from the run of the lane before (same
-        // tile), or for a channel's first run from its last run's lane in the
-        // previous tile
-        const int lw = tid & 63;
-        float xw[E + kMaxConvWidth - 1];
-#pragma unroll
-        for (int i = 0; i < kMaxConvWidth - 1; ++i) {
-          const float left = __shfl(uu[E - (kMaxConvWidth - 1) + i], chunk > 0 ? lw - 1 : lw);
-          const float prev = __shfl(tailp[i], chunk == 0 ? lw + G - 1 : lw);
-          xw[i] = chunk > 0 ? left : prev;
-          tailp[i] = uu[E - (kMaxConvWidth - 1) + i];
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) xw[kMaxConvWidth - 1 + e] = uu[e];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          float sacc = cbias;
-#pragma unroll
-          for (int j = 0; j < kMaxConvWidth; ++j) sacc = __builtin_fmaf(cw[j], xw[e + j], sacc);
-          uu[e] = silu_f32(sacc);
-        }
-      }
-      // Entries of channels past dim, or of steps past the tile end, hold
-      // harmless values (u = 0 there, so Delta*u = 0): those steps are never
-      // run and those lanes never store.
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float x = dd[e] + bias_cc;
-        const float dt = p.softplus ? softplus_f32(x) : x;
-        s_ddu[r0 + e][cc] = make_float2(dt, ZOH ? uu[e] : dt * uu[e]);
-      }
-      __syncthreads();
-
-      // ---- after the block's last tile is staged, issue the next block ------
-      if (j == KT - 1) {
-        const int64_t tn = tb + KT * TL;
-        if (tn < seg_end && block_full(tn)) fetch_block(tn);
-      }
-
-      // ---- checkpoint: the state entering this tile, (batch, tile, N, dim) ----
-      if constexpr (CKPT) {
-        if (dvalid) {
-          const int64_t ntiles = (L + TL - 1) / TL;
-          float* cp = ws_ckpt + (((int64_t)b * ntiles + t0 / TL) * N + g * NS) * p.dim + d;
-#pragma unroll
-          for (int k = 0; k < NS; ++k) cp[(int64_t)k * p.dim] = h[k];
-        }
-      }
-
-      // ---- the recurrence: TL steps x NS states per lane ---------------------
-      const T* bct = bcw + t0 * R;
-      if (tvalid == TL) {
-        // chunks of CH steps; the next chunk's LDS and scalar loads are issued
-        // before the current chunk's arithmetic so their latency is covered
-        float2 vc[CH], vn[CH];
-        float rc[CH][R], rn[CH][R];
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          vc[i] = s_ddu[i][lane];
-#pragma unroll
-          for (int q = 0; q < R; ++q) rc[i][q] = rec_value<T>(bct + i * R, q);
-        }
-#pragma unroll
-        for (int c = 0; c < TL / CH; ++c) {
-          if (c + 1 < TL / CH) {
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-              vn[i] = s_ddu[(c + 1) * CH + i][lane];
-#pragma unroll
-              for (int q = 0; q < R; ++q) rn[i][q] = rec_value<T>(bct + ((c + 1) * CH + i) * R, q);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < CH; ++i) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int k = 0; k < NS; ++k) {
-              const float x2 = vc[i].x * A2[k];
-              const float a = exp2_hw(x2);
-              h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, vc[i].x, vc[i].y * rc[i][k], rA[k]));
-              acc = __builtin_fmaf(rc[i][NS + k], h[k], acc);
-            }
-            if constexpr (READOUT) {
-              s_y[g][c * CH + i][lane] = acc;
-            } else if constexpr (AGG) {
-              if (g == 0) sumdt += (double)vc[i].x;
-            }
-          }
-          if (c + 1 < TL / CH) {
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-              vc[i] = vn[i];
-#pragma unroll
-              for (int q = 0; q < R; ++q) rc[i][q] = rn[i][q];
-            }
-          }
-        }
-      } else {
-        for (int t = 0; t < tvalid; ++t) {
-          const float2 v = s_ddu[t][lane];
-          float acc = 0.0f;
-#pragma unroll
-          for (int k = 0; k < NS; ++k) {
-            const float x2 = v.x * A2[k];
-            const float a = exp2_hw(x2);
-            h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, v.x, v.y * rec_value<T>(bct + t * R, k), rA[k]));
-            acc = __builtin_fmaf(rec_value<T>(bct + t * R, NS + k), h[k], acc);
-          }
-          if constexpr (READOUT) {
-            s_y[g][t][lane] = acc;
-          } else if constexpr (AGG) {
-            if (g == 0) sumdt += (double)v.x;
-          }
-        }
-      }
-      __syncthreads();
-
-      // ---- readout: sum the G partials, D-skip, gate, store y ------------------
-      if constexpr (READOUT) {
-        float yv[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          float s = s_y[0][r0 + e][cc];
-#pragma unroll
-          for (int gg = 1; gg < G; ++gg) s += s_y[gg][r0 + e][cc];
-          s = __builtin_fmaf(D_cc, uu[e], s);
-          if (has_z) s *= silu_f32(zz[e]);
-          yv[e] = s;
-        }
-        if (ccvalid) {
-          if (fast) {
-            pack_floats<T, E>(yv, py[j]);
-            if (j == KT - 1) {
-#pragma unroll
-              for (int jj = 0; jj < KT; ++jj)
-                buf_store_words<W>(by, voff, (uint32_t)((tb + jj * TL) * (int64_t)sizeof(T)), py[jj]);
-            }
-          } else {
-            const int64_t off = rowcc * L + t0 + r0;
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-              if (r0 + e < tvalid) Elem<T>::store(y + off + e, yv[e]);
-          }
-        }
-      }
-      // The next tile's LDS writes (s_ddu) are not read by this readout, and its
-      // s_y writes come after the next barrier, so no third barrier is needed.
+      if (fast) tile(BoolC<true>{}, j, tb, t0, TL);
+      else tile(BoolC<false>{}, j, tb, t0, min(TL, seg_end - t0));
     }
   }
 

@@ -189,8 +189,11 @@ bool group_rows_fit(int dim, int64_t seqlen, size_t es) {
   return (long double)rows * (long double)seqlen * (long double)es < (long double)INT32_MAX;
 }
 
+// The scan kernels keep step positions in 32 bits.
+constexpr int64_t kMaxSeqlen = INT32_MAX - 4096;
+
 bool shapes_fit(int batch, int dim, int64_t seqlen) {
-  if (batch < 0 || dim < 0 || seqlen < 0) return false;
+  if (batch < 0 || dim < 0 || seqlen < 0 || seqlen > kMaxSeqlen) return false;
   const long double total = (long double)batch * (long double)dim * (long double)(seqlen > 0 ? seqlen : 1);
   return total < (long double)(INT64_C(1) << 60);
 }
