@@ -113,11 +113,22 @@ __device__ __forceinline__ void load_run(const T* __restrict__ base, int64_t off
   }
 }
 
+// Per-element gradients are written once and never read back here: their
+// stores are non-temporal, so they do not displace from L2 the input lines
+// that the earlier tiles of the same lines still need.
 template <typename T, int E>
 __device__ __forceinline__ void store_run(T* __restrict__ base, int64_t off, bool vec_ok, int valid,
                                           const float (&f)[E]) {
   if (vec_ok) {
-    store_floats<T, E>(base + off, f);
+    constexpr int W = E * (int)sizeof(T) / 4;
+    uint32_t w[W];
+    pack_floats<T, E>(f, w);
+    if constexpr (W == 2) {
+      __builtin_nontemporal_store(((uint64_t)w[1] << 32) | w[0], reinterpret_cast<uint64_t*>(base + off));
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; ++i) __builtin_nontemporal_store(w[i], reinterpret_cast<uint32_t*>(base + off) + i);
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -499,6 +510,8 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
       }
       // dB, dC of this group's steps: the sums over the 64 channels
       const float sum = wave_sum16(terms, lane);
+      // (an ordinary store: these 4-byte pieces of the partial rows merge into
+      // whole lines in L2 before they are written back)
       if ((lane & 3) == 0 && (FULL || grp * TRS + so % TRS < tvalid)) pbc[t0 + grp * TRS] = sum;
     }
     __syncthreads();
