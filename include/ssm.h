@@ -32,8 +32,8 @@
  *    the positive time step; decoding one token at a time with a
  *    constant-size state (O(1) work, O(N) memory per token).
  *  - The D_skip term and the silu(z) output gate are not written out on the
- *    pages; the "Mamba" review says only that a gate mixes in the residual.
- *    They are applied as in the formula above.
+ *    pages; the "Mamba" review's block description only mentions a gate on
+ *    a residual branch.  They are applied as in the formula above.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The
@@ -205,8 +205,8 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
  *
  * (depthwise, causal, tap K-1 on the current input), and u feeds both the
  * recurrence and the D_skip term; x is read from HBM once.  Source: "Mamba"
- * paper review, "Mamba" block description (the input passes through a
- * convolution and a non-linearity before the SSM) and the NN LAB "Mamba"
+ * paper review, "Mamba" block description (before the SSM the input goes
+ * through a convolution and then a nonlinear function) and the NN LAB "Mamba"
  * page, "Kernel Fusion in On-Chip SRAM" (the causal 1-D convolution fused
  * with discretisation and scan).  Width, tap order and silu as the
  * non-linearity are not fixed by the pages; they are this interface's

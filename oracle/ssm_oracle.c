@@ -32,12 +32,12 @@
  *    y_k = C h_k (the readout comes after the update at the same step), the
  *    zero initial state of the worked impulse response, and
  *    softplus(x) = ln(1 + e^x) as the map that keeps Delta positive.
- *  - "Mamba" paper review, section "Mamba" block description: a gating
- *    mechanism mixes in the residual.  Read here as the output gate
- *    y <- (C.h + Dskip*u) * silu(z) with silu(z) = z / (1 + e^-z).
- *  - The same block description: the expanded input passes through a
- *    convolution and a non-linearity before the SSM; NN LAB "Mamba" page,
- *    "Kernel Fusion in On-Chip SRAM": that convolution is causal and 1-D.
+ *  - "Mamba" paper review, section "Mamba" block description: the block
+ *    gates its output with a residual branch (no formula given).  Read here
+ *    as the output gate y <- (C.h + Dskip*u) * silu(z), silu(z) = z/(1 + e^-z).
+ *  - The same block description: before the SSM the expanded input goes
+ *    through a convolution followed by a nonlinear function; NN LAB "Mamba"
+ *    page, "Kernel Fusion in On-Chip SRAM": that convolution is causal, 1-D.
  *    Read here as a depthwise (per channel) causal convolution of width K
  *    along t, the last tap on the current input, plus a per-channel bias,
  *    followed by silu:  u[t] = silu(cb[d] + sum_k w[d,k] x[t-K+1+k]),

@@ -31,14 +31,18 @@
 //    until the load block ends, then stored so each row line is written
 //    whole.
 //  * Optional convolution prologue ("Mamba" paper review, "Mamba" block
-//    description: the input passes through a convolution and a
-//    non-linearity before the SSM; NN LAB "Mamba" page, "Kernel Fusion in
+//    description: before the SSM the input goes through a convolution and
+//    then a nonlinear function; NN LAB "Mamba" page, "Kernel Fusion in
 //    On-Chip SRAM": a causal 1-D convolution fused with the scan):
 //    u = silu(cb + sum_k w[k] x[t-K+1+k]) per channel, computed in the
 //    staging step from the loaded x.  The K-1 <= 3 inputs before a thread's
 //    run come from the neighbouring run by a lane shuffle (the G runs of a
-//    channel sit in consecutive lanes of one wave), so x is read from HBM
-//    once, as u would be.
+//    channel sit in consecutive lanes of one wave), or for a channel's
+//    first run from the previous tile's last inputs kept in LDS, so x is
+//    read from HBM once, as u would be.  The taps also sit in LDS.
+//  * Whole load blocks are addressed through buffer descriptors over the
+//    workgroup's 64 rows: a lane's offset is fixed, the block's step offset
+//    is a scalar, so no lane holds 64-bit addresses.
 //  * Long sequences with too few channels to fill the GPU are split into
 //    segments.  The affine steps compose associatively ("NN LAB" Mamba page,
 //    "The Associative Property of Linear Recurrence"): a first launch runs

@@ -2,10 +2,11 @@
 ssm_conv_state_update) against the oracle's convolution followed by its
 scan.
 
-The prologue: "Mamba" paper review, "Mamba" block description (a
-convolution and a non-linearity before the SSM); NN LAB "Mamba" page,
-"Kernel Fusion in On-Chip SRAM" (causal 1-D convolution fused with the
-scan).  Read as depthwise, causal, tap K-1 on the current input, bias, silu.
+The prologue: "Mamba" paper review, "Mamba" block description (before the
+SSM the input goes through a convolution and then a nonlinear function); NN
+LAB "Mamba" page, "Kernel Fusion in On-Chip SRAM" (causal 1-D convolution
+fused with the scan).  Read as depthwise, causal, tap K-1 on the current
+input, bias, silu.
 """
 import numpy as np
 import pytest
