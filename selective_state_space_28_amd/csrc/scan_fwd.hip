@@ -142,17 +142,6 @@ __device__ __forceinline__ float input_term(float a, float x2, float dt, float q
   }
 }
 
-// Tiles whose u/delta/z loads are issued together: enough to cover a
-// 128-byte line of every row (so each line is fetched once, not once per
-// tile), within a budget of 24 VGPRs of raw words per thread.
-template <typename T, int G, int TL>
-constexpr int load_block_tiles() {
-  constexpr int W = (TL / G) * (int)sizeof(T) / 4;
-  constexpr int by_line = 128 / (TL * (int)sizeof(T));
-  constexpr int by_regs = 8 / W;
-  constexpr int kt = by_line < by_regs ? by_line : by_regs;
-  return kt < 1 ? 1 : (kt > 4 ? 4 : kt);
-}
 
 // PASS: kPassMain computes y (and last_state); kPassAgg runs every segment
 // but the last from a zero state and records its end state and Delta sum;
@@ -173,7 +162,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   constexpr int N = NS * G;
   constexpr int E = TL / G;                     // elements per thread, load/store phases
   constexpr int W = E * (int)sizeof(T) / 4;     // their size in 32-bit words
-  constexpr int KT = load_block_tiles<T, G, TL>();
+  constexpr int KT = scan_load_block_tiles((int)sizeof(T), G, TL);
   constexpr int LDW = 65;                       // padded LDS row: spreads the banks
   constexpr int CH = 2;                         // steps per software-pipelined chunk
   constexpr int R = 2 * NS;                     // floats per B, C record
@@ -227,15 +216,30 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     if (seg == 0 && h0 != nullptr && dvalid) h[k] = h0[row * N + n];
   }
   if (!AGG && seg > 0 && dvalid) {
-    // carry-in: compose the aggregates of segments 0 .. seg-1 in order
+    // carry-in: compose the aggregates of segments 0 .. seg-1 in order.  The
+    // aggregates' loads do not depend on the composition, so they are issued
+    // in groups whose latencies overlap (indices past seg-1 are clamped to
+    // it: in-bounds loads that are not composed).
+    constexpr int GRP = 8;
     const int64_t plane = (int64_t)p.batch * p.dim;
 #pragma unroll
     for (int k = 0; k < NS; ++k) h[k] = ws_hend[row * N + g * NS + k];
-    for (int j = 1; j < seg; ++j) {
-      const float sdt = ws_sumdt[j * plane + row];
+    for (int j0 = 1; j0 < seg; j0 += GRP) {
+      float sdt[GRP], he[GRP][NS];
 #pragma unroll
-      for (int k = 0; k < NS; ++k)
-        h[k] = __builtin_fmaf(segment_decay(sdt * A2[k]), h[k], ws_hend[(j * plane + row) * N + g * NS + k]);
+      for (int i = 0; i < GRP; ++i) {
+        const int j = min(j0 + i, seg - 1);
+        sdt[i] = ws_sumdt[j * plane + row];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) he[i][k] = ws_hend[(j * plane + row) * N + g * NS + k];
+      }
+#pragma unroll
+      for (int i = 0; i < GRP; ++i) {
+        if (j0 + i < seg) {
+#pragma unroll
+          for (int k = 0; k < NS; ++k) h[k] = __builtin_fmaf(segment_decay(sdt[i] * A2[k]), h[k], he[i][k]);
+        }
+      }
     }
   }
 
@@ -310,6 +314,9 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   };
   if (block_full(seg_begin)) fetch_block(seg_begin);
 
+  // Delta sum of this thread's runs (aggregate pass), gathered in the staging
+  // step, which every wave shares evenly, and reduced over a channel's G
+  // threads at the end
   double sumdt = 0.0;
 
   // The wave arbiter prefers older waves, so of the workgroups resident on a
@@ -373,12 +380,17 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     // Entries of channels past dim, or of steps past the tile end, hold
     // harmless values (u = 0 there, so Delta*u = 0): those steps are never
     // run and those lanes never store.
+    float dsum = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const float x = dd[e] + bias_cc;
       const float dt = p.softplus ? softplus_f32(x) : x;
       s_ddu[r0 + e][cc] = make_float2(dt, ZOH ? uu[e] : dt * uu[e]);
+      if constexpr (AGG) {
+        if (FAST || r0 + e < tvalid) dsum += dt;
+      }
     }
+    if constexpr (AGG) sumdt += (double)dsum;
     __syncthreads();
     if constexpr (CONV) {
       // this tile's last 3 inputs for the next tile (the reads above of the
@@ -438,11 +450,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
             h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, vc[i].x, vc[i].y * rc[i][k], rA[k]));
             acc = __builtin_fmaf(rc[i][NS + k], h[k], acc);
           }
-          if constexpr (READOUT) {
-            s_y[g][c * CH + i][lane] = acc;
-          } else if constexpr (AGG) {
-            if (g == 0) sumdt += (double)vc[i].x;
-          }
+          if constexpr (READOUT) s_y[g][c * CH + i][lane] = acc;
         }
         if (c + 1 < TL / CH) {
 #pragma unroll
@@ -464,11 +472,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
           h[k] = __builtin_fmaf(a, h[k], input_term<ZOH>(a, x2, v.x, v.y * rec_value<T>(bct + t * R, k), rA[k]));
           acc = __builtin_fmaf(rec_value<T>(bct + t * R, NS + k), h[k], acc);
         }
-        if constexpr (READOUT) {
-          s_y[g][t][lane] = acc;
-        } else if constexpr (AGG) {
-          if (g == 0) sumdt += (double)v.x;
-        }
+        if constexpr (READOUT) s_y[g][t][lane] = acc;
       }
     }
     __syncthreads();
@@ -524,12 +528,18 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   }
 
   // ---- segment results ---------------------------------------------------------
+  if constexpr (AGG) {
+    // a channel's G staging threads are consecutive lanes of one wave: sum
+    // their Delta sums in a fixed order (every lane takes part)
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) sumdt += __shfl_xor(sumdt, m);
+    if (chunk == 0 && ccvalid) ws_sumdt[(int64_t)seg * p.batch * p.dim + rowcc] = (float)sumdt;
+  }
   if (!dvalid) return;
   if constexpr (AGG) {
     const int64_t plane = (int64_t)p.batch * p.dim;
 #pragma unroll
     for (int k = 0; k < NS; ++k) ws_hend[(seg * plane + row) * N + g * NS + k] = h[k];
-    if (g == 0) ws_sumdt[seg * plane + row] = (float)sumdt;
   } else if constexpr (READOUT) {
     if (last_state != nullptr && seg == p.nseg - 1) {
 #pragma unroll

@@ -60,10 +60,13 @@ int elem_bytes(int dtype) { return dtype == SSM_BF16 ? 2 : 4; }
 
 bool flags_ok(int flags) { return (flags & ~(SSM_DELTA_SOFTPLUS | SSM_BBAR_ZOH)) == 0; }
 
-// Segments of the sequence for the forward scan.  SSM_SCAN_SEGMENTS (an
-// integer >= 1) overrides the choice; tests use it to run the carry path at
-// small sizes.
-SegPlan plan_segments(int batch, int dim, int dstate, int64_t L) {
+// Segments of the sequence for the forward scan.  A chosen segment length is
+// a whole number of the kernel's load blocks, so that every block of every
+// segment but the last is whole (its lines loaded and stored whole).
+// SSM_SCAN_SEGMENTS (an integer >= 1) overrides the choice, with segments of
+// whole tiles only; tests use it to run the carry path at small sizes and at
+// segment starts inside a load block.
+SegPlan plan_segments(int batch, int dim, int dstate, int64_t L, int dtype) {
   const int64_t tile = ssm::kScanTile;
   const int64_t G = dstate >= 4 ? dstate / 4 : 1;
   const int64_t ncg = (dim + 63) / 64;
@@ -71,11 +74,13 @@ SegPlan plan_segments(int batch, int dim, int dstate, int64_t L) {
   const int64_t capacity = kPlanCUs * kWavesPerCU / G;  // resident workgroups
   int64_t want = groups > 0 ? capacity / groups : 1;
   int64_t cap = L / kMinSegment;
+  int64_t granule = tile * ssm::scan_load_block_tiles(elem_bytes(dtype), (int)G);
   if (const char* env = std::getenv("SSM_SCAN_SEGMENTS")) {
     const long long v = std::atoll(env);
     if (v >= 1) {
       want = v;
       cap = want;
+      granule = tile;
     }
   }
   if (want > cap) want = cap;
@@ -83,7 +88,7 @@ SegPlan plan_segments(int batch, int dim, int dstate, int64_t L) {
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   int64_t seglen = (L + want - 1) / want;
-  seglen = (seglen + tile - 1) / tile * tile;
+  seglen = (seglen + granule - 1) / granule * granule;
   if (seglen < tile) seglen = tile;
   const int64_t nseg = (L + seglen - 1) / seglen;
   return SegPlan{(int)(nseg < 1 ? 1 : nseg), seglen};
@@ -206,7 +211,7 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
   if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return 0;
   if (batch == 0 || dim == 0 || seqlen == 0) return 0;
-  return workspace_layout(batch, dim, dstate, seqlen, dtype, plan_segments(batch, dim, dstate, seqlen))
+  return workspace_layout(batch, dim, dstate, seqlen, dtype, plan_segments(batch, dim, dstate, seqlen, dtype))
       .total;
 }
 
@@ -306,7 +311,7 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
     return SSM_OK;
   }
 
-  const SegPlan sp = plan_segments(batch, dim, dstate, seqlen);
+  const SegPlan sp = plan_segments(batch, dim, dstate, seqlen, dtype);
   const int64_t blocks = (int64_t)batch * ((dim + 63) / 64) * sp.nseg;
   const int64_t pack_blocks = (int64_t)batch * ((seqlen + 255) / 256);
   if (blocks > INT_MAX || pack_blocks > INT_MAX) return SSM_ERR_SHAPE;
@@ -494,7 +499,7 @@ size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return 0;
   if (batch == 0 || dim == 0 || seqlen == 0) return 0;
   return bwd_workspace_layout(batch, dim, dstate, seqlen, dtype,
-                              plan_segments(batch, dim, dstate, seqlen))
+                              plan_segments(batch, dim, dstate, seqlen, dtype))
       .total;
 }
 
@@ -546,7 +551,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
 
-  const SegPlan sp = plan_segments(batch, dim, dstate, seqlen);
+  const SegPlan sp = plan_segments(batch, dim, dstate, seqlen, dtype);
   const int64_t blocks = (int64_t)batch * ((dim + 63) / 64) * sp.nseg;
   const int64_t pack_blocks = (int64_t)batch * ((seqlen + 255) / 256);
   const int64_t red_blocks = (2 * (int64_t)batch * dstate * seqlen + 255) / 256;

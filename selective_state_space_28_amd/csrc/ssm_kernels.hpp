@@ -10,6 +10,18 @@ namespace ssm {
 // Time steps one workgroup stages per tile of the forward scan.
 constexpr int kScanTile = 16;
 
+// Tiles of the forward scan whose u/delta/z loads are issued together (a
+// load block): enough to cover a 128-byte line of every row, so each line is
+// fetched once rather than once per tile, within a budget of 8 32-bit words
+// of each array per thread.  A thread loads TL/G steps of a tile.
+constexpr int scan_load_block_tiles(int elem_bytes, int G, int TL = kScanTile) {
+  const int W = (TL / G) * elem_bytes / 4;
+  const int by_line = 128 / (TL * elem_bytes);
+  const int by_regs = 8 / W;
+  const int kt = by_line < by_regs ? by_line : by_regs;
+  return kt < 1 ? 1 : (kt > 4 ? 4 : kt);
+}
+
 // Storage type of the per-token tensors.
 enum class Dtype { F32 = 0, BF16 = 1 };
 
