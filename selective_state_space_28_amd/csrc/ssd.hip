@@ -247,7 +247,8 @@ __device__ __forceinline__ int causal_tile_row(int q) { return q < 1 ? 0 : q < 3
 
 // The k-th (k < 3) causal tile that wave w (w < 4) forms in the scan, or -1:
 // one diagonal tile per wave (0, 5, 2, 9; the costly ones, with a decay per
-// entry), then the off-diagonal ones.
+// entry) as k = 0, then the ones below the diagonal as k = 1, 2 (the mask
+// step relies on this order).
 __device__ __forceinline__ int wave_mask_tile(int w, int k) {
   const int t0 = w == 0 ? 0 : w == 1 ? 5 : w == 2 ? 2 : 9;
   const int t1 = w == 0 ? 4 : w == 1 ? 1 : w == 2 ? 6 : 3;
@@ -327,6 +328,11 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(const T* __restrict__ B, 
     g = tile_mma<T>(&sBt[0][0], LN, 16 * j, &sCt[0][0], LN, 16 * i, KN, lane, g);
     G[(((int64_t)b * nchunks + c) * 10 + q) * 64 + lane] = make_float4(g[0], g[1], g[2], g[3]);
   }
+}
+
+// Eight bf16 operand values of a lane from LDS (one 16-byte read).
+__device__ __forceinline__ bf16x8_t lds_frag8(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8_t*>(p);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
@@ -639,41 +645,66 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
     if constexpr (FULL) load_part_xc(next);  // x and C^T are in LDS
 
     // the 10 causal 16x16 tiles (t-block i, s-block j <= i) dealt over the 4
-    // waves one diagonal tile each (wave_mask_tile); a lane holds 4
-    // consecutive s of one t and writes them at once
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int q = wave_mask_tile(w, k);
-      if (q < 0) break;
-      const int i = causal_tile_row(q), j = q - i * (i + 1) / 2;
-      const float gv[4] = {rg[k].x, rg[k].y, rg[k].z, rg[k].w};
-      const int t = 16 * i + (lane & 15), s0 = 16 * j + 4 * (lane >> 4);
-      float mv[4];
-      if (i == j) {  // diagonal tile: the decay between s and t directly
-        const float ct = sCum2[t];
-        const float4 cs = *reinterpret_cast<const float4*>(&sCum2[s0]);
-        const float4 bs = *reinterpret_cast<const float4*>(&sCoef[s0]);
-        const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mv[r] = s0 + r <= t ? (gv[r] * bsv[r]) * exp2_hw(ct - csv[r]) : 0.0f;
-      } else {  // s < 16i <= t: split at step 16i
-        const float e1 = sE1[t];
-        const float4 w2 = *reinterpret_cast<const float4*>(&sW2[i][s0]);
-        mv[0] = (gv[0] * w2.x) * e1;
-        mv[1] = (gv[1] * w2.y) * e1;
-        mv[2] = (gv[2] * w2.z) * e1;
-        mv[3] = (gv[3] * w2.w) * e1;
+    // waves: tile 0 of a wave is its diagonal tile, tiles 1 and 2 (when
+    // dealt) lie below the diagonal (wave_mask_tile).  A lane holds 4
+    // consecutive s of one t and writes them at once; every LDS read of the
+    // wave's tiles is issued before the first is used.
+    {
+      const int tl = lane & 15, sl = 4 * (lane >> 4);
+      const int q1 = wave_mask_tile(w, 1), q2 = wave_mask_tile(w, 2);
+      const int i0 = causal_tile_row(wave_mask_tile(w, 0));
+      const int i1 = causal_tile_row(q1), j1 = q1 - i1 * (i1 + 1) / 2;
+      const bool has2 = q2 >= 0;
+      const int i2 = has2 ? causal_tile_row(q2) : 0, j2 = has2 ? q2 - i2 * (i2 + 1) / 2 : 0;
+      const int t0d = 16 * i0 + tl, s0d = 16 * i0 + sl;
+      const int t1 = 16 * i1 + tl, s01 = 16 * j1 + sl;
+      const int t2 = 16 * i2 + tl, s02 = 16 * j2 + sl;
+      const float ct = sCum2[t0d];
+      const float4 cs = *reinterpret_cast<const float4*>(&sCum2[s0d]);
+      const float4 bs = *reinterpret_cast<const float4*>(&sCoef[s0d]);
+      const float e1a = sE1[t1];
+      const float4 w2a = *reinterpret_cast<const float4*>(&sW2[i1][s01]);
+      float e1b = 0.0f;
+      float4 w2b = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (has2) {
+        e1b = sE1[t2];
+        w2b = *reinterpret_cast<const float4*>(&sW2[i2][s02]);
       }
-      uint32_t wv[4 * sizeof(T) / 4];
-      pack_floats<T, 4>(mv, wv);
-      store_words<4 * sizeof(T) / 4>(&sM[t][s0], wv);
+      {  // diagonal tile: the decay between s and t directly
+        const float gv[4] = {rg[0].x, rg[0].y, rg[0].z, rg[0].w};
+        const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, bsv[4] = {bs.x, bs.y, bs.z, bs.w};
+        float mv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mv[r] = s0d + r <= t0d ? (gv[r] * bsv[r]) * exp2_hw(ct - csv[r]) : 0.0f;
+        uint32_t wv[4 * sizeof(T) / 4];
+        pack_floats<T, 4>(mv, wv);
+        store_words<4 * sizeof(T) / 4>(&sM[t0d][s0d], wv);
+      }
+      // below the diagonal (s < 16i <= t): the decay split at step 16i
+      auto off_tile = [&](const float4& g, float e1, const float4& w2, int t, int s0) {
+        float mv[4];
+        mv[0] = (g.x * w2.x) * e1;
+        mv[1] = (g.y * w2.y) * e1;
+        mv[2] = (g.z * w2.z) * e1;
+        mv[3] = (g.w * w2.w) * e1;
+        uint32_t wv[4 * sizeof(T) / 4];
+        pack_floats<T, 4>(mv, wv);
+        store_words<4 * sizeof(T) / 4>(&sM[t][s0], wv);
+      };
+      off_tile(rg[1], e1a, w2a, t1, s01);
+      if (has2) off_tile(rg[2], e1b, w2b, t2, s02);
     }
     if constexpr (FULL) load_part_g(next);  // this chunk's G tiles are used
     __syncthreads();
 
     // ---- (3) Y = M X^T + diag(exp(cum_t)) C^T H for this wave's channels, staged [p][t]
     // ----------------------------------------------------------------------------------
-    {
+    if constexpr (sizeof(T) == 2) {
+      // bf16: every LDS operand of a t-block is read before its first product,
+      // so the reads' latencies overlap instead of each product waiting for
+      // its own; the x operands of the diagonal product (this wave's channels,
+      // both K halves) serve every t-block
+      const int rr = lane & 15, kk = 8 * (lane >> 4);
       typename Mma<T>::StatePack hp[NPK];
       const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -681,20 +712,28 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         const int k1 = TPP * m + 1 < HT ? TPP * m + 1 : HT - 1;
         hp[m] = Mma<T>::pack_state(H[TPP * m], TPP * m + 1 < HT ? H[k1] : zero);
       }
+      const bf16x8_t xb0 = lds_frag8(&sX[16 * w + rr][kk]);
+      const bf16x8_t xb1 = lds_frag8(&sX[16 * w + rr][32 + kk]);
 #pragma unroll
       for (int i = 0; i < Q / 16; ++i) {
-        f32x4_t yd = zero, yo = zero;
-        // diagonal part: t-block i needs s < 16 (i + 1)
-        yd = tile_mma<T>(&sM[0][0], LQ, 16 * i, &sX[0][0], LQ, 16 * w, 16 * (i + 1), lane, yd);
-        // the state entering the chunk
+        // t-block i needs s < 16 (i + 1): one product of K = 32 for i < 2 (the
+        // staged zeros above the diagonal fill it), two for i >= 2
+        const bf16x8_t ma0 = lds_frag8(&sM[16 * i + rr][kk]);
+        const bf16x8_t ma1 = i >= 2 ? lds_frag8(&sM[16 * i + rr][32 + kk]) : bf16x8_t{};
+        bf16x8_t ca[NPK];
 #pragma unroll
-        for (int m = 0; m < NPK; ++m) yo = Mma<T>::mma_state(&sCt[16 * i][PS * m], LN, hp[m], yo, lane);
-        // y = (Y + D x) silu(z) for this lane's 4 steps, staged in the storage type;
-        // the state part takes its decay exp2(cum_t) here
+        for (int m = 0; m < NPK; ++m) ca[m] = lds_frag8(&sCt[16 * i + rr][PS * m + kk]);
         const int tc = 16 * i + ty;
         uint32_t xr[RW / 2];
         load_words<RW / 2>(&sX[py][tc], xr);
         const float4 e4 = *reinterpret_cast<const float4*>(&sE0[tc]);
+        f32x4_t yd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ma0, xb0, zero, 0, 0, 0);
+        if (i >= 2) yd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ma1, xb1, yd, 0, 0, 0);
+        f32x4_t yo = zero;
+#pragma unroll
+        for (int m = 0; m < NPK; ++m) yo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[m], hp[m], yo, 0, 0, 0);
+        // y = (Y + D x) silu(z) for this lane's 4 steps, staged in the storage
+        // type; the state part takes its decay exp2(cum_t) here
         const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
         float yv[4];
 #pragma unroll
@@ -707,22 +746,76 @@ __global__ __launch_bounds__(256, 2) void ssd_kernel(
         pack_floats<T, 4>(yv, yw);
         store_words<RW / 2>(&sY[py][tc], yw);
       }
-    }
-    if constexpr (FULL && GATE) load_gate(full_c, next);  // this chunk's z are used
-    // ---- H <- exp(cum_Q) H + B (x o w)^T ----------------------------------------------------
-    {
+      if constexpr (FULL && GATE) load_gate(full_c, next);  // this chunk's z are used
+      // H <- exp(cum_Q) H + B (x o w)^T, the B operands of each K half read
+      // together before its products
       const float decay = exp2_hw(cum2Q);
 #pragma unroll
       for (int k = 0; k < HT; ++k) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) H[k][r] *= decay;
       }
-      const int rr = lane & 15, kk = Mma<T>::KL * (lane >> 4);
 #pragma unroll
-      for (int k0 = 0; k0 < Q; k0 += Mma<T>::K) {
-        const Op* bx = &sXw[16 * w + rr][k0 + kk];
+      for (int k0 = 0; k0 < Q; k0 += 32) {
+        const bf16x8_t bx = lds_frag8(&sXw[16 * w + rr][k0 + kk]);
+        bf16x8_t ba[HT];
 #pragma unroll
-        for (int k = 0; k < HT; ++k) H[k] = Mma<T>::mma(&sB[16 * k + rr][k0 + kk], bx, H[k]);
+        for (int k = 0; k < HT; ++k) ba[k] = lds_frag8(&sB[16 * k + rr][k0 + kk]);
+#pragma unroll
+        for (int k = 0; k < HT; ++k) H[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba[k], bx, H[k], 0, 0, 0);
+      }
+    } else {
+      {
+        typename Mma<T>::StatePack hp[NPK];
+        const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < NPK; ++m) {
+          const int k1 = TPP * m + 1 < HT ? TPP * m + 1 : HT - 1;
+          hp[m] = Mma<T>::pack_state(H[TPP * m], TPP * m + 1 < HT ? H[k1] : zero);
+        }
+#pragma unroll
+        for (int i = 0; i < Q / 16; ++i) {
+          f32x4_t yd = zero, yo = zero;
+          // diagonal part: t-block i needs s < 16 (i + 1)
+          yd = tile_mma<T>(&sM[0][0], LQ, 16 * i, &sX[0][0], LQ, 16 * w, 16 * (i + 1), lane, yd);
+          // the state entering the chunk
+#pragma unroll
+          for (int m = 0; m < NPK; ++m) yo = Mma<T>::mma_state(&sCt[16 * i][PS * m], LN, hp[m], yo, lane);
+          // y = (Y + D x) silu(z) for this lane's 4 steps, staged in the storage type;
+          // the state part takes its decay exp2(cum_t) here
+          const int tc = 16 * i + ty;
+          uint32_t xr[RW / 2];
+          load_words<RW / 2>(&sX[py][tc], xr);
+          const float4 e4 = *reinterpret_cast<const float4*>(&sE0[tc]);
+          const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+          float yv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float v = __builtin_fmaf(Dp, run_elem4<T>(xr, r), __builtin_fmaf(ev[r], yo[r], yd[r]));
+            if constexpr (GATE) v *= silu_f32(run_elem4<T>(rz[i], r));
+            yv[r] = v;
+          }
+          uint32_t yw[RW / 2];
+          pack_floats<T, 4>(yv, yw);
+          store_words<RW / 2>(&sY[py][tc], yw);
+        }
+      }
+      if constexpr (FULL && GATE) load_gate(full_c, next);  // this chunk's z are used
+      // ---- H <- exp(cum_Q) H + B (x o w)^T ----------------------------------------------------
+      {
+        const float decay = exp2_hw(cum2Q);
+#pragma unroll
+        for (int k = 0; k < HT; ++k) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) H[k][r] *= decay;
+        }
+        const int rr = lane & 15, kk = Mma<T>::KL * (lane >> 4);
+#pragma unroll
+        for (int k0 = 0; k0 < Q; k0 += Mma<T>::K) {
+          const Op* bx = &sXw[16 * w + rr][k0 + kk];
+#pragma unroll
+          for (int k = 0; k < HT; ++k) H[k] = Mma<T>::mma(&sB[16 * k + rr][k0 + kk], bx, H[k]);
+        }
       }
     }
     __syncthreads();
