@@ -148,21 +148,21 @@ def settle(step, dev, min_ms):
 
 
 def timed(step, dev, stream, steps):
-    """Mean milliseconds per call over `steps` calls, each bracketed by HIP
-    events recorded on the stream the kernels run on."""
+    """Milliseconds per call over `steps` back-to-back calls: one pair of HIP
+    events recorded on the stream the kernels run on brackets all of them
+    (so no event sits between two calls), with a device synchronisation
+    before and after.  Also returns the host wall time per call."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    for s_, e_ in ev:
-        s_.record(stream)
+    start.record(stream)
+    for _ in range(steps):
         step()
-        e_.record(stream)
+    end.record(stream)
     torch.cuda.synchronize(dev)
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = np.array([s_.elapsed_time(e_) for s_, e_ in ev])
-    return float(per.mean()), wall
+    return float(start.elapsed_time(end)) / steps, wall
 
 
 def main():
