@@ -1,9 +1,10 @@
 """GPU checks of what include/ssm.h promises beyond finite, stable inputs:
 
 * NaN and Inf inputs propagate: planted into u, delta and z (and the decode
-  state), the non-finite outputs appear exactly where the fp64 oracle puts
-  them (NaN where it has NaN, Inf of the same sign where it has Inf), and
-  every other output still matches the oracle within the usual tolerance.
+  state), and into the B and C that a batch row's channels share, the
+  non-finite outputs appear exactly where the fp64 oracle puts them (NaN
+  where it has NaN, Inf of the same sign where it has Inf), and every other
+  output still matches the oracle within the usual tolerance.
 * A > 0 is not rejected: the state grows ("Exercises -- State-space models
   (Mamba, S4)", the stability exercise: |Abar| > 1 diverges; NN LAB "Mamba",
   "Proof of Spectral Stability & Contraction Mapping": the bound needs
@@ -93,6 +94,40 @@ def test_scan_nan_inf_propagate(dev, dtype, bbar, segs, monkeypatch):
     # the planted channels are the only ones with non-finite outputs
     bad = {(int(b), int(d)) for b, d, _ in np.argwhere(~np.isfinite(y))}
     assert bad <= {(b, d) for _, (b, d, _), _v in PLANTS}
+
+
+# B and C are shared by every channel of a batch row: a non-finite B at step t
+# reaches every channel's state (and output) of that row from t on; a
+# non-finite C reaches the outputs of step t only.
+PLANTS_BC = [  # (array, (b, n, t), value)
+    ("B", (0, 3, 50), NAN),
+    ("C", (1, 10, 200), PINF),
+    ("C", (1, 0, 260), NINF),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("bbar", ["euler", "zoh"])
+@pytest.mark.parametrize("segs", [None, 3])
+def test_scan_nan_inf_in_B_C(dev, dtype, bbar, segs, monkeypatch):
+    if segs is not None:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+    cfg = ScanConfig("naninf-bc", 2, 130, 16, 300, dtype, seed=24, a_jitter=0.1)
+    inp = synth.make_scan_inputs(cfg)
+    for key, idx, v in PLANTS_BC:
+        _plant(inp[key], dtype, idx, v)
+    y, last = gpu_scan(inp, dev, bbar=bbar)
+    yr, lr = oracle_scan(inp, bbar=bbar)
+    ny, fin = _same_nonfinite(y, yr, f"y ({dtype}, {bbar}, segments {segs})")
+    assert ny > 0
+    assert_parity(y[fin], yr[fin], dtype, "finite part of y")
+    _, finl = _same_nonfinite(last, lr, "last_state")
+    assert_parity(last[finl], lr[finl], "f32", "finite part of last_state")
+    # row 0: every channel non-finite from step 50 on, finite before; row 1:
+    # every channel non-finite at steps 200 and 260 only
+    assert np.all(~np.isfinite(y[0, :, 50:])) and np.all(np.isfinite(y[0, :, :50]))
+    bad_t = sorted({int(t) for t in np.argwhere(~np.isfinite(y[1]))[:, 1]})
+    assert bad_t == [200, 260] and np.all(~np.isfinite(y[1][:, [200, 260]]))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
