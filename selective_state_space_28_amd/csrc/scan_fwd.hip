@@ -408,12 +408,13 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     }
 
     // ---- checkpoint: the state entering this tile, (batch, tile, N, dim) ------
+    // (non-temporal: read once, by the backward pass, long after this pass)
     if constexpr (CKPT) {
       if (dvalid) {
         const int64_t ntiles = (L + TL - 1) / TL;
         float* cp = ws_ckpt + (((int64_t)b * ntiles + t0 / TL) * N + g * NS) * p.dim + d;
 #pragma unroll
-        for (int k = 0; k < NS; ++k) cp[(int64_t)k * p.dim] = h[k];
+        for (int k = 0; k < NS; ++k) __builtin_nontemporal_store(h[k], cp + (int64_t)k * p.dim);
       }
     }
 
