@@ -142,7 +142,6 @@ __device__ __forceinline__ float input_term(float a, float x2, float dt, float q
   }
 }
 
-
 // PASS: kPassMain computes y (and last_state); kPassAgg runs every segment
 // but the last from a zero state and records its end state and Delta sum;
 // kPassCkpt runs like the main pass but, instead of y, records the state
