@@ -1,0 +1,203 @@
+"""Seeded sweep of random shapes and options against the oracle.
+
+The other GPU tests each vary one thing; here every case draws all of them
+at once from its own seed -- batch, channels (ragged 64-channel groups),
+states, sequence length (ragged tiles and load blocks), storage type, input
+term (Euler or zero-order hold), gate, D-skip, h0, a forced segment count,
+and for the convolution its width -- so that combinations no hand-written
+case names still meet the oracle.  Every case prints what it drew before it
+runs.  Sizes stay small: each case runs in well under a second.
+
+Comparison as everywhere: max|gpu - oracle| <= tol * max|oracle| over each
+output tensor (tol 1e-4 for fp32 storage, 2e-2 for bf16)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.configs import DecodeConfig, ScanConfig, SsdConfig
+from tests.helpers import assert_parity, gpu_scan, oracle_scan, to_torch, widened
+
+pytestmark = pytest.mark.gpu
+
+NCASES = 48
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import selective_state_space_28_amd as ssm
+    ssm.load()
+    return torch.device("cuda:0")
+
+
+def _draw(i: int, salt: int) -> dict:
+    rng = np.random.default_rng([salt, i])
+    L = int(np.exp(rng.uniform(0.0, np.log(700.0))))
+    return dict(
+        dtype=str(rng.choice(["f32", "bf16"])),
+        batch=int(rng.integers(1, 4)),
+        dim=int(rng.integers(1, 200)),
+        n=int(rng.choice([1, 2, 4, 8, 16])),
+        L=max(1, L),
+        bbar=str(rng.choice(["euler", "zoh"])),
+        gate=bool(rng.integers(0, 2)),
+        dskip=bool(rng.integers(0, 2)),
+        h0=bool(rng.integers(0, 2)),
+        segs=int(rng.choice([0, 0, 2, 3, 5])),
+        K=int(rng.integers(1, 5)),
+        jitter=float(rng.choice([0.0, 0.1])),
+        seed=int(rng.integers(0, 2**31 - 1)),
+    )
+
+
+def _inputs(c):
+    cfg = ScanConfig("sweep", c["batch"], c["dim"], c["n"], c["L"], c["dtype"], seed=c["seed"],
+                     a_jitter=c["jitter"], gate=c["gate"], dskip=c["dskip"])
+    inp = synth.make_scan_inputs(cfg)
+    h0 = None
+    if c["h0"]:
+        rng = np.random.default_rng([c["seed"], 7])
+        h0 = (0.5 * rng.standard_normal((c["batch"], c["dim"], c["n"]))).astype(np.float32)
+    return inp, h0
+
+
+@pytest.mark.parametrize("i", range(NCASES))
+def test_sweep_scan(dev, i, monkeypatch):
+    c = _draw(i, 101)
+    print("case", c, flush=True)
+    if c["segs"]:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(c["segs"]))
+    inp, h0 = _inputs(c)
+    y, last = gpu_scan(inp, dev, h0=h0, bbar=c["bbar"])
+    yr, lr = oracle_scan(inp, h0=h0, bbar=c["bbar"])
+    assert_parity(y, yr, c["dtype"], "y")
+    assert_parity(last, lr, "f32", "last_state")
+
+
+@pytest.mark.parametrize("i", range(NCASES))
+def test_sweep_conv_scan(dev, i, monkeypatch):
+    import torch
+    import selective_state_space_28_amd as ssm
+    c = _draw(i, 202)
+    print("case", c, flush=True)
+    if c["segs"]:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(c["segs"]))
+    inp, h0 = _inputs(c)
+    K = c["K"]
+    cp = synth.make_conv_params(c["dim"], K, c["seed"], state_batch=c["batch"] if (c["h0"] and K > 1) else None)
+    dt = c["dtype"]
+    t = {k: to_torch(inp.get(k), dt, dev) for k in ("u", "delta", "B", "C", "z")}
+    A, D, bias = (to_torch(inp.get(k), "f32", dev) for k in ("A", "D", "delta_bias"))
+    w, cb, st = (to_torch(cp.get(k), "f32", dev) for k in ("conv_w", "conv_b", "conv_state"))
+    y, last, cs = ssm.ssm_conv_scan_fwd(t["u"], w, cb, t["delta"], A, t["B"], t["C"], D, t["z"], bias,
+                                        h0=to_torch(h0, "f32", dev), conv_state_in=st, return_conv_state=True,
+                                        return_last_state=True, bbar=c["bbar"])
+    torch.cuda.synchronize(dev)
+    wd = widened(inp)
+    yr, lr, csr = oracle.conv_scan_fwd(wd["u"], cp["conv_w"], cp["conv_b"], cp.get("conv_state"), wd["delta"],
+                                       wd["A"], wd["B"], wd["C"], wd["D"], wd["z"], wd["delta_bias"], True,
+                                       None if h0 is None else h0.astype(np.float64), nthreads=8, bbar=c["bbar"])
+    assert_parity(y.float().cpu().numpy(), yr, dt, "y")
+    assert_parity(last.cpu().numpy(), lr, "f32", "last_state")
+    # the carried inputs are copies of x (or of the incoming state)
+    np.testing.assert_array_equal(cs.cpu().numpy().astype(np.float64), csr)
+
+
+@pytest.mark.parametrize("i", range(NCASES // 2))
+def test_sweep_bwd(dev, i, monkeypatch):
+    import torch
+    import selective_state_space_28_amd as ssm
+    c = _draw(i, 303)
+    c["L"] = min(c["L"], 300)
+    print("case", c, flush=True)
+    if c["segs"]:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(c["segs"]))
+    inp, h0 = _inputs(c)
+    rng = np.random.default_rng([c["seed"], 9])
+    dy = rng.standard_normal((c["batch"], c["dim"], c["L"]), dtype=np.float32)
+    dt = c["dtype"]
+    dyk = synth.bf16_bits(dy) if dt == "bf16" else dy
+    t = {k: to_torch(inp.get(k), dt, dev) for k in ("u", "delta", "B", "C", "z")}
+    A, D, bias = (to_torch(inp.get(k), "f32", dev) for k in ("A", "D", "delta_bias"))
+    g = ssm.ssm_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias, h0=to_torch(h0, "f32", dev),
+                         dy=to_torch(dyk, dt, dev), bbar=c["bbar"])
+    torch.cuda.synchronize(dev)
+    wd = widened(inp)
+    r = oracle.scan_bwd(wd["u"], wd["delta"], wd["A"], wd["B"], wd["C"], wd["D"], wd["z"], wd["delta_bias"],
+                        True, None if h0 is None else h0.astype(np.float64), dy=synth.widen(dyk, dt),
+                        dlast=None, nthreads=8, bbar=c["bbar"])
+    for k, ref in r.items():
+        if ref is None or g.get(k) is None:
+            continue
+        assert_parity(g[k].float().cpu().numpy(), ref, "bf16" if dt == "bf16" else "f32", k)
+
+
+@pytest.mark.parametrize("i", range(NCASES // 2))
+def test_sweep_ssd(dev, i):
+    import torch
+    import selective_state_space_28_amd as ssm
+    c = _draw(i, 404)
+    n = int(np.random.default_rng([404, i, 1]).choice([16, 32, 64, 128] if c["dtype"] == "bf16" else [16, 32, 64]))
+    nheads = 1 + c["dim"] % 3
+    print("case", c, "N", n, "heads", nheads, flush=True)
+    cfg = SsdConfig("sweep", c["batch"], nheads, 64, n, c["L"], c["dtype"], seed=c["seed"],
+                    gate=c["gate"], dskip=c["dskip"])
+    inp = synth.make_ssd_inputs(cfg)
+    h0 = None
+    if c["h0"]:
+        h0 = (0.5 * np.random.default_rng([c["seed"], 8]).standard_normal((c["batch"], cfg.dim, n))).astype(np.float32)
+    dt = c["dtype"]
+    t = {k: to_torch(inp.get(k), dt, dev) for k in ("x", "dt", "B", "C", "z")}
+    A, D, bias = (to_torch(inp.get(k), "f32", dev) for k in ("A", "D", "dt_bias"))
+    y, last = ssm.ssm_ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], D, t["z"], bias,
+                                   h0=to_torch(h0, "f32", dev), bbar=c["bbar"], return_last_state=True)
+    torch.cuda.synchronize(dev)
+    w = {k: (None if inp.get(k) is None else synth.widen(inp[k], dt)) for k in ("x", "dt", "B", "C", "z")}
+    yr, lr = oracle.ssd_scan_fwd(w["x"], w["dt"], inp["A"], w["B"], w["C"], inp.get("D"), w["z"],
+                                 inp.get("dt_bias"), True, h0, nthreads=8, bbar=c["bbar"])
+    assert_parity(y.float().cpu().numpy(), yr, dt, "y")
+    assert_parity(last.cpu().numpy(), lr, "bf16" if dt == "bf16" else "f32", "last_state")
+
+
+@pytest.mark.parametrize("i", range(NCASES // 2))
+def test_sweep_decode(dev, i):
+    """Several one-token steps (with the convolution prologue when the draw's
+    width is above 1), the state carried on the GPU and in the oracle."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    c = _draw(i, 505)
+    steps = 1 + i % 4
+    print("case", c, "steps", steps, flush=True)
+    cfg = DecodeConfig("sweep", c["batch"], c["dim"], c["n"], steps, c["dtype"], seed=c["seed"],
+                       gate=c["gate"], dskip=c["dskip"])
+    p = synth.make_decode_params(cfg)
+    dt, K = c["dtype"], c["K"]
+    conv = K > 1
+    cp = synth.make_conv_params(c["dim"], K, c["seed"], state_batch=c["batch"]) if conv else None
+    st = to_torch(p["h0"], "f32", dev)
+    cst = to_torch(cp["conv_state"], "f32", dev) if conv else None
+    w, cb = (to_torch(cp[k], "f32", dev) for k in ("conv_w", "conv_b")) if conv else (None, None)
+    A, D, bias = (to_torch(p.get(k), "f32", dev) for k in ("A", "D", "delta_bias"))
+    sr = p["h0"].astype(np.float64)
+    csr = cp["conv_state"].astype(np.float64) if conv else None
+    for s_ in range(steps):
+        tok = synth.make_decode_step(cfg, s_)
+        t = {k: to_torch(tok.get(k), dt, dev) for k in ("u", "delta", "B", "C", "z")}
+        if conv:
+            y = ssm.ssm_conv_state_update(cst, st, t["u"], w, cb, t["delta"], A, t["B"], t["C"], D, t["z"],
+                                          bias, bbar=c["bbar"])
+        else:
+            y = ssm.ssm_state_update(st, t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias, bbar=c["bbar"])
+        torch.cuda.synchronize(dev)
+        wt = {k: (None if tok.get(k) is None else synth.widen(tok[k], dt)) for k in ("u", "delta", "B", "C", "z")}
+        x = wt["u"]
+        if conv:
+            x, csr = oracle.conv_step(csr, x, cp["conv_w"], cp["conv_b"])
+        yr, sr = oracle.state_update(sr, x, wt["delta"], p["A"], wt["B"], wt["C"], p.get("D"), wt["z"],
+                                     p["delta_bias"], bbar=c["bbar"])
+        assert_parity(y.float().cpu().numpy(), yr, dt, f"y of step {s_}")
+        assert_parity(st.cpu().numpy(), sr, "f32", f"state after step {s_}")
+        if conv:
+            np.testing.assert_array_equal(cst.cpu().numpy().astype(np.float64), csr)
