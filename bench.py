@@ -251,7 +251,7 @@ def main():
     trace_ns = scan_prof.get("trace_avg_ns")
     hbm_view = {"achieved": round(alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(alg_gbps / HBM_PEAK_GBPS, 4),
-                "note": "algorithmic bytes per launch / event-timed step"}
+                "note": "algorithmic bytes per launch / timed step (the timed calls between one HIP event pair, over their number)"}
     if traffic:
         hbm_view["measured_GBps"] = round(traffic / (ms * 1e-3) / 1e9, 1)
         hbm_view["measured_frac"] = round(traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
