@@ -136,6 +136,29 @@ __device__ __forceinline__ void store_run(T* __restrict__ base, int64_t off, boo
   }
 }
 
+// A whole run of E elements through a buffer descriptor, non-temporal (the
+// slc bit of the cache policy: nt on this architecture).
+template <typename T, int E>
+__device__ __forceinline__ void buf_store_run_nt(const Buf& bb, uint32_t voff, uint32_t soff, const float (&f)[E]) {
+  constexpr int W = E * (int)sizeof(T) / 4;
+  uint32_t w[W];
+  pack_floats<T, E>(f, w);
+  if constexpr (W == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], bb.r, voff, soff, 2);
+  } else if constexpr (W == 2) {
+    u32x2_t v;
+    v.x = w[0]; v.y = w[1];
+    __builtin_amdgcn_raw_buffer_store_b64(v, bb.r, voff, soff, 2);
+  } else {
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      u32x4_t v;
+      v.x = w[4 * i]; v.y = w[4 * i + 1]; v.z = w[4 * i + 2]; v.w = w[4 * i + 3];
+      __builtin_amdgcn_raw_buffer_store_b128(v, bb.r, voff + 16 * i, soff, 2);
+    }
+  }
+}
+
 // ---- 2. reverse aggregates of segments 1 .. nseg-1 ------------------------------
 template <typename T, int NS, int G, int TL>
 __global__ __launch_bounds__(64 * G) void bwd_agg_kernel(
@@ -304,6 +327,18 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   const float bias_cc = (bias != nullptr && ccvalid) ? bias[dcc] : 0.0f;
   const float D_cc = (Dskip != nullptr && ccvalid) ? Dskip[dcc] : 0.0f;
   const bool has_z = z != nullptr;
+  // whole tiles address the workgroup's 64 rows through buffer descriptors:
+  // a lane's 32-bit offset is fixed, the tile's step offset is a scalar
+  const int64_t grow = (int64_t)b * p.dim + (int64_t)cg * 64;
+  const int64_t gbytes = p.vec ? (int64_t)min(64, p.dim - cg * 64) * L * (int64_t)sizeof(T) : 0;
+  const Buf b_u = make_buf(u + grow * L, gbytes);
+  const Buf b_dl = make_buf(delta + grow * L, gbytes);
+  const Buf b_g = make_buf(dy + grow * L, gbytes);
+  const Buf b_z = make_buf(has_z ? z + grow * L : u, has_z ? gbytes : 0);
+  const Buf b_du = make_buf(du + grow * L, gbytes);
+  const Buf b_dd = make_buf(ddelta + grow * L, gbytes);
+  const Buf b_dz = make_buf(has_z ? dz + grow * L : du, has_z ? gbytes : 0);
+  const uint32_t voff = p.vec ? (uint32_t)(((int64_t)cc * L + r0) * (int64_t)sizeof(T)) : 0u;
   float accD = 0.0f, accBias = 0.0f;
 
   float hist[TL][NS];
@@ -341,11 +376,11 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
     }
   };
   auto prefetch = [&](int64_t t0) {
-    const int64_t off = rowcc * L + t0 + r0;
-    load_words<W>(u + off, pu);
-    load_words<W>(delta + off, pd);
-    load_words<W>(dy + off, pg);
-    if (has_z) load_words<W>(z + off, pz);
+    const uint32_t so = (uint32_t)t0 * (uint32_t)sizeof(T);
+    buf_load_words<W>(b_u, voff, so, pu);
+    buf_load_words<W>(b_dl, voff, so, pd);
+    buf_load_words<W>(b_g, voff, so, pg);
+    if (has_z) buf_load_words<W>(b_z, voff, so, pz);
     load_rec(t0, false, prec);
 #pragma unroll
     for (int k = 0; k < NS; ++k)
@@ -460,7 +495,8 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
         }
         zo[e] = e_gz[e] * __builtin_fmaf(D_cc, e_u[e], s);
       }
-      if (valid > 0) store_run<T, E>(dz, eoff, vec_ok, valid, zo);
+      if constexpr (FULL) buf_store_run_nt<T, E>(b_dz, voff, (uint32_t)t0 * (uint32_t)sizeof(T), zo);
+      else if (valid > 0) store_run<T, E>(dz, eoff, vec_ok, valid, zo);
     }
 
     // ---- reverse sweep, in groups of TRS steps ----------------------------------
@@ -544,8 +580,13 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
       }
     }
     if (valid > 0) {
-      store_run<T, E>(du, eoff, vec_ok, valid, e_du);
-      store_run<T, E>(ddelta, eoff, vec_ok, valid, e_dd);
+      if constexpr (FULL) {
+        buf_store_run_nt<T, E>(b_du, voff, (uint32_t)t0 * (uint32_t)sizeof(T), e_du);
+        buf_store_run_nt<T, E>(b_dd, voff, (uint32_t)t0 * (uint32_t)sizeof(T), e_dd);
+      } else {
+        store_run<T, E>(du, eoff, vec_ok, valid, e_du);
+        store_run<T, E>(ddelta, eoff, vec_ok, valid, e_dd);
+      }
     }
   };
 

@@ -185,13 +185,15 @@ bool writes_overlap(const Span (&outs)[NO], const Span (&ins)[NI]) {
   return false;
 }
 
-// The forward scan's vectorised path addresses the rows of a 64-channel group
-// through one buffer descriptor, whose extent must stay below 2^31 bytes
-// (sequences of up to 16M bf16 or 8M float32 steps); longer ones take the
+// The scan kernels' vectorised paths address the rows of a 64-channel group
+// through buffer descriptors with a 32-bit per-lane offset (channel * L +
+// step) * element bytes.  Every lane of the group forms one, also the lanes
+// past dim (whose accesses fall beyond the descriptor's extent and are
+// dropped), so 64 rows must span less than 2^31 bytes whatever dim is:
+// sequences of up to 16M bf16 or 8M float32 steps.  Longer ones take the
 // element-wise path.
-bool group_rows_fit(int dim, int64_t seqlen, size_t es) {
-  const int64_t rows = dim < 64 ? dim : 64;
-  return (long double)rows * (long double)seqlen * (long double)es < (long double)INT32_MAX;
+bool group_rows_fit(int64_t seqlen, size_t es) {
+  return (long double)64 * (long double)seqlen * (long double)es < (long double)INT32_MAX;
 }
 
 // The scan kernels keep step positions in 32 bits.
@@ -370,7 +372,7 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
     a.conv_k = cv->k;
   }
   const bool rows16 = ((int64_t)es * seqlen) % 16 == 0;
-  a.vec = rows16 && group_rows_fit(dim, seqlen, es) && aligned(u, 16) && aligned(delta, 16) &&
+  a.vec = rows16 && group_rows_fit(seqlen, es) && aligned(u, 16) && aligned(delta, 16) &&
           aligned(z, 16) && aligned(y, 16);
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
   a.ncu = device_cu_count();
@@ -598,7 +600,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   f.nseg = sp.nseg;
   f.softplus = (flags & SSM_DELTA_SOFTPLUS) ? 1 : 0;
   f.zoh = (flags & SSM_BBAR_ZOH) ? 1 : 0;
-  f.vec = rows16 && group_rows_fit(dim, seqlen, es) && aligned(u, 16) && aligned(delta, 16);
+  f.vec = rows16 && group_rows_fit(seqlen, es) && aligned(u, 16) && aligned(delta, 16);
   f.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
   f.ncu = device_cu_count();
   f.prio_epochs = prio_epochs();
@@ -640,8 +642,8 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.nseg = sp.nseg;
   a.softplus = f.softplus;
   a.zoh = f.zoh;
-  a.vec = rows16 && aligned(u, 16) && aligned(delta, 16) && aligned(z, 16) && aligned(dy, 16) &&
-          aligned(du, 16) && aligned(ddelta, 16) && aligned(dz, 16);
+  a.vec = rows16 && group_rows_fit(seqlen, es) && aligned(u, 16) && aligned(delta, 16) && aligned(z, 16) &&
+          aligned(dy, 16) && aligned(du, 16) && aligned(ddelta, 16) && aligned(dz, 16);
   a.dtype = f.dtype;
   return ssm::launch_scan_bwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -231,3 +231,17 @@ def test_unaligned_pointers_match_aligned(dev):
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
     assert torch.equal(l0, l1)
+
+
+def test_one_channel_very_long_row(dev):
+    """One channel over 40M bf16 steps.  The lanes of a workgroup address 64
+    rows through one buffer descriptor with 32-bit offsets, also the 63 lanes
+    past the one real channel; 64 such rows would span more than 2^31 bytes,
+    so the scan must take the element path (a wrapped offset of an idle lane
+    would land back inside the real row).  The whole output and state match
+    the oracle."""
+    inp = _case("bf16", b=1, d=1, n=1, L=40_000_000, gate=False, seed=31)
+    y, last = gpu_scan(inp, dev)
+    yr, lr = oracle_scan(inp)
+    assert_parity(y, yr, "bf16")
+    assert_parity(last, lr, "f32", "last_state")
