@@ -46,7 +46,9 @@
  *    h0, last_state, state: (batch, dim, dstate).  Contiguous, no strides.
  *  - Pointers must be aligned to their element size (SSM_ERR_ALIGN
  *    otherwise).  16-byte aligned pointers with rows of a multiple of 16
- *    bytes take the vectorised path; any other legal alignment works, slower.
+ *    bytes take the vectorised path of the scans (when 64 rows span less
+ *    than 2^31 bytes: up to 16M bf16 or 8M float32 steps); any other legal
+ *    alignment or length works, slower.
  *  - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work and return; they never synchronise.  Two calls that write the same
  *    outputs or workspace on different streams race.
