@@ -17,7 +17,9 @@
 //     associative affine step of the NN LAB "Mamba" page, run in reverse.
 //  3. bwd_kernel walks each segment's tiles from last to first: it
 //     recomputes the tile's 16 states from the checkpoint into registers,
-//     then sweeps the steps in reverse, carrying lambda per state and
+//     keeping each step's Abar beside them (the sweep reuses it instead of
+//     a second exponential), then sweeps the steps in reverse, carrying
+//     lambda per state and
 //     forming every gradient term.  dB and dC are sums over channels: each
 //     wave sums its terms over its 64 channels in registers with lane
 //     exchanges (permlane swaps and DPP), a few steps at a time, and writes
@@ -342,6 +344,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   float accD = 0.0f, accBias = 0.0f;
 
   float hist[TL][NS];
+  float ahist[TL][NS];  // Abar of each step and state, kept from the recompute
   // where this lane writes its wave sums of the dB, dC terms (lanes 4o write
   // term o of a group; see the reverse sweep)
   const int so = lane >> 2;
@@ -475,6 +478,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
             else
               h[k] = __builtin_fmaf(a, h[k], v.y * rec_w[t * R + k]);
             hist[t][k] = h[k];
+            ahist[t][k] = a;
             acc = __builtin_fmaf(rec_w[t * R + RNS + k], h[k], acc);
           }
           s_y[g][t][lane] = acc;
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
             const float x2 = v.x * A2[k];
-            const float a = exp2_hw(x2);
+            const float a = ahist[t][k];
             const float lam = __builtin_fmaf(v.z, rec_w[t * R + RNS + k], carry[k]);
             const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hp0[k];
             const float cn = a * lam;  // the carry into step t - 1
