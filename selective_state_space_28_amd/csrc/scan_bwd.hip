@@ -17,10 +17,9 @@
 //     associative affine step of the NN LAB "Mamba" page, run in reverse.
 //  3. bwd_kernel walks each segment's tiles from last to first: it
 //     recomputes the tile's 16 states from the checkpoint into registers,
-//     keeping each step's Abar beside them (the sweep reuses it instead of
-//     a second exponential), then sweeps the steps in reverse, carrying
-//     lambda per state and
-//     forming every gradient term.  dB and dC are sums over channels: each
+//     keeping each step's Abar (and the zero-order-hold coefficient) beside
+//     them so the sweep need not form them again, then sweeps the steps in
+//     reverse, carrying lambda per state and forming every gradient term.  dB and dC are sums over channels: each
 //     wave sums its terms over its 64 channels in registers with lane
 //     exchanges (permlane swaps and DPP), a few steps at a time, and writes
 //     them as per-channel-group partials.  dA, dD and the bias gradient are
@@ -344,7 +343,13 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
   float accD = 0.0f, accBias = 0.0f;
 
   float hist[TL][NS];
-  float ahist[TL][NS];  // Abar of each step and state, kept from the recompute
+  // Abar of each step and state, and the zero-order-hold coefficient, kept
+  // from the recompute for the sweep where the registers allow (few state
+  // groups give long element runs, whose registers leave no room: there the
+  // sweep forms Abar again)
+  constexpr bool KEEP = ZOH || G >= 4;
+  float ahist[KEEP ? TL : 1][KEEP ? NS : 1];
+  float chist[ZOH ? TL : 1][ZOH ? NS : 1];
   // where this lane writes its wave sums of the dB, dC terms (lanes 4o write
   // term o of a group; see the reverse sweep)
   const int so = lane >> 2;
@@ -474,11 +479,15 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
             const float x2 = v.x * A2[k];
             const float a = exp2_hw(x2);
             if constexpr (ZOH)
-              h[k] = __builtin_fmaf(a, h[k], zoh_coef(a, x2, v.x, rA[k]) * (v.w * rec_w[t * R + k]));
+            {
+              const float coef = zoh_coef(a, x2, v.x, rA[k]);
+              chist[ZOH ? t : 0][ZOH ? k : 0] = coef;
+              h[k] = __builtin_fmaf(a, h[k], coef * (v.w * rec_w[t * R + k]));
+            }
             else
               h[k] = __builtin_fmaf(a, h[k], v.y * rec_w[t * R + k]);
             hist[t][k] = h[k];
-            ahist[t][k] = a;
+            if constexpr (KEEP) ahist[t][k] = a;
             acc = __builtin_fmaf(rec_w[t * R + RNS + k], h[k], acc);
           }
           s_y[g][t][lane] = acc;
@@ -522,7 +531,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
 #pragma unroll
           for (int k = 0; k < NS; ++k) {
             const float x2 = v.x * A2[k];
-            const float a = ahist[t][k];
+            const float a = KEEP ? ahist[KEEP ? t : 0][KEEP ? k : 0] : exp2_hw(x2);
             const float lam = __builtin_fmaf(v.z, rec_w[t * R + RNS + k], carry[k]);
             const float hp = t > 0 ? hist[t > 0 ? t - 1 : 0][k] : hp0[k];
             const float cn = a * lam;  // the carry into step t - 1
@@ -530,7 +539,7 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
             dd = __builtin_fmaf(gh, A2[k], dd);
             if constexpr (ZOH) {
               // input term Bbar B u with Bbar = (Abar - 1)/A: dBbar/dDelta = Abar
-              const float coef = zoh_coef(a, x2, v.x, rA[k]);
+              const float coef = chist[ZOH ? t : 0][ZOH ? k : 0];
               const float lB = lam * rec_w[t * R + k];
               dA[k] = __builtin_fmaf(gh, v.x, __builtin_fmaf(lB * v.w, zoh_coef_dA(a, x2, v.x, rA[k]), dA[k]));
               lb = __builtin_fmaf(lB, coef, lb);
