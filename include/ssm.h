@@ -92,7 +92,8 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
 typedef enum {
   SSM_OK = 0,
   SSM_ERR_NULL = -1,      /* a required pointer is NULL                          */
-  SSM_ERR_SHAPE = -2,     /* negative size, dstate not in {1,2,4,8,16}, too large */
+  SSM_ERR_SHAPE = -2,     /* negative size, dstate not in {1,2,4,8,16}, too large
+                             (seqlen above 2^31 - 4097: steps are 32-bit in the kernels) */
   SSM_ERR_DTYPE = -3,     /* dtype not an ssm_dtype_t value                      */
   SSM_ERR_ALIGN = -4,     /* a pointer not aligned to its element size           */
   SSM_ERR_WORKSPACE = -5, /* workspace NULL or smaller than the query's answer   */

@@ -70,6 +70,8 @@ def _upd(**kw):
     (dict(last=P + 0x40), ALIAS), (dict(h0=at(2), last=at(2)), ALIAS),
     (dict(last=at(1) + 64 * 2048 * 2 - 4), ALIAS), (dict(last=at(1) + 64 * 2048 * 2), WS),
     (dict(sp=4), FLAGS), (dict(sp=-1), FLAGS), (dict(sp=8 | 1), FLAGS),
+    # step positions are 32-bit in the kernels: longer sequences are refused
+    (dict(L=(1 << 31) - 4096), SHAPE), (dict(L=1 << 40), SHAPE),
 ])
 def test_scan_validation(kw, code):
     assert _scan(**kw) == code
@@ -83,6 +85,15 @@ def test_scan_workspace_checked_before_launch(monkeypatch):
     # the workspace must not overlap a buffer of the call
     assert _scan(ws=at(1) - 256, wsb=need) == ALIAS
     assert _scan(ws=P, wsb=need) == ALIAS
+
+
+def test_workspace_query_refuses_too_long_sequences():
+    q = load().ssm_scan_fwd_workspace_bytes
+    longest = (1 << 31) - 4097
+    assert q(1, 1, 16, longest, 1) > 0
+    assert q(1, 1, 16, longest + 1, 1) == 0
+    assert load().ssm_scan_bwd_workspace_bytes(1, 1, 16, longest, 1) > 0
+    assert load().ssm_scan_bwd_workspace_bytes(1, 1, 16, longest + 1, 1) == 0
 
 
 def test_empty_problems_need_no_gpu():
