@@ -659,14 +659,28 @@ __global__ __launch_bounds__(256) void reduce_bc_kernel(const float* __restrict_
   Elem<T>::store((w == 0 ? dB : dC) + j, s);
 }
 
-// out[i] = sum_j src[j * n + i], j < terms (dA, dD, d(bias) over batch rows and segments).
-__global__ __launch_bounds__(256) void reduce_terms_kernel(const float* __restrict__ src, float* __restrict__ out,
-                                                           int64_t n, int terms) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.0f;
-  for (int j = 0; j < terms; ++j) s += src[(int64_t)j * n + i];
-  out[i] = s;
+// out[i] = sum_j src[j * n + i], j < terms, for the per-workgroup partials of
+// dA, dD and d(bias) (over batch rows and segments), the three in one launch:
+// thread i takes element i of the concatenated outputs (a NULL output has
+// n = 0 and no elements).
+struct TermSums {
+  const float* src[3];
+  float* out[3];
+  int64_t n[3];
+};
+
+__global__ __launch_bounds__(256) void reduce_terms_kernel(const TermSums t, int terms) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    if (i < t.n[k]) {
+      float s = 0.0f;
+      for (int j = 0; j < terms; ++j) s += t.src[k][(int64_t)j * t.n[k] + i];
+      t.out[k][i] = s;
+      return;
+    }
+    i -= t.n[k];
+  }
 }
 
 template <typename T, int NS, int G>
@@ -706,14 +720,18 @@ static hipError_t launch_bwd_typed(const BwdLaunch& a, hipStream_t stream) {
   reduce_bc_kernel<T><<<(unsigned)((nbc + 255) / 256), 256, 0, stream>>>(
       a.ws_part_bc, static_cast<T*>(a.dB), static_cast<T*>(a.dC), a.batch, s.ncg, N, a.seqlen);
   const int terms = a.batch * a.nseg;
-  const int64_t na = (int64_t)a.dim * N;
-  reduce_terms_kernel<<<(unsigned)((na + 255) / 256), 256, 0, stream>>>(a.ws_part_a, a.dA, na, terms);
-  if (a.dD != nullptr)
-    reduce_terms_kernel<<<(unsigned)((a.dim + 255) / 256), 256, 0, stream>>>(a.ws_part_d, a.dD, a.dim,
-                                                                            terms);
-  if (a.dbias != nullptr)
-    reduce_terms_kernel<<<(unsigned)((a.dim + 255) / 256), 256, 0, stream>>>(a.ws_part_bias, a.dbias,
-                                                                            a.dim, terms);
+  TermSums ts;
+  ts.src[0] = a.ws_part_a;
+  ts.out[0] = a.dA;
+  ts.n[0] = (int64_t)a.dim * N;
+  ts.src[1] = a.ws_part_d;
+  ts.out[1] = a.dD;
+  ts.n[1] = a.dD != nullptr ? a.dim : 0;
+  ts.src[2] = a.ws_part_bias;
+  ts.out[2] = a.dbias;
+  ts.n[2] = a.dbias != nullptr ? a.dim : 0;
+  const int64_t nall = ts.n[0] + ts.n[1] + ts.n[2];
+  reduce_terms_kernel<<<(unsigned)((nall + 255) / 256), 256, 0, stream>>>(ts, terms);
   return hipGetLastError();
 }
 
