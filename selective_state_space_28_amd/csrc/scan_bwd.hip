@@ -390,9 +390,11 @@ __global__ __launch_bounds__(64 * G, ZOH ? 1 : 2) void bwd_kernel(
     buf_load_words<W>(b_g, voff, so, pg);
     if (has_z) buf_load_words<W>(b_z, voff, so, pz);
     load_rec(t0, false, prec);
+    // (non-temporal: each checkpoint is read once, and kept out of L2 it
+    // leaves room for the input lines that the next tiles read again)
 #pragma unroll
     for (int k = 0; k < NS; ++k)
-      pck[k] = dvalid ? ckpt[(((int64_t)b * ntiles + t0 / TL) * N + g * NS + k) * p.dim + d] : 0.0f;
+      pck[k] = dvalid ? __builtin_nontemporal_load(&ckpt[(((int64_t)b * ntiles + t0 / TL) * N + g * NS + k) * p.dim + d]) : 0.0f;
   };
 
   auto tile = [&](auto full_c, int64_t t0, int64_t next) {

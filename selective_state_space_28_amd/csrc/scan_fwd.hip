@@ -586,7 +586,14 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   if (a.nseg > 1) {
     s.nseg_launch = a.nseg - 1;
     const unsigned grid = (unsigned)(base * s.nseg_launch);
-    scan_kernel<T, NS, G, TL, kPassAgg, MODE><<<grid, 64 * G, 0, stream>>>(
+    // the aggregate pass has no readout: with 16 states it takes 32-step
+    // tiles, half the barriers per step (same load blocks, so the same
+    // segment granule)
+    constexpr int TLA = G == 4 ? 2 * TL : TL;
+    static_assert(scan_load_block_tiles((int)sizeof(T), G, TLA) * TLA ==
+                      scan_load_block_tiles((int)sizeof(T), G, TL) * TL,
+                  "the aggregate and main passes share the load-block granule");
+    scan_kernel<T, NS, G, TLA, kPassAgg, MODE><<<grid, 64 * G, 0, stream>>>(
         u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, nullptr,
         s, cv);
   }
