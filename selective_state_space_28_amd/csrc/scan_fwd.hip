@@ -66,7 +66,7 @@ struct ScanSizes {
   int softplus;
   int vec;
   int ncu;           // compute units of the device (blocks launched per "rank")
-  int prio_epochs;   // priority rotations per segment (0: no rotation)
+  int prio_blocks;   // load blocks per wave-priority step (0: no rotation)
   int conv_k;        // convolution width (CONV variants)
 };
 
@@ -322,10 +322,11 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   // CU the oldest ones would race ahead and the youngest run alone at the
   // end, unable to fill the SIMDs.  Blocks are dispatched round-robin over
   // the CUs, so blockIdx / ncu is a block's age rank on its CU; rotating a
-  // raised wave priority over the ranks keeps them progressing together.
+  // raised wave priority over the ranks keeps them progressing together; the
+  // priorities move on every prio_blocks load blocks (every block by default:
+  // the tighter the rotation, the closer together the ranks finish).
   const int prio_rank = (int)(blockIdx.x / (unsigned)p.ncu) % 5;
-  const int nblocks = (seg_end - seg_begin + KT * TL - 1) / (KT * TL);
-  const int epoch_len = p.prio_epochs > 0 ? (nblocks + p.prio_epochs - 1) / p.prio_epochs : 0;
+  const int epoch_len = p.prio_blocks;
 
   // One tile of TL steps.  FAST: a whole tile of a whole load block, its runs
   // already in registers (pu, pd, pz) and its y packed into py; otherwise a
@@ -575,7 +576,7 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   s.softplus = a.softplus;
   s.vec = a.vec;
   s.ncu = a.ncu > 0 ? a.ncu : 1;
-  s.prio_epochs = a.prio_epochs;
+  s.prio_blocks = a.prio_blocks;
   s.conv_k = a.conv_k;
   const ConvArgs cv{a.conv_w, a.conv_b, a.conv_state_in, a.conv_state_out};
   const T* u = static_cast<const T*>(a.u);

@@ -56,7 +56,7 @@ struct ScanLaunch {
   int softplus;
   int vec;                // 16-byte vector loads/stores allowed
   int ncu;                // compute units of the device
-  int prio_epochs;        // wave-priority rotations per segment (0: none)
+  int prio_blocks;        // load blocks per wave-priority step (0: no rotation)
   int zoh;                // zero-order-hold input term (else Euler)
   // convolution prologue (conv_w null: none); u then holds its input x
   const float* conv_w;          // (dim, conv_k)
