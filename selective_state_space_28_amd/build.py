@@ -69,5 +69,23 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+MICROBENCH = os.path.join(PKG, "microbench", "valu_rate.hip")
+
+
+def build_microbench(verbose: bool = False) -> str:
+    """Compile the standalone VALU-rate microbenchmark (microbench/valu_rate.hip)
+    into an executable beside its source."""
+    exe = os.path.splitext(MICROBENCH)[0]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", MICROBENCH, "-o", exe]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {MICROBENCH}:\n{r.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_microbench(verbose="-v" in sys.argv))
