@@ -7,12 +7,15 @@
 //
 //   fma      8 chains of fma: 8 VALU instructions per iteration
 //   exp      8 chains of x = exp2(x) * c: 8 exp + 8 multiplies per iteration
+//   mul      8 chains of multiplies by a scalar (SGPR) or per-lane (VGPR)
+//            factor
 //   scan     the forward scan's recurrence, 4 states and 2 steps per
 //            iteration: per (step, state) a multiply (Delta A log2 e),
 //            exp2, a multiply (Delta u B), the state fma and the readout fma
 //            (B, C, A per state): 46 VALU instructions per iteration in
 //            the compiled loop, 8 of them exp (40 for the 8 (step, state)
-//            updates, the rest forming the step values)
+//            updates, the rest forming the step values); A per lane as in
+//            the kernel, B and C as scalar operands or held in VGPRs
 //
 // Build: hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops valu_rate.hip -o valu_rate
 #include <hip/hip_runtime.h>
@@ -50,12 +53,44 @@ __global__ __launch_bounds__(256) void exp_kernel(float* out, float a, float) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// plain multiplies by a scalar operand (SGPR) or by a per-lane one (VGPR)
+template <bool VGPR>
+__global__ __launch_bounds__(256) void mul_kernel(float* out, float a, float) {
+  float x[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) x[c] = threadIdx.x * 1e-3f + c;
+  float m = a;
+  if constexpr (VGPR) asm volatile("" : "+v"(m));  // keep the factor in a VGPR
+  for (int i = 0; i < kIters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = x[c] * m;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s += x[c];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 struct ScanParams {
   float A2[4], B[4], C[4];
 };
 
+// VGPR_BC: B and C held in VGPRs instead of read as scalar operands
+template <bool VGPR_BC>
 __global__ __launch_bounds__(256) void scan_kernel(float* out, ScanParams p, float) {
   float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc = 0.0f;
+  float A2[4], B[4], C[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    A2[k] = p.A2[k];
+    B[k] = p.B[k];
+    C[k] = p.C[k];
+    asm volatile("" : "+v"(A2[k]));  // per-lane in the scan kernel: a VGPR
+    if constexpr (VGPR_BC) {
+      asm volatile("" : "+v"(B[k]));
+      asm volatile("" : "+v"(C[k]));
+    }
+  }
   float dt = 0.01f + threadIdx.x * 1e-6f, du = 0.5f;
   for (int i = 0; i < kIters; ++i) {
 #pragma unroll
@@ -63,9 +98,9 @@ __global__ __launch_bounds__(256) void scan_kernel(float* out, ScanParams p, flo
       const float d = dt + s * 1e-4f, q = du - s * 1e-4f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float a = __builtin_amdgcn_exp2f(d * p.A2[k]);
-        h[k] = __builtin_fmaf(a, h[k], q * p.B[k]);
-        acc = __builtin_fmaf(p.C[k], h[k], acc);
+        const float a = __builtin_amdgcn_exp2f(d * A2[k]);
+        h[k] = __builtin_fmaf(a, h[k], q * B[k]);
+        acc = __builtin_fmaf(C[k], h[k], acc);
       }
     }
     dt = dt * 0.9999f + 1e-6f;
@@ -107,13 +142,18 @@ int main() {
     const double wave_iters_per_simd = (double)blocks * 4 * kIters / (ncu * 4.0);
     const float t_fma = time_ms(fma_kernel, blocks, out, 0.999f, 1e-3f);
     const float t_exp = time_ms(exp_kernel, blocks, out, 0.999f, 0.0f);
-    const float t_scan = time_ms(scan_kernel, blocks, out, sp, 0.0f);
+    const float t_scan = time_ms(scan_kernel<false>, blocks, out, sp, 0.0f);
+    const float t_scan_v = time_ms(scan_kernel<true>, blocks, out, sp, 0.0f);
+    const float t_mul_s = time_ms(mul_kernel<false>, blocks, out, 0.999f, 0.0f);
+    const float t_mul_v = time_ms(mul_kernel<true>, blocks, out, 0.999f, 0.0f);
     const double r_fma = wave_iters_per_simd * 8 / (t_fma * 1e6);
     const double r_exp = wave_iters_per_simd * 16 / (t_exp * 1e6);
     const double r_scan = wave_iters_per_simd * 46 / (t_scan * 1e6);
-    printf("{\"waves_per_simd\": %d, \"fma\": %.4f, \"exp_mul\": %.4f, \"scan\": %.4f, "
-           "\"scan_element_states_per_simd_ns\": %.3f, \"clock_ghz_from_fma\": %.3f}\n",
-           w, r_fma, r_exp, r_scan, wave_iters_per_simd * 8 * 64 / (t_scan * 1e6), 4.0 * r_fma);
+    printf("{\"waves_per_simd\": %d, \"fma\": %.4f, \"mul_sgpr\": %.4f, \"mul_vgpr\": %.4f, \"exp_mul\": %.4f, "
+           "\"scan\": %.4f, \"scan_element_states_per_simd_ns\": %.3f, \"scan_bc_vgpr_element_states_per_simd_ns\": %.3f, "
+           "\"clock_ghz_from_fma\": %.3f}\n",
+           w, r_fma, wave_iters_per_simd * 8 / (t_mul_s * 1e6), wave_iters_per_simd * 8 / (t_mul_v * 1e6), r_exp, r_scan,
+           wave_iters_per_simd * 8 * 64 / (t_scan * 1e6), wave_iters_per_simd * 8 * 64 / (t_scan_v * 1e6), 4.0 * r_fma);
   }
   hipFree(out);
   return 0;
