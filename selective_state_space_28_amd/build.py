@@ -77,7 +77,8 @@ def build_microbench(verbose: bool = False) -> str:
     into an executable beside its source."""
     exe = os.path.splitext(MICROBENCH)[0]
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", MICROBENCH, "-o", exe]
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
+           MICROBENCH, "-o", exe]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

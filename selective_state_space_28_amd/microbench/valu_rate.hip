@@ -16,8 +16,19 @@
 //            the compiled loop, 8 of them exp (40 for the 8 (step, state)
 //            updates, the rest forming the step values); A per lane as in
 //            the kernel, B and C as scalar operands or held in VGPRs
+//   scan, no input product
+//            the same recurrence with Delta u added to the state unscaled:
+//            the rate the mix would reach if the multiply by B cost nothing
+//   scan, input product on the matrix core
+//            per step one v_mfma_f32_4x4x1_16b_f32 forms the 4 states'
+//            Delta u * B at once (the 16 blocks of 4x4 outer products: lane
+//            l supplies B[l % 4] and its own Delta u, and its 4 result
+//            registers hold Delta u * B[r], r = 0..3)
 //
-// Build: hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops valu_rate.hip -o valu_rate
+// Build: hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops
+//        -mllvm -amdgpu-mfma-vgpr-form valu_rate.hip -o valu_rate
+// (the last option lets the matrix instruction write VGPRs directly, where
+// the default would route its result through AGPRs and VALU moves)
 #include <hip/hip_runtime.h>
 #include <cstdio>
 
@@ -109,6 +120,46 @@ __global__ __launch_bounds__(256) void scan_kernel(float* out, ScanParams p, flo
   out[blockIdx.x * 256 + threadIdx.x] = acc + h[0] + h[1] + h[2] + h[3];
 }
 
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// The recurrence of scan_kernel with B as scalar operands, but the input
+// product Delta u * B either left out (MFMA false: the state takes Delta u
+// itself) or formed on the matrix core (MFMA true)
+template <bool MFMA>
+__global__ __launch_bounds__(256) void scan_input_kernel(float* out, ScanParams p, float) {
+  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, acc = 0.0f;
+  float A2[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    A2[k] = p.A2[k];
+    asm volatile("" : "+v"(A2[k]));
+  }
+  const int q4 = threadIdx.x & 3;
+  float bvec = q4 == 0 ? p.B[0] : q4 == 1 ? p.B[1] : q4 == 2 ? p.B[2] : p.B[3];
+  asm volatile("" : "+v"(bvec));
+  float dt = 0.01f + threadIdx.x * 1e-6f, du = 0.5f;
+  for (int i = 0; i < kIters; ++i) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float d = dt + s * 1e-4f, q = du - s * 1e-4f;
+      float4v qv = {q, q, q, q};
+      if constexpr (MFMA) {
+        const float4v zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        qv = __builtin_amdgcn_mfma_f32_4x4x1f32(bvec, q, zero, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a = __builtin_amdgcn_exp2f(d * A2[k]);
+        h[k] = __builtin_fmaf(a, h[k], qv[k]);
+        acc = __builtin_fmaf(p.C[k], h[k], acc);
+      }
+    }
+    dt = dt * 0.9999f + 1e-6f;
+    du = du * 0.9999f;
+  }
+  out[blockIdx.x * 256 + threadIdx.x] = acc + h[0] + h[1] + h[2] + h[3];
+}
+
 template <typename F, typename P>
 float time_ms(F f, int blocks, float* out, P p, float b) {
   hipEvent_t e0, e1;
@@ -146,14 +197,18 @@ int main() {
     const float t_scan_v = time_ms(scan_kernel<true>, blocks, out, sp, 0.0f);
     const float t_mul_s = time_ms(mul_kernel<false>, blocks, out, 0.999f, 0.0f);
     const float t_mul_v = time_ms(mul_kernel<true>, blocks, out, 0.999f, 0.0f);
+    const float t_noq = time_ms(scan_input_kernel<false>, blocks, out, sp, 0.0f);
+    const float t_mfma = time_ms(scan_input_kernel<true>, blocks, out, sp, 0.0f);
     const double r_fma = wave_iters_per_simd * 8 / (t_fma * 1e6);
     const double r_exp = wave_iters_per_simd * 16 / (t_exp * 1e6);
     const double r_scan = wave_iters_per_simd * 46 / (t_scan * 1e6);
     printf("{\"waves_per_simd\": %d, \"fma\": %.4f, \"mul_sgpr\": %.4f, \"mul_vgpr\": %.4f, \"exp_mul\": %.4f, "
            "\"scan\": %.4f, \"scan_element_states_per_simd_ns\": %.3f, \"scan_bc_vgpr_element_states_per_simd_ns\": %.3f, "
-           "\"clock_ghz_from_fma\": %.3f}\n",
+           "\"scan_no_input_product_element_states_per_simd_ns\": %.3f, "
+           "\"scan_mfma_input_product_element_states_per_simd_ns\": %.3f, \"clock_ghz_from_fma\": %.3f}\n",
            w, r_fma, wave_iters_per_simd * 8 / (t_mul_s * 1e6), wave_iters_per_simd * 8 / (t_mul_v * 1e6), r_exp, r_scan,
-           wave_iters_per_simd * 8 * 64 / (t_scan * 1e6), wave_iters_per_simd * 8 * 64 / (t_scan_v * 1e6), 4.0 * r_fma);
+           wave_iters_per_simd * 8 * 64 / (t_scan * 1e6), wave_iters_per_simd * 8 * 64 / (t_scan_v * 1e6),
+           wave_iters_per_simd * 8 * 64 / (t_noq * 1e6), wave_iters_per_simd * 8 * 64 / (t_mfma * 1e6), 4.0 * r_fma);
   }
   hipFree(out);
   return 0;
