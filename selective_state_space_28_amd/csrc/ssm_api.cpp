@@ -332,11 +332,16 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
     const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
     const size_t bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
     const size_t state = (size_t)batch * (size_t)dim * (size_t)dstate * sizeof(float);
+    const size_t ck = cv != nullptr && cv->k > 1 ? (size_t)batch * (size_t)dim * (size_t)(cv->k - 1) * 4 : 0;
     const Span outs[] = {span(workspace, wl.total)};
     const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(B, bc), span(C, bc),
                         span(A, (size_t)dim * (size_t)dstate * 4), span(D_skip, (size_t)dim * 4),
                         span(delta_bias, (size_t)dim * 4), span(h0, state), span(y, tok),
-                        span(last_state, state)};
+                        span(last_state, state),
+                        span(cv != nullptr ? cv->w : nullptr, cv != nullptr ? (size_t)dim * (size_t)cv->k * 4 : 0),
+                        span(cv != nullptr ? cv->b : nullptr, cv != nullptr ? (size_t)dim * 4 : 0),
+                        span(cv != nullptr ? cv->state_in : nullptr, ck),
+                        span(cv != nullptr ? cv->state_out : nullptr, ck)};
     if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
   }
 

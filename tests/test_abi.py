@@ -182,6 +182,12 @@ def test_conv_scan_validation(kw, code):
 def test_conv_scan_workspace_checked_before_launch():
     assert _cscan(ws=None, wsb=0) == WS
     assert _cscan(batch=0) == OK
+    # the workspace must not overlap the taps, the bias or the carried inputs
+    need = load().ssm_scan_fwd_workspace_bytes(1, 64, 16, 2048, 1)
+    assert _cscan(ws=at(2), wsb=need) == ALIAS
+    assert _cscan(cb=at(3) + 512, ws=at(3), wsb=need) == ALIAS
+    assert _cscan(sin=at(3) + 1024, ws=at(3), wsb=need) == ALIAS
+    assert _cscan(sout=at(3) + need - 4, ws=at(3), wsb=need) == ALIAS
 
 
 @pytest.mark.parametrize("kw,code", [
