@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
-SOURCES = ["scan_fwd.hip", "scan_bwd.hip", "ssd.hip", "state_update.hip", "ssm_api.cpp"]
+SOURCES = ["scan_fwd.hip", "scan_wave.hip", "scan_bwd.hip", "ssd.hip", "state_update.hip", "ssm_api.cpp"]
 ARCH = "gfx950"
 # Per-source options.  The backward sweep runs two waves per SIMD, so the
 # scheduler that favours instruction-level parallelism hides more of its

@@ -55,6 +55,7 @@ struct ScanLaunch {
   int nseg;               // segments the sequence is split into
   int softplus;
   int vec;                // 16-byte vector loads/stores allowed
+  int vec_bc;             // B and C rows 16-byte aligned (time-parallel kernel)
   int ncu;                // compute units of the device
   int prio_blocks;        // load blocks per wave-priority step (0: no rotation)
   int zoh;                // zero-order-hold input term (else Euler)
@@ -167,6 +168,10 @@ struct SsdLaunch {
 };
 
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream);
+// The time-parallel forward scan for long sequences with few channels
+// (scan_wave.hip): N = 16, no convolution prologue, no checkpoints; it reads
+// B and C directly and needs no workspace.
+hipError_t launch_scan_wave(const ScanLaunch& a, hipStream_t stream);
 hipError_t launch_ssd_fwd(const SsdLaunch& a, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdLaunch& a, hipStream_t stream);
 hipError_t launch_state_update(const DecodeLaunch& a, hipStream_t stream);

@@ -46,6 +46,15 @@ def _plant(arr, dtype, idx, value):
         arr[idx] = value
 
 
+def _path(monkeypatch, segs):
+    """None: the plan's own path; an integer: that many segments; "wave": the
+    time-parallel kernel."""
+    if segs == "wave":
+        monkeypatch.setenv("SSM_SCAN_WAVE", "1")
+    elif segs is not None:
+        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+
+
 def _same_nonfinite(got, ref, what):
     """NaN exactly where ref has NaN; +-Inf exactly where ref has +-Inf; the
     finite rest within tolerance of the finite rest of ref."""
@@ -76,10 +85,9 @@ PLANTS = [  # (array, (b, d, t), value)
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bbar", ["euler", "zoh"])
-@pytest.mark.parametrize("segs", [None, 3])
+@pytest.mark.parametrize("segs", [None, 3, "wave"])
 def test_scan_nan_inf_propagate(dev, dtype, bbar, segs, monkeypatch):
-    if segs is not None:
-        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+    _path(monkeypatch, segs)
     cfg = ScanConfig("naninf", 2, 130, 16, 300, dtype, seed=21, a_jitter=0.1)
     inp = synth.make_scan_inputs(cfg)
     for key, idx, v in PLANTS:
@@ -108,10 +116,9 @@ PLANTS_BC = [  # (array, (b, n, t), value)
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bbar", ["euler", "zoh"])
-@pytest.mark.parametrize("segs", [None, 3])
+@pytest.mark.parametrize("segs", [None, 3, "wave"])
 def test_scan_nan_inf_in_B_C(dev, dtype, bbar, segs, monkeypatch):
-    if segs is not None:
-        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+    _path(monkeypatch, segs)
     cfg = ScanConfig("naninf-bc", 2, 130, 16, 300, dtype, seed=24, a_jitter=0.1)
     inp = synth.make_scan_inputs(cfg)
     for key, idx, v in PLANTS_BC:
@@ -163,12 +170,11 @@ def test_decode_nan_inf_propagate(dev, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bbar", ["euler", "zoh"])
-@pytest.mark.parametrize("segs", [None, 4])
+@pytest.mark.parametrize("segs", [None, 4, "wave"])
 def test_positive_A_grows(dev, dtype, bbar, segs, monkeypatch):
     """A > 0: every state of every channel grows; the GPU still matches the
     oracle (tolerance relative to the largest output, as everywhere)."""
-    if segs is not None:
-        monkeypatch.setenv("SSM_SCAN_SEGMENTS", str(segs))
+    _path(monkeypatch, segs)
     cfg = ScanConfig("growth", 2, 70, 16, 400, dtype, seed=23)
     inp = synth.make_scan_inputs(cfg)
     inp["A"] = (0.02 * (1 + np.arange(16, dtype=np.float32)))[None, :].repeat(70, 0)
