@@ -379,7 +379,47 @@ def main():
         out["bwd_zoh"] = {"workload": "ssm_scan_bwd of the same scan with the zero-order-hold input term",
                           "steps": nb, "ms_per_step": ms_bz, "value": elements / (ms_bz * 1e-3),
                           "unit": "elements/s"}
-        del gy, bws
+        del bws
+
+        # the training pair: the forward writes the tile checkpoints beside y
+        # and the backward starts from them (no checkpoint pass of its own)
+        ck = torch.empty((cfg.batch, (cfg.seqlen + 15) // 16, cfg.dstate, cfg.dim), dtype=torch.float32,
+                         device=dev)
+        cws = torch.empty(max(1, ssm.ssm_scan_bwd_ckpt_workspace_bytes(cfg.batch, cfg.dim, cfg.dstate,
+                                                                       cfg.seqlen, u.dtype)),
+                          dtype=torch.uint8, device=dev)
+        train = {"workload": "one training step of the same scan: forward then backward "
+                             "(Euler input term unless named)", "steps": nb}
+        for bbar in ("euler", "zoh"):
+            sfx = "" if bbar == "euler" else "_zoh"
+
+            def step_fwd_ckpt():
+                ssm.ssm_scan_fwd_ckpt(u, delta, A, B, C, D, z, bias, out=y, ckpt=ck, workspace=ws,
+                                      bbar=bbar)
+
+            def step_bwd_ckpt():
+                ssm.ssm_scan_bwd_ckpt(u, delta, A, B, C, D, z, bias, ckpt=ck, dy=gy, workspace=cws,
+                                      bbar=bbar)
+
+            def step_train():
+                step_fwd_ckpt()
+                step_bwd_ckpt()
+
+            for name, fn, n in (("fwd_ckpt", step_fwd_ckpt, args.steps), ("bwd_ckpt", step_bwd_ckpt, nb),
+                                ("fwd_plus_bwd_ckpt", step_train, nb)):
+                fn()
+                settle(fn, dev, args.settle_ms)
+                ms_t, _ = timed(fn, dev, stream, n)
+                train[name + sfx + "_ms"] = ms_t
+            fwd_ms = ms if bbar == "euler" else ms_z
+            bwd_ms = ms_b if bbar == "euler" else ms_bz
+            train["fwd_plus_bwd_plain" + sfx + "_ms"] = fwd_ms + bwd_ms
+        train["note"] = ("fwd_ckpt: ssm_scan_fwd_ckpt (y, last_state and the tile checkpoints); bwd_ckpt: "
+                         "ssm_scan_bwd_ckpt from them; fwd_plus_bwd_ckpt: the two timed back to back; "
+                         "fwd_plus_bwd_plain: ssm_scan_fwd + ssm_scan_bwd (the latter running its own "
+                         "checkpoint pass), the sum of their timings above")
+        out["train"] = train
+        del gy, ck, cws
     del u, delta, B, C, z, y, ws
 
     if not args.no_split:

@@ -303,6 +303,71 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ssm_scan_ckpt_bytes -- bytes of the tile checkpoints of a scan: the state
+ * entering every 16-step tile, (batch, ceil(seqlen/16), dstate, dim) float32
+ * (tile j holds h_{16j-1}, the zero or h0 state for j = 0).  Pure host
+ * function; 0 for an empty problem and for a dstate or size ssm_scan_fwd
+ * would reject.
+ */
+size_t ssm_scan_ckpt_bytes(int batch, int dim, int dstate, int64_t seqlen);
+
+/*
+ * ssm_scan_fwd_ckpt -- ssm_scan_fwd for a training step: besides y and
+ * last_state it writes the tile checkpoints, which ssm_scan_bwd_ckpt then
+ * starts from instead of running the states forward again.  The backward
+ * still recomputes every state inside a tile from that tile's checkpoint
+ * ("Mamba" paper review, "Optimization": intermediate states recomputed for
+ * backpropagation rather than stored); only one state in 16 is kept.
+ *
+ *   ckpt         out  at least ssm_scan_ckpt_bytes(...) bytes, 4-byte
+ *                     aligned, owned by the caller            required when
+ *                     the query is above 0 (SSM_ERR_NULL; too small:
+ *                     SSM_ERR_WORKSPACE); must not overlap any other buffer
+ *                     of the call (SSM_ERR_ALIAS)
+ *   every other argument, result and error as for ssm_scan_fwd (the same
+ *   workspace query); y and last_state carry the same bits as ssm_scan_fwd's.
+ */
+int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D_skip, const void* z,
+                      const float* delta_bias, int flags, const float* h0, void* y,
+                      float* last_state, float* ckpt, size_t ckpt_bytes, int batch, int dim,
+                      int dstate, int64_t seqlen, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_scan_bwd_ckpt_workspace_bytes -- bytes of device workspace
+ * ssm_scan_bwd_ckpt needs: ssm_scan_bwd's without the checkpoint region.
+ * Pure host function; 0 for an empty problem and for arguments
+ * ssm_scan_bwd_ckpt would reject.
+ */
+size_t ssm_scan_bwd_ckpt_workspace_bytes(int batch, int dim, int dstate, int64_t seqlen,
+                                         int dtype);
+
+/*
+ * ssm_scan_bwd_ckpt -- ssm_scan_bwd starting from the tile checkpoints that
+ * ssm_scan_fwd_ckpt wrote for the same inputs, flags and h0, so the forward
+ * checkpoint pass is skipped.  Given those checkpoints every gradient
+ * carries the same bits as ssm_scan_bwd's.
+ *
+ *   ckpt         in   the checkpoints, ssm_scan_ckpt_bytes(...) bytes or more,
+ *                     4-byte aligned                            required when
+ *                     the query is above 0 (SSM_ERR_NULL; too small:
+ *                     SSM_ERR_WORKSPACE); no output or the workspace may
+ *                     overlap it (SSM_ERR_ALIAS)
+ *   workspace    at least ssm_scan_bwd_ckpt_workspace_bytes(...) bytes,
+ *                256-byte aligned, owned by the caller
+ *   every other argument, result and error as for ssm_scan_bwd.
+ */
+int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D_skip, const void* z,
+                      const float* delta_bias, int flags, const float* h0, const float* ckpt,
+                      size_t ckpt_bytes, const void* dy, const float* dlast_state, void* du,
+                      void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                      float* ddelta_bias, float* dh0, int batch, int dim, int dstate,
+                      int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * ssm_ssd_scan_fwd -- the SSD (Mamba-2) form: the same recurrence with a
  * scalar A per head, computed by chunks on the matrix cores.  The dim =
  * nheads * headdim channels form heads of headdim consecutive channels;

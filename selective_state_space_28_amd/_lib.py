@@ -56,6 +56,17 @@ def load():
     lib.ssm_scan_bwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, vp, vp, fp, vp,
                                  vp, fp, vp, fp, fp, i32, i32, i32, i64, i32, vp, sz, vp]
     lib.ssm_scan_bwd.restype = i32
+    lib.ssm_scan_ckpt_bytes.argtypes = [i32, i32, i32, i64]
+    lib.ssm_scan_ckpt_bytes.restype = sz
+    lib.ssm_scan_fwd_ckpt.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, fp, sz,
+                                      i32, i32, i32, i64, i32, vp, sz, vp]
+    lib.ssm_scan_fwd_ckpt.restype = i32
+    lib.ssm_scan_bwd_ckpt_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
+    lib.ssm_scan_bwd_ckpt_workspace_bytes.restype = sz
+    lib.ssm_scan_bwd_ckpt.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, fp, sz, vp, fp, vp,
+                                      vp, fp, vp, vp, fp, vp, fp, fp, i32, i32, i32, i64, i32, vp,
+                                      sz, vp]
+    lib.ssm_scan_bwd_ckpt.restype = i32
     lib.ssm_ssd_scan_fwd.argtypes = [vp, vp, fp, vp, vp, fp, vp, fp, i32, fp, vp, fp, i32, i32, i32,
                                      i32, i64, i32, vp, sz, vp]
     lib.ssm_ssd_scan_fwd_workspace_bytes.argtypes = [i32, i32, i64, i32]

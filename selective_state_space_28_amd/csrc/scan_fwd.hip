@@ -145,7 +145,8 @@ __device__ __forceinline__ float input_term(float a, float x2, float dt, float q
 // PASS: kPassMain computes y (and last_state); kPassAgg runs every segment
 // but the last from a zero state and records its end state and Delta sum;
 // kPassCkpt runs like the main pass but, instead of y, records the state
-// entering every tile (the checkpoints the backward pass starts from).
+// entering every tile (the checkpoints the backward pass starts from);
+// kPassMainCkpt computes y and records the checkpoints too.
 template <typename T, int NS, int G, int TL, int PASS, int MODE>
 __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     float* __restrict__ last_state, float* __restrict__ ws_hend, float* __restrict__ ws_sumdt,
     float* __restrict__ ws_ckpt, const ScanSizes p, const ConvArgs cv) {
   constexpr bool AGG = PASS == kPassAgg;
-  constexpr bool READOUT = PASS == kPassMain;
-  constexpr bool CKPT = PASS == kPassCkpt;
+  constexpr bool READOUT = PASS == kPassMain || PASS == kPassMainCkpt;
+  constexpr bool CKPT = PASS == kPassCkpt || PASS == kPassMainCkpt;
   constexpr bool ZOH = (MODE & kModeZoh) != 0;
   constexpr bool CONV = (MODE & kModeConv) != 0;
   constexpr int N = NS * G;
@@ -603,6 +604,12 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   s.nseg_launch = a.nseg;
   const unsigned grid = (unsigned)(base * s.nseg_launch);
   if constexpr ((MODE & kModeConv) == 0) {  // the backward pass covers both input terms, no prologue
+    if (a.ws_ckpt != nullptr && a.ckpt_with_y) {
+      scan_kernel<T, NS, G, TL, kPassMainCkpt, MODE><<<grid, 64 * G, 0, stream>>>(
+          u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt,
+          a.ws_ckpt, s, cv);
+      return hipGetLastError();
+    }
     if (a.ws_ckpt != nullptr) {
       scan_kernel<T, NS, G, TL, kPassCkpt, MODE><<<grid, 64 * G, 0, stream>>>(
           u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt,
@@ -613,6 +620,27 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   scan_kernel<T, NS, G, TL, kPassMain, MODE><<<grid, 64 * G, 0, stream>>>(
       u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, nullptr,
       s, cv);
+  return hipGetLastError();
+}
+
+template <typename T, int NS, int G>
+static void pack_only(const ScanLaunch& a, hipStream_t stream) {
+  const int tblocks = (int)((a.seqlen + 255) / 256);
+  pack_bc_kernel<T, NS, G><<<(unsigned)((int64_t)a.batch * tblocks), 256, 0, stream>>>(
+      static_cast<const T*>(a.B), static_cast<const T*>(a.C), static_cast<T*>(a.ws_bc), a.seqlen,
+      tblocks);
+}
+
+template <typename T>
+static hipError_t pack_by_state(const ScanLaunch& a, hipStream_t stream) {
+  switch (a.dstate) {
+    case 1: pack_only<T, 1, 1>(a, stream); break;
+    case 2: pack_only<T, 2, 1>(a, stream); break;
+    case 4: pack_only<T, 4, 1>(a, stream); break;
+    case 8: pack_only<T, 4, 2>(a, stream); break;
+    case 16: pack_only<T, 4, 4>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -644,6 +672,11 @@ hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream) {
   if (a.conv_w != nullptr && (a.conv_k < 1 || a.conv_k > kMaxConvWidth)) return hipErrorInvalidValue;
   if (a.ws_ckpt != nullptr && a.conv_w != nullptr) return hipErrorInvalidValue;
   return a.dtype == Dtype::BF16 ? launch_by_mode<uint16_t>(a, stream) : launch_by_mode<float>(a, stream);
+}
+
+hipError_t launch_pack_records(const ScanLaunch& a, hipStream_t stream) {
+  if (a.batch == 0 || a.seqlen == 0) return hipSuccess;
+  return a.dtype == Dtype::BF16 ? pack_by_state<uint16_t>(a, stream) : pack_by_state<float>(a, stream);
 }
 
 __global__ void fill_state_kernel(float* __restrict__ dst, const float* __restrict__ src, int64_t n) {

@@ -140,16 +140,25 @@ struct BwdWsLayout {
   size_t ckpt, lagg, lsum, part_bc, part_a, part_d, part_bias, total;
 };
 
-BwdWsLayout bwd_workspace_layout(int batch, int dim, int dstate, int64_t L, int dtype, const SegPlan& sp) {
+// Bytes of the tile checkpoints: the state entering every kScanTile-step tile,
+// (batch, ntiles, dstate, dim) float32.
+size_t ckpt_bytes_of(int batch, int dim, int dstate, int64_t L) {
+  const size_t ntiles = (size_t)((L + ssm::kScanTile - 1) / ssm::kScanTile);
+  return (size_t)batch * ntiles * (size_t)dstate * (size_t)dim * sizeof(float);
+}
+
+// with_ckpt false: the checkpoints come from the caller (the forward pass
+// wrote them), so the workspace holds no region for them.
+BwdWsLayout bwd_workspace_layout(int batch, int dim, int dstate, int64_t L, int dtype, const SegPlan& sp,
+                                 bool with_ckpt = true) {
   BwdWsLayout w{};
   w.fwd = workspace_layout(batch, dim, dstate, L, dtype, sp);
   const size_t plane = (size_t)batch * (size_t)dim;
-  const size_t ntiles = (size_t)((L + ssm::kScanTile - 1) / ssm::kScanTile);
   const size_t ncg = (size_t)((dim + 63) / 64);
   const size_t segs = (size_t)sp.nseg;
   size_t off = round256(w.fwd.total);
   w.ckpt = off;
-  off += round256((size_t)batch * ntiles * (size_t)dstate * (size_t)dim * sizeof(float));
+  if (with_ckpt) off += round256(ckpt_bytes_of(batch, dim, dstate, L));
   w.lagg = off;
   off += round256((segs - 1) * plane * (size_t)dstate * sizeof(float));
   w.lsum = off;
@@ -279,7 +288,8 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
               const float* D_skip, const void* z, const float* delta_bias, int flags,
               const float* h0, void* y, float* last_state, int batch, int dim, int dstate,
               int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes, void* stream,
-              const ConvIn* cv, bool use_scratch = false) {
+              const ConvIn* cv, bool use_scratch = false, bool want_ckpt = false,
+              float* ckpt = nullptr, size_t ckpt_bytes = 0) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return SSM_ERR_SHAPE;
@@ -291,11 +301,15 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
   if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) ||
       !aligned(z, es) || !aligned(y, es) || !aligned(A, 4) || !aligned(D_skip, 4) ||
       !aligned(delta_bias, 4) || !aligned(h0, 4) || !aligned(last_state, 4) ||
-      !aligned(workspace, 256))
+      !aligned(workspace, 256) || !aligned(ckpt, 4))
     return SSM_ERR_ALIGN;
   if (!conv_aligned(cv)) return SSM_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (empty) return SSM_OK;
+  // the checkpoints: every tile's entering state, so none for an empty sequence
+  const size_t ckb = want_ckpt ? ckpt_bytes_of(batch, dim, dstate, seqlen) : 0;
+  if (ckb > 0 && ckpt == nullptr) return SSM_ERR_NULL;
+  if (ckb > 0 && ckpt_bytes < ckb) return SSM_ERR_WORKSPACE;
   {
     const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
     const size_t bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
@@ -304,7 +318,7 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
     const size_t ck = cv != nullptr && cv->k > 1 ? (size_t)batch * (size_t)dim * (size_t)(cv->k - 1) * 4 : 0;
     const size_t cw = cv != nullptr ? (size_t)dim * (size_t)cv->k * 4 : 0;
     const Span outs[] = {span(y, tok), span(last_state, state),
-                         span(cv != nullptr ? cv->state_out : nullptr, ck)};
+                         span(cv != nullptr ? cv->state_out : nullptr, ck), span(ckpt, ckb)};
     const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(B, bc), span(C, bc),
                         span(A, per_dim * (size_t)dstate), span(D_skip, per_dim),
                         span(delta_bias, per_dim), span(h0, state),
@@ -353,7 +367,7 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
                         span(cv != nullptr ? cv->w : nullptr, cv != nullptr ? (size_t)dim * (size_t)cv->k * 4 : 0),
                         span(cv != nullptr ? cv->b : nullptr, cv != nullptr ? (size_t)dim * 4 : 0),
                         span(cv != nullptr ? cv->state_in : nullptr, ck),
-                        span(cv != nullptr ? cv->state_out : nullptr, ck)};
+                        span(cv != nullptr ? cv->state_out : nullptr, ck), span(ckpt, ckb)};
     if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
   }
 
@@ -397,6 +411,11 @@ int scan_impl(const void* u, const void* delta, const float* A, const void* B, c
   a.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
   a.ncu = device_cu_count();
   a.prio_blocks = prio_blocks();
+  if (ckb > 0) {
+    a.ws_ckpt = ckpt;
+    a.ckpt_with_y = 1;
+    return ssm::launch_scan_fwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
   if (use_wave_kernel(dstate, cv != nullptr))
     return ssm::launch_scan_wave(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   return ssm::launch_scan_fwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
@@ -527,12 +546,16 @@ size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int dstate, int64_t seql
       .total;
 }
 
-int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                 const float* D_skip, const void* z, const float* delta_bias, int flags,
-                 const float* h0, const void* dy, const float* dlast_state, void* du, void* ddelta,
-                 float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
-                 float* dh0, int batch, int dim, int dstate, int64_t seqlen, int dtype,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+// ckpt_given: the checkpoints come from the caller (ckpt_in, written by
+// ssm_scan_fwd_ckpt), so the forward checkpoint pass is skipped and only the
+// B, C records are packed.
+static int bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                    const float* D_skip, const void* z, const float* delta_bias, int flags,
+                    const float* h0, const void* dy, const float* dlast_state, void* du, void* ddelta,
+                    float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                    float* dh0, int batch, int dim, int dstate, int64_t seqlen, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream, bool ckpt_given,
+                    const float* ckpt_in, size_t ckpt_bytes) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (!flags_ok(flags)) return SSM_ERR_FLAGS;
   if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return SSM_ERR_SHAPE;
@@ -547,10 +570,13 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
       !aligned(dB, es) || !aligned(dC, es) || !aligned(dz, es) || !aligned(A, 4) ||
       !aligned(D_skip, 4) || !aligned(delta_bias, 4) || !aligned(h0, 4) || !aligned(dlast_state, 4) ||
       !aligned(dA, 4) || !aligned(dD, 4) || !aligned(ddelta_bias, 4) || !aligned(dh0, 4) ||
-      !aligned(workspace, 256))
+      !aligned(workspace, 256) || !aligned(ckpt_in, 4))
     return SSM_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (empty) return SSM_OK;
+  const size_t ckb = ckpt_given ? ckpt_bytes_of(batch, dim, dstate, seqlen) : 0;
+  if (ckb > 0 && ckpt_in == nullptr) return SSM_ERR_NULL;
+  if (ckb > 0 && ckpt_bytes < ckb) return SSM_ERR_WORKSPACE;
   {
     const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
     const size_t bc = (size_t)batch * (size_t)dstate * (size_t)seqlen * es;
@@ -561,7 +587,8 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                          span(ddelta_bias, per_dim), span(dh0, state)};
     const Span ins[] = {span(u, tok), span(delta, tok), span(z, tok), span(dy, tok), span(B, bc),
                         span(C, bc), span(A, per_dim * (size_t)dstate), span(D_skip, per_dim),
-                        span(delta_bias, per_dim), span(h0, state), span(dlast_state, state)};
+                        span(delta_bias, per_dim), span(h0, state), span(dlast_state, state),
+                        span(ckpt_in, ckb)};
     if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
   }
 
@@ -580,7 +607,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   const int64_t pack_blocks = (int64_t)batch * ((seqlen + 255) / 256);
   const int64_t red_blocks = (2 * (int64_t)batch * dstate * seqlen + 255) / 256;
   if (blocks > INT_MAX || pack_blocks > INT_MAX || red_blocks > INT_MAX) return SSM_ERR_SHAPE;
-  const BwdWsLayout wl = bwd_workspace_layout(batch, dim, dstate, seqlen, dtype, sp);
+  const BwdWsLayout wl = bwd_workspace_layout(batch, dim, dstate, seqlen, dtype, sp, !ckpt_given);
   if (workspace == nullptr || workspace_bytes < wl.total) return SSM_ERR_WORKSPACE;
   {
     const size_t tok = (size_t)batch * (size_t)dim * (size_t)seqlen * es;
@@ -593,7 +620,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                         span(delta_bias, per_dim), span(h0, state), span(dlast_state, state),
                         span(du, tok), span(ddelta, tok), span(dz, tok), span(dB, bc), span(dC, bc),
                         span(dA, per_dim * (size_t)dstate), span(dD, per_dim),
-                        span(ddelta_bias, per_dim), span(dh0, state)};
+                        span(ddelta_bias, per_dim), span(dh0, state), span(ckpt_in, ckb)};
     if (writes_overlap(outs, ins)) return SSM_ERR_ALIAS;
   }
   char* ws = static_cast<char*>(workspace);
@@ -626,8 +653,12 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   f.dtype = dtype == SSM_BF16 ? Dtype::BF16 : Dtype::F32;
   f.ncu = device_cu_count();
   f.prio_blocks = prio_blocks();
-  f.ws_ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
-  if (ssm::launch_scan_fwd(f, st) != hipSuccess) return SSM_ERR_HIP;
+  if (ckpt_given) {
+    if (ssm::launch_pack_records(f, st) != hipSuccess) return SSM_ERR_HIP;
+  } else {
+    f.ws_ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
+    if (ssm::launch_scan_fwd(f, st) != hipSuccess) return SSM_ERR_HIP;
+  }
 
   // 2-4. reverse aggregates, the backward sweep, the sums of the partials
   ssm::BwdLaunch a{};
@@ -649,7 +680,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.dD = dD;
   a.dbias = ddelta_bias;
   a.ws_bc = ws + wl.fwd.bc;
-  a.ws_ckpt = reinterpret_cast<const float*>(ws + wl.ckpt);
+  a.ws_ckpt = ckpt_given ? ckpt_in : reinterpret_cast<const float*>(ws + wl.ckpt);
   a.ws_lagg = reinterpret_cast<float*>(ws + wl.lagg);
   a.ws_lsum = reinterpret_cast<float*>(ws + wl.lsum);
   a.ws_part_bc = reinterpret_cast<float*>(ws + wl.part_bc);
@@ -668,6 +699,53 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
           aligned(dy, 16) && aligned(du, 16) && aligned(ddelta, 16) && aligned(dz, 16);
   a.dtype = f.dtype;
   return ssm::launch_scan_bwd(a, st) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                 const float* D_skip, const void* z, const float* delta_bias, int flags,
+                 const float* h0, const void* dy, const float* dlast_state, void* du, void* ddelta,
+                 float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                 float* dh0, int batch, int dim, int dstate, int64_t seqlen, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(u, delta, A, B, C, D_skip, z, delta_bias, flags, h0, dy, dlast_state, du, ddelta,
+                  dA, dB, dC, dD, dz, ddelta_bias, dh0, batch, dim, dstate, seqlen, dtype, workspace,
+                  workspace_bytes, stream, false, nullptr, 0);
+}
+
+size_t ssm_scan_ckpt_bytes(int batch, int dim, int dstate, int64_t seqlen) {
+  if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return 0;
+  return ckpt_bytes_of(batch, dim, dstate, seqlen);
+}
+
+int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D_skip, const void* z, const float* delta_bias, int flags,
+                      const float* h0, void* y, float* last_state, float* ckpt, size_t ckpt_bytes,
+                      int batch, int dim, int dstate, int64_t seqlen, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return scan_impl(u, delta, A, B, C, D_skip, z, delta_bias, flags, h0, y, last_state, batch, dim,
+                   dstate, seqlen, dtype, workspace, workspace_bytes, stream, nullptr, false, true, ckpt,
+                   ckpt_bytes);
+}
+
+size_t ssm_scan_bwd_ckpt_workspace_bytes(int batch, int dim, int dstate, int64_t seqlen, int dtype) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return 0;
+  if (!dstate_ok(dstate) || !shapes_fit(batch, dim, seqlen)) return 0;
+  if (batch == 0 || dim == 0 || seqlen == 0) return 0;
+  return bwd_workspace_layout(batch, dim, dstate, seqlen, dtype,
+                              plan_segments(batch, dim, dstate, seqlen, dtype), false)
+      .total;
+}
+
+int ssm_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                      const float* D_skip, const void* z, const float* delta_bias, int flags,
+                      const float* h0, const float* ckpt, size_t ckpt_bytes, const void* dy,
+                      const float* dlast_state, void* du, void* ddelta, float* dA, void* dB, void* dC,
+                      float* dD, void* dz, float* ddelta_bias, float* dh0, int batch, int dim,
+                      int dstate, int64_t seqlen, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return bwd_impl(u, delta, A, B, C, D_skip, z, delta_bias, flags, h0, dy, dlast_state, du, ddelta,
+                  dA, dB, dC, dD, dz, ddelta_bias, dh0, batch, dim, dstate, seqlen, dtype, workspace,
+                  workspace_bytes, stream, true, ckpt, ckpt_bytes);
 }
 
 size_t ssm_ssd_scan_fwd_workspace_bytes(int batch, int dstate, int64_t seqlen, int dtype) {

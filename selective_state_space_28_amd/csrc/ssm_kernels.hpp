@@ -29,6 +29,7 @@ enum class Dtype { F32 = 0, BF16 = 1 };
 constexpr int kPassMain = 0;  // y and last_state
 constexpr int kPassAgg = 1;   // segment aggregates (end state from zero, Delta sum)
 constexpr int kPassCkpt = 2;  // the state entering every tile, for the backward pass
+constexpr int kPassMainCkpt = 3;  // y and last_state, and the state entering every tile
 
 // Kernel variants (bits of the MODE template argument).
 constexpr int kModeZoh = 1;   // zero-order-hold input term (else Euler)
@@ -65,8 +66,11 @@ struct ScanLaunch {
   const float* conv_state_in;   // (batch, dim, conv_k-1) nullable
   float* conv_state_out;        // (batch, dim, conv_k-1) nullable
   int conv_k;                   // 1..4
-  // checkpoint pass instead of the main pass (backward): (batch, ntiles, N, dim)
+  // checkpoints, the state entering every tile: (batch, ntiles, N, dim).  With
+  // ckpt_with_y the main pass writes them beside y (a forward pass whose
+  // backward follows); otherwise a checkpoint pass replaces the main pass.
   float* ws_ckpt;
+  int ckpt_with_y;
   Dtype dtype;
 };
 
@@ -96,9 +100,11 @@ struct DecodeLaunch {
 // Widest convolution the kernels take.
 constexpr int kMaxConvWidth = 4;
 
-// Backward pass (Euler input term, no convolution prologue).  The caller has
-// already run the forward checkpoint pass (launch_scan_fwd with ws_ckpt),
-// which also packs the B, C records into ws_bc.
+// Backward pass (either input term, no convolution prologue).  The caller has
+// already put the checkpoints in ws_ckpt and the B, C records in ws_bc: by the
+// forward checkpoint pass (launch_scan_fwd with ws_ckpt, which packs the
+// records too), or by a forward pass that wrote the checkpoints beside y,
+// followed by launch_pack_records.
 struct BwdLaunch {
   int zoh;                // zero-order-hold input term (else Euler)
   const void* u;
@@ -118,7 +124,7 @@ struct BwdLaunch {
   void* dC;
   float* dD;              // nullable
   float* dbias;           // nullable
-  const void* ws_bc;      // records from the checkpoint pass
+  const void* ws_bc;      // B, C records (batch, G, seqlen, 2*dstate/G)
   const float* ws_ckpt;   // (batch, ntiles, dstate, dim)
   float* ws_lagg;         // (nseg-1, batch, dim, dstate) when nseg > 1
   float* ws_lsum;         // (nseg-1, batch, dim) when nseg > 1
@@ -168,6 +174,9 @@ struct SsdLaunch {
 };
 
 hipError_t launch_scan_fwd(const ScanLaunch& a, hipStream_t stream);
+// Packs only the B, C records into a.ws_bc (a backward pass whose checkpoints
+// came from the forward pass needs them and nothing else of launch_scan_fwd).
+hipError_t launch_pack_records(const ScanLaunch& a, hipStream_t stream);
 // The time-parallel forward scan for long sequences with few channels
 // (scan_wave.hip): N = 16, no convolution prologue, no checkpoints; it reads
 // B and C directly and needs no workspace.

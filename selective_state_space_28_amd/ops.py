@@ -231,13 +231,8 @@ def ssm_scan_bwd_workspace_bytes(batch: int, dim: int, dstate: int, seqlen: int,
     return int(load().ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, _DTYPES[dtype]))
 
 
-def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                 h0=None, *, dy, dlast_state=None, bbar="euler", workspace=None):
-    """Gradients through ssm_scan_fwd (input term `bbar`: "euler" or "zoh")
-    given dy = dL/dy and optionally dL/dlast_state; the states are
-    recomputed, not stored.
-    Returns a dict: du, ddelta, dz (None without z) and dB, dC in the input
-    dtype; dA, dD, ddelta_bias, dh0 in float32."""
+def _bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, dy, dlast_state, bbar,
+         workspace, ckpt):
     lib = load()
     dev = u.device
     if dev.type != "cuda":
@@ -257,12 +252,15 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     _check("h0", h0, (batch, dim, N), torch.float32, dev, required=False)
     _check("dy", dy, (batch, dim, L), dt, dev)
     _check("dlast_state", dlast_state, (batch, dim, N), torch.float32, dev, required=False)
+    if ckpt is not None:
+        _check("ckpt", ckpt, (batch, (L + 15) // 16, N, dim), torch.float32, dev)
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u), dA=torch.empty((dim, N), **f32),
              dB=torch.empty_like(B), dC=torch.empty_like(C), dD=torch.empty(dim, **f32),
              dz=torch.empty_like(u) if z is not None else None,
              ddelta_bias=torch.empty(dim, **f32), dh0=torch.empty((batch, dim, N), **f32))
-    need = int(lib.ssm_scan_bwd_workspace_bytes(batch, dim, N, L, code))
+    query = lib.ssm_scan_bwd_ckpt_workspace_bytes if ckpt is not None else lib.ssm_scan_bwd_workspace_bytes
+    need = int(query(batch, dim, N, L, code))
     ws_bytes = 0
     if need > 0:
         if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
@@ -273,15 +271,97 @@ def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
     else:
         workspace = None
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(dy),
-                          _ptr(dlast_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
-                          _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-                          _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), batch, dim, N, L, code,
-                          _ptr(workspace), ws_bytes, stream)
+    head = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            _flags(delta_softplus, bbar), _ptr(h0))
+    tail = (_ptr(dy), _ptr(dlast_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+            _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
+            _ptr(g["dh0"]), batch, dim, N, L, code, _ptr(workspace), ws_bytes, stream)
+    if ckpt is None:
+        rc = lib.ssm_scan_bwd(*head, *tail)
+        where = "ssm_scan_bwd"
+    else:
+        rc = lib.ssm_scan_bwd_ckpt(*head, _ptr(ckpt), ckpt.numel() * 4, *tail)
+        where = "ssm_scan_bwd_ckpt"
     if rc != 0:
-        raise SsmError(rc, "ssm_scan_bwd")
+        raise SsmError(rc, where)
     return g
+
+
+def ssm_scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                 h0=None, *, dy, dlast_state=None, bbar="euler", workspace=None):
+    """Gradients through ssm_scan_fwd (input term `bbar`: "euler" or "zoh")
+    given dy = dL/dy and optionally dL/dlast_state; the states are
+    recomputed, not stored.
+    Returns a dict: du, ddelta, dz (None without z) and dB, dC in the input
+    dtype; dA, dD, ddelta_bias, dh0 in float32."""
+    return _bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, dy, dlast_state, bbar,
+                workspace, None)
+
+
+def ssm_scan_ckpt_bytes(batch: int, dim: int, dstate: int, seqlen: int) -> int:
+    return int(load().ssm_scan_ckpt_bytes(batch, dim, dstate, seqlen))
+
+
+def ssm_scan_bwd_ckpt_workspace_bytes(batch: int, dim: int, dstate: int, seqlen: int,
+                                      dtype: torch.dtype) -> int:
+    return int(load().ssm_scan_bwd_ckpt_workspace_bytes(batch, dim, dstate, seqlen, _DTYPES[dtype]))
+
+
+def ssm_scan_fwd_ckpt(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                      h0=None, *, bbar="euler", out=None, ckpt=None, workspace=None):
+    """ssm_scan_fwd that also writes the tile checkpoints (the state entering
+    every 16-step tile) for ssm_scan_bwd_ckpt.
+    Returns (y, last_state, ckpt); ckpt is (batch, ceil(L/16), N, dim) float32."""
+    lib = load()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("libssm runs on the GPU: tensors must be on a cuda device")
+    dt = u.dtype
+    code = _code(u)
+    batch, dim, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    _check("u", u, (batch, dim, L), dt, dev)
+    _check("delta", delta, (batch, dim, L), dt, dev)
+    _check("A", A, (dim, N), torch.float32, dev)
+    _check("B", B, (batch, N, L), dt, dev)
+    _check("C", C, (batch, N, L), dt, dev)
+    _check("D", D, (dim,), torch.float32, dev, required=False)
+    _check("z", z, (batch, dim, L), dt, dev, required=False)
+    _check("delta_bias", delta_bias, (dim,), torch.float32, dev, required=False)
+    _check("h0", h0, (batch, dim, N), torch.float32, dev, required=False)
+    y = out if out is not None else torch.empty_like(u)
+    _check("out", y, (batch, dim, L), dt, dev)
+    cshape = (batch, (L + 15) // 16, N, dim)
+    if ckpt is None:
+        ckpt = torch.empty(cshape, dtype=torch.float32, device=dev)
+    _check("ckpt", ckpt, cshape, torch.float32, dev)
+    last = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    need = int(lib.ssm_scan_fwd_workspace_bytes(batch, dim, N, L, code))
+    ws_bytes = 0
+    if need > 0:
+        if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    else:
+        workspace = None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssm_scan_fwd_ckpt(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), _flags(delta_softplus, bbar), _ptr(h0), _ptr(y),
+                               _ptr(last), _ptr(ckpt), ckpt.numel() * 4, batch, dim, N, L, code,
+                               _ptr(workspace), ws_bytes, stream)
+    if rc != 0:
+        raise SsmError(rc, "ssm_scan_fwd_ckpt")
+    return y, last, ckpt
+
+
+def ssm_scan_bwd_ckpt(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                      h0=None, *, ckpt, dy, dlast_state=None, bbar="euler", workspace=None):
+    """ssm_scan_bwd from the checkpoints ssm_scan_fwd_ckpt wrote for the same
+    inputs: the same gradients, without the forward checkpoint pass."""
+    return _bwd(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, dy, dlast_state, bbar,
+                workspace, ckpt)
 
 
 def ssm_ssd_scan_fwd_workspace_bytes(batch: int, dstate: int, seqlen: int, dtype: torch.dtype) -> int:

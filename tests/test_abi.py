@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_state_update",
                           "ssm_conv_scan_fwd", "ssm_conv_state_update", "ssm_scan_bwd_workspace_bytes",
                           "ssm_scan_bwd", "ssm_ssd_scan_fwd", "ssm_ssd_scan_fwd_workspace_bytes",
-                          "ssm_scan_fwd_noalloc", "ssm_status_string"}
+                          "ssm_scan_fwd_noalloc", "ssm_status_string", "ssm_scan_ckpt_bytes",
+                          "ssm_scan_fwd_ckpt", "ssm_scan_bwd_ckpt_workspace_bytes", "ssm_scan_bwd_ckpt"}
     lib = ctypes.CDLL(load()._name)
     for n in names:
         assert hasattr(lib, n), n
@@ -243,6 +244,89 @@ def test_bwd_workspace_query_and_check():
     assert _bwd(ws=at(12), wsb=need - 1) == WS
     assert _bwd(ws=at(6) + 256, wsb=need) == ALIAS   # overlaps du
     assert _bwd(batch=0) == OK
+
+
+# ---- the training pair: forward with tile checkpoints, backward from them ----
+
+CK = 1 * 128 * 16 * 64 * 4   # checkpoints of (batch 1, dim 64, N 16, L 2048)
+
+
+def test_ckpt_bytes_query():
+    lib = load()
+    assert lib.ssm_scan_ckpt_bytes(1, 64, 16, 2048) == CK
+    assert lib.ssm_scan_ckpt_bytes(3, 70, 4, 2049) == 3 * 129 * 4 * 70 * 4   # a ragged last tile
+    assert lib.ssm_scan_ckpt_bytes(1, 64, 16, 16) == 16 * 64 * 4
+    assert lib.ssm_scan_ckpt_bytes(1, 64, 16, 0) == 0
+    assert lib.ssm_scan_ckpt_bytes(0, 64, 16, 2048) == 0
+    assert lib.ssm_scan_ckpt_bytes(1, 64, 12, 2048) == 0      # dstate refused
+    assert lib.ssm_scan_ckpt_bytes(1, 64, 16, 1 << 40) == 0   # too long
+
+
+def _fwdck(**kw):
+    a = dict(u=P, delta=P, A=P, B=P, C=P, D=None, z=None, bias=None, sp=1, h0=None, y=at(1),
+             last=None, ck=at(3), ckb=CK, batch=1, dim=64, dstate=16, L=2048, dtype=1, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return load().ssm_scan_fwd_ckpt(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                    a["bias"], a["sp"], a["h0"], a["y"], a["last"], a["ck"], a["ckb"],
+                                    a["batch"], a["dim"], a["dstate"], a["L"], a["dtype"], a["ws"],
+                                    a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ck=None), NULL), (dict(ckb=CK - 1), WS), (dict(ck=at(3) + 2), ALIGN),
+    (dict(ck=at(1) + 256), ALIAS),            # inside y
+    (dict(ck=P + 64), ALIAS),                 # inside the inputs
+    (dict(last=at(3) + CK - 4), ALIAS),       # last_state at the checkpoints' end
+    (dict(dstate=3), SHAPE), (dict(sp=4), FLAGS), (dict(dtype=2), DTYPE), (dict(u=None), NULL),
+    (dict(ws=None), WS),                      # every checkpoint check passed: the workspace next
+    (dict(ws=at(3) + 4096, wsb=1 << 20), ALIAS),   # workspace inside the checkpoints
+    (dict(batch=0), OK), (dict(L=0, ck=None, ckb=0), OK),   # nothing to checkpoint, no HIP call
+])
+def test_fwd_ckpt_validation(kw, code):
+    assert _fwdck(**kw) == code
+
+
+def _bwdck(**kw):
+    a = dict(u=P, delta=at(1), A=at(2), B=at(3), C=at(4), D=None, z=None,
+             bias=None, fl=1, h0=None, ck=at(13), ckb=CK, dy=at(5), dlast=None, du=at(6), dd=at(7),
+             dA=at(8), dB=at(9), dC=at(10), dD=None, dz=None, dbias=None, dh0=None,
+             batch=1, dim=64, dstate=16, L=2048, dtype=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return load().ssm_scan_bwd_ckpt(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                    a["bias"], a["fl"], a["h0"], a["ck"], a["ckb"], a["dy"], a["dlast"],
+                                    a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                                    a["dbias"], a["dh0"], a["batch"], a["dim"], a["dstate"], a["L"],
+                                    a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ck=None), NULL), (dict(ckb=CK - 4), WS), (dict(ck=at(13) + 1), ALIGN),
+    (dict(du=at(13) + 1024), ALIAS),          # a gradient inside the checkpoints
+    (dict(dh0=at(13) + CK - 8), ALIAS),
+    (dict(dA=at(13)), ALIAS),
+    (dict(ck=at(1)), WS),                     # overlapping inputs are allowed: reaches the workspace check
+    (dict(fl=4), FLAGS), (dict(dtype=7), DTYPE), (dict(dy=None), NULL),
+    (dict(ws=None), WS), (dict(ws=at(13) + 256, wsb=1 << 24), ALIAS),
+    (dict(batch=0), OK),
+])
+def test_bwd_ckpt_validation(kw, code):
+    assert _bwdck(**kw) == code
+
+
+def test_bwd_ckpt_workspace_query():
+    """The checkpointed backward's workspace is the plain backward's without
+    the checkpoint region."""
+    lib = load()
+    for shape in ((1, 64, 16, 2048), (2, 70, 4, 1031), (1, 2048, 16, 65536), (3, 5, 1, 17)):
+        plain = lib.ssm_scan_bwd_workspace_bytes(*shape, 1)
+        ck = lib.ssm_scan_bwd_ckpt_workspace_bytes(*shape, 1)
+        cb = lib.ssm_scan_ckpt_bytes(*shape)
+        assert ck == plain - (cb + 255) // 256 * 256, shape
+    assert lib.ssm_scan_bwd_ckpt_workspace_bytes(0, 64, 16, 2048, 1) == 0
+    assert lib.ssm_scan_bwd_ckpt_workspace_bytes(1, 64, 16, 2048, 5) == 0
+    need = lib.ssm_scan_bwd_ckpt_workspace_bytes(1, 64, 16, 2048, 1)
+    assert _bwdck(ws=at(14), wsb=need - 1) == WS
 
 
 def _ssd(**kw):
