@@ -132,6 +132,17 @@ def test_sweep_bwd(dev, i, monkeypatch):
         if ref is None or g.get(k) is None:
             continue
         assert_parity(g[k].float().cpu().numpy(), ref, "bf16" if dt == "bf16" else "f32", k)
+    # the training pair on the same case: the forward's checkpoints give the
+    # backward the same bits
+    args = (t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias)
+    _, _, ck = ssm.ssm_scan_fwd_ckpt(*args, h0=to_torch(h0, "f32", dev), bbar=c["bbar"])
+    g2 = ssm.ssm_scan_bwd_ckpt(*args, h0=to_torch(h0, "f32", dev), ckpt=ck, dy=to_torch(dyk, dt, dev),
+                               bbar=c["bbar"])
+    torch.cuda.synchronize(dev)
+    for k, v in g.items():
+        if v is not None:
+            assert torch.equal(v.view(torch.int16) if v.dtype == torch.bfloat16 else v.view(torch.int32),
+                               g2[k].view(torch.int16) if v.dtype == torch.bfloat16 else g2[k].view(torch.int32)), k
 
 
 @pytest.mark.parametrize("i", range(NCASES // 2))
