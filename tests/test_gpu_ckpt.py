@@ -199,3 +199,34 @@ def test_full_size_c3_ckpt_pair(dev, bbar):
     row = {k: (v[0:1] if isinstance(v, np.ndarray) and v.ndim == 3 and v.shape[0] == cfg.batch else v)
            for k, v in inp.items()}
     _check_ckpt(row, ckpt[0:1], None, True, bbar, tiles=(1, 64, 127))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ckpt_pair_unaligned_pointers(dev, dtype):
+    """Inputs, y and the checkpoints one element past an aligned start take
+    the element-wise paths of both kernels; every result keeps its bits."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    inp = _case(dtype, b=2, d=70, L=128, seed=540)
+    t = {k: to_torch(inp.get(k), dtype, dev) for k in ("u", "delta", "B", "C", "z", "dy")}
+    A, D, bias = (to_torch(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+
+    def off(x):
+        flat = torch.empty(x.numel() + 1, dtype=x.dtype, device=x.device)
+        v = flat[1:].view(x.shape)
+        v.copy_(x)
+        return v
+
+    args = (t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias)
+    y0, l0, c0 = ssm.ssm_scan_fwd_ckpt(*args)
+    g0 = ssm.ssm_scan_bwd_ckpt(*args, ckpt=c0, dy=t["dy"])
+    tu = {k: off(v) for k, v in t.items()}
+    argsu = (tu["u"], tu["delta"], A, tu["B"], tu["C"], D, tu["z"], bias)
+    y1, l1, c1 = ssm.ssm_scan_fwd_ckpt(*argsu, out=off(torch.empty_like(t["u"])), ckpt=off(torch.empty_like(c0)))
+    g1 = ssm.ssm_scan_bwd_ckpt(*argsu, ckpt=c1, dy=tu["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y0), _bits(y1)) and torch.equal(_bits(l0), _bits(l1))
+    assert torch.equal(_bits(c0), _bits(c1))
+    for k in GRADS:
+        if g0[k] is not None:
+            assert torch.equal(_bits(g0[k]), _bits(g1[k])), k
