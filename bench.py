@@ -71,6 +71,10 @@ KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 0>"
 KERNEL_NAME_ZOH = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 1>"
 KERNEL_NAME_CONV = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 2>"
 PACK_KERNEL_NAME = "ssm::pack_bc_kernel<unsigned short, 4, 4>"
+# VALU counters of the scan kernel (one rocprofv3 pass): waves, VALU
+# instructions, and VALU-active quad-cycles summed over the waves
+VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU")
+NUM_SIMDS = 256 * 4
 # the plain device copy that calibrates the byte counters: 1 GiB, three times
 CALIB_BYTES = 1 << 30
 CALIB_COPIES = 3
@@ -271,6 +275,20 @@ def main():
     if t_alu < t_hbm:
         roof.update({"achieved": round(alg_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(alg_gbps / HBM_PEAK_GBPS, 4)})
+    vc = scan_prof.get("valu_counters")
+    if vc and vc.get("SQ_WAVES"):
+        tiles = (cfg.seqlen + 15) // 16
+        active = vc["SQ_ACTIVE_INST_VALU"] * 4 / NUM_SIMDS  # VALU-busy cycles per SIMD
+        roof["valu"] = {
+            "wave_insts_per_element": round(vc["SQ_INSTS_VALU"] / elements, 3),
+            "lane_ops_per_element": round(vc["SQ_INSTS_VALU"] * 64 / elements, 1),
+            "insts_per_wave_tile": round(vc["SQ_INSTS_VALU"] / (vc["SQ_WAVES"] * tiles), 1),
+            "active_cycles_per_simd": round(active),
+            "busy_frac": (round(active / (trace_ns * 1e-9 * 2.4e9), 4) if trace_ns else None),
+            "note": "SQ_INSTS_VALU and SQ_ACTIVE_INST_VALU (quad-cycles) per dispatch, measured in this run; a wave "
+                    "instruction covers 64 lanes (lane_ops = 64 x wave instructions; the recurrence alone is 5 x 16 "
+                    "states = 80 per element); a wave-tile is one wave's 16 steps of its 64 channels; busy_frac = "
+                    "VALU-active cycles per SIMD over the traced kernel time at the 2.4 GHz peak clock"}
 
     out = {
         "metric": METRIC, "value": value, "unit": "elements/s", "n_gpus": 1,
@@ -528,7 +546,8 @@ def _starts(name, prefix):
 def parse_profile_dirs(dirs, steps):
     """Bytes per launch and traced durations from the child runs' CSV files.
 
-    dirs: {"fetch": dir, "write": dir, "trace": dir} (any may be missing).
+    dirs: {"fetch": dir, "write": dir, "valu": dir, "trace": dir} (any may be
+    missing).
     In the fetch and write runs, the copies after the last scan dispatch are
     the calibration: CALIB_COPIES x CALIB_BYTES read and written, so
     scale = known bytes / counted bytes turns a counter reading into bytes.
@@ -559,6 +578,20 @@ def parse_profile_dirs(dirs, steps):
     for name, k in kernels.items():
         if "read_bytes" in k and "write_bytes" in k:
             k["hbm_bytes_per_launch"] = k["read_bytes"] + k["write_bytes"]
+    if "valu" in dirs:
+        # VALU instructions and VALU-active quad-cycles (summed over the
+        # device's SIMDs) per dispatch, and the waves that ran them
+        rows = _csv_rows(dirs["valu"], "counter_collection.csv")
+        for name in (KERNEL_NAME, KERNEL_NAME_CONV):
+            got = {}
+            for counter in VALU_COUNTERS:
+                vals = [v for i, (n, v) in _counter_per_dispatch(rows, counter).items() if _starts(n, name)]
+                if vals:
+                    got[counter] = float(np.mean(vals))
+            if len(got) == len(VALU_COUNTERS):
+                kernels.setdefault(name, {})["valu_counters"] = {c: round(v) for c, v in got.items()}
+            elif name == KERNEL_NAME:
+                err = err or "no VALU counter rows for the scan kernel in the 'valu' run"
     if "trace" in dirs:
         rows = _csv_rows(dirs["trace"], "kernel_trace.csv")
         for name in (KERNEL_NAME, KERNEL_NAME_CONV, PACK_KERNEL_NAME):
@@ -579,11 +612,11 @@ def parse_profile_dirs(dirs, steps):
 
 
 def collect_profiles(args):
-    """Three child runs of this program under rocprofv3, before this process
+    """Four child runs of this program under rocprofv3, before this process
     touches the GPU: FETCH_SIZE and WRITE_SIZE per dispatch (each run ends
     with plain copies of known size, whose counter reading gives the factor
-    that turns the counter into bytes), then a kernel trace of the same step
-    after a settle phase.  Returns per-kernel bytes per launch and the traced
+    that turns the counter into bytes), the VALU instruction counters, then a
+    kernel trace of the same step after a settle phase.  Returns per-kernel bytes per launch and the traced
     mean duration of the last --steps dispatches; or an 'error' entry."""
     exe = shutil.which("rocprofv3")
     if exe is None:
@@ -596,6 +629,7 @@ def collect_profiles(args):
     me = os.path.abspath(__file__)
     runs = [("fetch", ["--kernel-trace", "--pmc", "FETCH_SIZE"], ["--child-calibrate"], 3),
             ("write", ["--kernel-trace", "--pmc", "WRITE_SIZE"], ["--child-calibrate"], 3),
+            ("valu", ["--kernel-trace", "--pmc", *VALU_COUNTERS], [], 3),
             ("trace", ["--kernel-trace", "--stats"], [], args.steps)]
     res = {"commands": [], "note": "child runs of this program under rocprofv3, in this bench run"}
     dirs = {}

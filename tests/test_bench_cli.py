@@ -68,3 +68,25 @@ def test_profile_parsing_reports_a_missing_calibration(tmp_path):
                [[1, bench.KERNEL_NAME, "FETCH_SIZE", 5.0]])
     calib, kernels, err = bench.parse_profile_dirs({"fetch": str(tmp_path / "fetch")}, steps=2)
     assert "calibration" in err and calib == {} and kernels == {}
+
+
+def test_profile_parsing_reads_the_valu_counters(tmp_path):
+    """The VALU pass gives each counter's mean per dispatch of the scan
+    kernel; a pass without the scan kernel's rows is reported."""
+    sys.path.insert(0, ROOT)
+    import bench
+    scan = bench.KERNEL_NAME
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    for d, (waves, insts, active) in enumerate([(5120, 2.9e8, 3.4e8), (5120, 3.1e8, 3.6e8)]):
+        rows += [[d, scan, "SQ_WAVES", waves], [d, scan, "SQ_INSTS_VALU", insts],
+                 [d, scan, "SQ_ACTIVE_INST_VALU", active]]
+    rows += [[9, bench.PACK_KERNEL_NAME, "SQ_INSTS_VALU", 5.0]]
+    _write_csv(str(tmp_path / "valu" / "v_counter_collection.csv"), hdr, rows)
+    calib, kernels, err = bench.parse_profile_dirs({"valu": str(tmp_path / "valu")}, steps=2)
+    assert err is None
+    assert kernels[scan]["valu_counters"] == {"SQ_WAVES": 5120, "SQ_INSTS_VALU": 300000000,
+                                              "SQ_ACTIVE_INST_VALU": 350000000}
+    _write_csv(str(tmp_path / "valu2" / "v_counter_collection.csv"), hdr, rows[-1:])
+    _, _, err = bench.parse_profile_dirs({"valu": str(tmp_path / "valu2")}, steps=2)
+    assert err is not None and "VALU" in err
