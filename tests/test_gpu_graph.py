@@ -159,3 +159,57 @@ def test_bwd_graph_replays(dev, bbar):
                 assert torch.equal(v, ref[k]), (i, k)
         ssm.ssm_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], None, None, None)  # eager work in between
         torch.cuda.synchronize()
+
+
+def test_training_pair_graph_replays(dev):
+    """ssm_scan_fwd_ckpt then ssm_scan_bwd_ckpt captured together (a training
+    step): every replay rewrites y, last_state, the checkpoints and every
+    gradient with the eager bits."""
+    import torch
+    import selective_state_space_28_amd as ssm
+    b, d, n, L = 2, 96, 16, 300
+    inp = synth.make_scan_inputs(ScanConfig("g", b, d, n, L, "bf16", seed=34))
+    t = {k: to_torch(inp[k], "bf16", dev) for k in ("u", "delta", "B", "C", "z")}
+    A, D, bias = (to_torch(inp[k], "f32", dev) for k in ("A", "D", "delta_bias"))
+    dy = to_torch(synth.bf16_bits(np.random.default_rng(35).standard_normal((b, d, L), dtype=np.float32)),
+                  "bf16", dev)
+    args = (t["u"], t["delta"], A, t["B"], t["C"], D, t["z"], bias)
+    y_ref, last_ref, ck_ref = ssm.ssm_scan_fwd_ckpt(*args)
+    g_ref = ssm.ssm_scan_bwd_ckpt(*args, ckpt=ck_ref, dy=dy)
+    torch.cuda.synchronize()
+    y, ck = torch.empty_like(y_ref), torch.empty_like(ck_ref)
+    ws = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_bytes(b, d, n, L, torch.bfloat16)), dtype=torch.uint8,
+                     device=dev)
+    bws = torch.empty(max(1, ssm.ssm_scan_bwd_ckpt_workspace_bytes(b, d, n, L, torch.bfloat16)),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        _, last, _ = ssm.ssm_scan_fwd_ckpt(*args, out=y, ckpt=ck, workspace=ws)
+        return last, ssm.ssm_scan_bwd_ckpt(*args, ckpt=ck, dy=dy, workspace=bws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up off the default stream, as capture expects
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        last, grads = step()
+
+    def bits(x):
+        return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+    for i in range(4):
+        for x in [y, ck, last] + [v for v in grads.values() if v is not None]:
+            x.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), bits(y_ref)), f"replay {i}: y"
+        assert torch.equal(bits(ck), bits(ck_ref)), f"replay {i}: checkpoints"
+        assert torch.equal(bits(last), bits(last_ref)), f"replay {i}: last_state"
+        for k, v in grads.items():
+            if v is not None:
+                assert torch.equal(bits(v), bits(g_ref[k])), f"replay {i}: {k}"
+        # eager work between replays, with buffers of its own
+        ssm.ssm_scan_bwd(*args, dy=dy)
+        torch.cuda.synchronize()
