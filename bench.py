@@ -67,9 +67,9 @@ OPS_PER_ELEMENT_CONV = CONV_WIDTH + 4
 # FMA, dB and dC terms, the carry Abar*lambda) and one add each for the
 # channel sums of dB and dC.
 OPS_PER_ELEMENT_STATE_BWD = 16
-KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 0>"
-KERNEL_NAME_ZOH = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 1>"
-KERNEL_NAME_CONV = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 2>"
+KERNEL_NAME = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 0, true>"
+KERNEL_NAME_ZOH = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 1, true>"
+KERNEL_NAME_CONV = "ssm::scan_kernel<unsigned short, 4, 4, 16, 0, 2, true>"
 PACK_KERNEL_NAME = "ssm::pack_bc_kernel<unsigned short, 4, 4>"
 # VALU counters of the scan kernel (one rocprofv3 pass): waves, VALU
 # instructions, and VALU-active quad-cycles summed over the waves

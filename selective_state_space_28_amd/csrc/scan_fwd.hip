@@ -146,8 +146,11 @@ __device__ __forceinline__ float input_term(float a, float x2, float dt, float q
 // but the last from a zero state and records its end state and Delta sum;
 // kPassCkpt runs like the main pass but, instead of y, records the state
 // entering every tile (the checkpoints the backward pass starts from);
-// kPassMainCkpt computes y and records the checkpoints too.
-template <typename T, int NS, int G, int TL, int PASS, int MODE>
+// kPassMainCkpt computes y and records the checkpoints too.  GATE: the
+// passes that compute y apply the silu(z) gate (z given); a compile-time
+// choice, so the ungated instantiation carries no gate work and the gated one
+// no select.
+template <typename T, int NS, int G, int TL, int PASS, int MODE, bool GATE = false>
 __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
     const T* __restrict__ u, const T* __restrict__ delta, const float* __restrict__ A,
     const T* __restrict__ bc, const float* __restrict__ Dskip, const T* __restrict__ z,
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(64 * G, G == 4 ? 5 : 1) void scan_kernel(
   const int64_t rowcc = (int64_t)b * p.dim + (ccvalid ? dcc : 0);
   const float bias_cc = (bias != nullptr && ccvalid) ? bias[dcc] : 0.0f;
   const float D_cc = (Dskip != nullptr && ccvalid) ? Dskip[dcc] : 0.0f;
-  const bool has_z = READOUT && (z != nullptr);
+  constexpr bool has_z = READOUT && GATE;
   const bool vec = p.vec != 0;
 
   if constexpr (CONV) {
@@ -605,9 +608,10 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
   const unsigned grid = (unsigned)(base * s.nseg_launch);
   if constexpr ((MODE & kModeConv) == 0) {  // the backward pass covers both input terms, no prologue
     if (a.ws_ckpt != nullptr && a.ckpt_with_y) {
-      scan_kernel<T, NS, G, TL, kPassMainCkpt, MODE><<<grid, 64 * G, 0, stream>>>(
-          u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt,
-          a.ws_ckpt, s, cv);
+      auto kernel = z != nullptr ? scan_kernel<T, NS, G, TL, kPassMainCkpt, MODE, true>
+                                 : scan_kernel<T, NS, G, TL, kPassMainCkpt, MODE, false>;
+      kernel<<<grid, 64 * G, 0, stream>>>(u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state,
+                                          a.ws_hend, a.ws_sumdt, a.ws_ckpt, s, cv);
       return hipGetLastError();
     }
     if (a.ws_ckpt != nullptr) {
@@ -617,9 +621,10 @@ static hipError_t launch_typed(const ScanLaunch& a, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  scan_kernel<T, NS, G, TL, kPassMain, MODE><<<grid, 64 * G, 0, stream>>>(
-      u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state, a.ws_hend, a.ws_sumdt, nullptr,
-      s, cv);
+  auto kernel = z != nullptr ? scan_kernel<T, NS, G, TL, kPassMain, MODE, true>
+                             : scan_kernel<T, NS, G, TL, kPassMain, MODE, false>;
+  kernel<<<grid, 64 * G, 0, stream>>>(u, dl, a.A, bc, a.Dskip, z, a.bias, a.h0, y, a.last_state,
+                                      a.ws_hend, a.ws_sumdt, nullptr, s, cv);
   return hipGetLastError();
 }
 
